@@ -1,0 +1,307 @@
+"""Pins of the CPU oracle against facts fixed outside the oracle itself:
+a hand-worked example, closed forms, algebraic identities, brute-force
+enumeration on tiny inputs, the O(n^2 / r) pair count, and a library routine
+(PyTorch's scaled_dot_product_attention in float64) for dense attention.
+Each test is chosen so that a plausible slip in the oracle (off-by-one block,
+dropped ReLU, wrong sign, wrong tie order, wrong GQA head map, missing causal
+mask on the diagonal block) fails it.
+"""
+import itertools
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import gen
+import oracle
+from gen.configs import CONFIGS
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def bf(x):
+    return gen.f32_to_bf16(np.asarray(x, np.float32))
+
+
+def widen(a):
+    return gen.bf16_to_f64(a)
+
+
+# ------------------------------------------------------------- worked example
+def _parse_worked():
+    rows = [l.split() for l in open(os.path.join(GOLDEN, "worked_example.txt")) if l.strip() and l[0] != "#"]
+    keys = np.array([float(v) for v in rows[0][1:]]).reshape(12, 2)
+    blocks = np.array([float(v) for v in rows[1][1:]]).reshape(3, 2)
+    queries = []
+    for r in rows[2:]:
+        t = int(r[1])
+        q = np.array([float(v) for v in r[2:6]]).reshape(2, 2)
+        i_s, i_sel = r.index("scores"), r.index("sel")
+        sc = [float(v) for v in r[i_s + 1:i_sel]]
+        sel = [int(v) for v in r[i_sel + 1:]]
+        queries.append((t, q, sc, sel))
+    return keys, blocks, queries
+
+
+def test_worked_example():
+    keys, blocks, queries = _parse_worked()
+    cb = oracle.compress(bf(keys), 4)
+    assert np.array_equal(widen(cb), blocks)
+    for t, q, sc, sel in queries:
+        b = t // 4
+        got = oracle.scores(bf(q), cb[:b], 0.5)
+        assert got.tolist() == sc
+        s, c, _, pairs = oracle.select(bf(q)[None], cb, t, 4, 2, 0.5)
+        assert s[0].tolist() == sel, (t, s[0], sel)
+        assert c[0] == sum(1 for v in sel if v >= 0)
+        assert pairs == b
+
+
+# ------------------------------------------------------------------------ O1
+def test_compress_block_constants():
+    # each block's 4 tokens hold the same distinct value -> block key = value
+    L, d, r = 64, 8, 4
+    vals = np.arange(L // r, dtype=np.float32) * 0.5 - 3.0
+    keys = np.repeat(vals, r)[:, None] * np.ones((1, d), np.float32)
+    out = oracle.compress(bf(keys), r)
+    assert np.array_equal(widen(out)[:, 0], vals.astype(np.float64))
+
+
+def test_compress_integer_mean_exact_and_tail_skipped():
+    L, d, r = 4 * 50 + 3, 16, 4  # ragged tail of 3 tokens is not a block
+    keys = gen.ints(7, 5, (L, d), -8, 8)
+    out = oracle.compress(keys, r)
+    assert out.shape == (50, d)
+    ik = widen(keys)[:200].reshape(50, r, d).sum(1)  # exact integer sums
+    assert np.array_equal(widen(out), ik / 4.0)  # multiples of 1/4 in [-8, 8]: exact in bf16
+
+
+@pytest.mark.parametrize("r", [1, 2, 4, 8])
+def test_compress_vs_double_mean(r):
+    L, d = 4096, 64
+    keys = gen.normal(11, 5, (L, d))
+    out = oracle.compress(keys, r)
+    if r == 1:
+        assert np.array_equal(out, keys)
+        return
+    m = widen(keys).reshape(L // r, r, d).mean(1)
+    ref = bf(m.astype(np.float32))  # fp32 of the exact mean, then bf16
+    diff = np.abs(out.astype(np.int32) - ref.astype(np.int32))
+    # the fp32 running sum can only move the result across a bf16 rounding
+    # boundary: at most one bf16 step, and rarely
+    assert diff.max() <= 1
+    assert (diff == 0).mean() > 0.995
+
+
+# ------------------------------------------------------------------------ O2
+def test_scores_single_head_is_relu_dot():
+    q = gen.normal(3, 4, (1, 64))
+    c = gen.normal(3, 5, (300, 64))
+    got = oracle.scores(q, c, 1.0)
+    ref = np.maximum(widen(c) @ widen(q)[0], 0.0).astype(np.float32)
+    assert np.array_equal(got, ref)
+
+
+def test_scores_relu_identity_and_sign():
+    # relu(x) - relu(-x) = x, so s(q) - s(-q) = w * sum_h q_h . c  (matmul)
+    H, d, n, w = 8, 64, 500, 1.0 / 8
+    q = gen.normal(5, 4, (H, d))
+    c = gen.normal(5, 5, (n, d))
+    neg = q ^ np.uint16(0x8000)
+    lhs = oracle.scores(q, c, w).astype(np.float64) - oracle.scores(neg, c, w).astype(np.float64)
+    rhs = w * (widen(c) @ widen(q).T).sum(1)
+    assert np.allclose(lhs, rhs, rtol=0, atol=1e-5)
+    # scores are non-negative and exactly 0 when every head is negative
+    s = oracle.scores(q, c, w)
+    assert (s >= 0).all()
+    allneg = ((widen(c) @ widen(q).T) <= 0).all(1)
+    assert (s[allneg] == 0).all()
+
+
+def test_scores_head_permutation_and_scaling():
+    H, d, n = 4, 64, 400
+    q = gen.normal(9, 4, (H, d))
+    c = gen.normal(9, 5, (n, d))
+    s = oracle.scores(q, c, 0.25)
+    perm = oracle.scores(q[[2, 0, 3, 1]], c, 0.25)
+    assert np.allclose(s, perm, rtol=1e-6, atol=0)
+    # doubling q (exact in bf16) doubles every score exactly; w scales linearly
+    q2 = bf(widen(q) * 2.0)
+    assert np.array_equal(oracle.scores(q2, c, 0.25), s * 2)
+    assert np.array_equal(oracle.scores(q, c, 0.5), s * 2)
+
+
+# ------------------------------------------------------------------------ O3
+def _brute_kept(s, m):
+    """The unique m-subset whose members all precede all non-members in
+    (score desc, index asc) order, found by enumeration."""
+    n = len(s)
+    found = []
+    for sub in itertools.combinations(range(n), m):
+        ss = set(sub)
+        ok = all((s[a] > s[x]) or (s[a] == s[x] and a < x) for a in ss for x in range(n) if x not in ss)
+        if ok:
+            found.append(sub)
+    assert len(found) == 1
+    return list(found[0])
+
+
+@pytest.mark.parametrize("r", [1, 2, 4])
+@pytest.mark.parametrize("kind", ["ints", "normal"])
+def test_select_bruteforce(r, kind):
+    L, d = 28, 8
+    rng_seed = 100 + r
+    for H in (1, 3):
+        if kind == "ints":  # many exact ties, including zeros
+            keys = gen.ints(rng_seed, 5, (L, d), -1, 1)
+            q = gen.ints(rng_seed, 4, (L, H, d), -1, 1)
+        else:
+            keys = gen.normal(rng_seed, 5, (L, d))
+            q = gen.normal(rng_seed, 4, (L, H, d))
+        blocks = oracle.compress(keys, r)
+        for k in range(1, 7):
+            sel, cnt, band, pairs = oracle.select(q, blocks, 0, r, k, 1.0 / H)
+            assert pairs == sum(t // r for t in range(L))
+            for t in range(L):
+                b = t // r
+                s = oracle.scores(q[t], blocks[:b], 1.0 / H).tolist()
+                m = min(k - 1, b)
+                kept = _brute_kept(s, m) if b else []
+                want = sorted(kept + [b])
+                assert sel[t, :cnt[t]].tolist() == want, (r, H, k, t)
+                assert (sel[t, cnt[t]:] == -1).all()
+                assert cnt[t] == min(k, b + 1)
+
+
+@pytest.mark.parametrize("name", ["c1"])
+def test_select_invariants_config(name):
+    W = CONFIGS[name]
+    keys = gen.idx_keys(W.seed, 0, W.L, 0, W.L, W.di, W.needle_window, W.r)
+    blocks = oracle.compress(keys, W.r)
+    q = gen.normal(W.seed, gen.STREAM_IDX_Q, (W.n_q, W.Hi, W.di))
+    sel, cnt, band, pairs = oracle.select(q, blocks, 0, W.r, W.k, W.w)
+    t = np.arange(W.n_q)
+    b = t // W.r
+    N = W.L // W.r
+    assert pairs == W.r * N * (N - 1) // 2  # sum_t floor(t / r), from position 0
+    assert pairs / W.L ** 2 == pytest.approx(1.0 / (2 * W.r), rel=1e-3)  # the O(n^2 / r) claim
+    assert (cnt == np.minimum(W.k, b + 1)).all()
+    for i in range(W.n_q):
+        row = sel[i, :cnt[i]]
+        assert (np.diff(row) > 0).all()
+        assert row[-1] == b[i]  # diagonal present, nothing after it (causal)
+        ntok = sum(min(W.r, t[i] - j * W.r + 1) for j in row)
+        assert ntok <= W.k * W.r
+    # near-tie band bookkeeping: last kept >= first dropped
+    has = ~np.isnan(band).any(1)
+    assert (band[has, 0] >= band[has, 1]).all()
+
+
+def test_select_budget_covers_context_keeps_everything():
+    L, r = 64, 4
+    keys = gen.normal(21, 5, (L, 64))
+    q = gen.normal(21, 4, (L, 2, 64))
+    blocks = oracle.compress(keys, r)
+    sel, cnt, _, _ = oracle.select(q, blocks, 0, r, L // r, 0.5)
+    for t in range(L):
+        assert sel[t, :cnt[t]].tolist() == list(range(t // r + 1))
+
+
+def test_select_ragged_start_and_length():
+    # queries starting mid-block, context not a multiple of r
+    L, r, k = 203, 4, 5
+    keys = gen.normal(31, 5, (L, 64))
+    q = gen.normal(31, 4, (L, 2, 64))
+    blocks = oracle.compress(keys, r)
+    t0 = 77
+    sel, cnt, _, pairs = oracle.select(q[t0:], blocks, t0, r, k, 0.5)
+    assert pairs == sum(t // r for t in range(t0, L))
+    for i, t in enumerate(range(t0, L)):
+        b = t // r
+        s = oracle.scores(q[t], blocks[:b], 0.5).tolist()
+        assert sel[i, :cnt[i]].tolist() == sorted(_brute_kept(s, min(k - 1, b)) + [b])
+
+
+# -------------------------------------------------------------------- O5/O6
+def _torch_dense(Q, K, V, t0, scale):
+    q = torch.from_numpy(widen(Q)).permute(1, 0, 2)[None]  # [1, Hq, nq, D]
+    G = Q.shape[1] // K.shape[1]
+    L = t0 + Q.shape[0]
+    k = torch.from_numpy(widen(K[:L])).repeat_interleave(G, 1).permute(1, 0, 2)[None]
+    v = torch.from_numpy(widen(V[:L])).repeat_interleave(G, 1).permute(1, 0, 2)[None]
+    # causal with an offset: query i sits at position t0 + i
+    mask = torch.arange(L)[None, :] <= (t0 + torch.arange(Q.shape[0]))[:, None]
+    o = torch.nn.functional.scaled_dot_product_attention(q, k, v, attn_mask=mask, scale=scale)
+    return o[0].permute(1, 0, 2).numpy()
+
+
+def test_dense_vs_torch_sdpa_fp64():
+    L, Hq, Hkv, D = 96, 8, 2, 128
+    Q = gen.normal(41, 1, (L, Hq, D))
+    K = gen.normal(41, 2, (L, Hkv, D))
+    V = gen.normal(41, 3, (L, Hkv, D))
+    t0 = 30
+    o, lse = oracle.dense_attn(Q[t0:], K, V, t0)
+    ref = _torch_dense(Q[t0:], K, V, t0, D ** -0.5)
+    assert np.abs(o - ref).max() < 1e-12
+
+
+def test_sparse_equals_dense_when_budget_covers_context():
+    L, Hq, Hkv, D, r = 80, 4, 1, 128, 4
+    Q = gen.normal(43, 1, (L, Hq, D))
+    K = gen.normal(43, 2, (L, Hkv, D))
+    V = gen.normal(43, 3, (L, Hkv, D))
+    q = gen.normal(43, 4, (L, 2, 64))
+    blocks = oracle.compress(gen.normal(43, 5, (L, 64)), r)
+    sel, cnt, _, _ = oracle.select(q, blocks, 0, r, L // r, 0.5)
+    o1, l1 = oracle.sparse_attn(Q, K, V, 0, r, sel, cnt)
+    o2, l2 = oracle.dense_attn(Q, K, V, 0)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+def test_attend_closed_forms():
+    L, Hq, Hkv, D = 40, 4, 2, 128
+    K = gen.normal(47, 2, (L, Hkv, D))
+    V = gen.normal(47, 3, (L, Hkv, D))
+    q = gen.normal(47, 1, (Hq, D))
+    # one kept token: output is that token's V row, lse is its logit
+    o, lse = oracle.attend_tokens(q, K, V, [17])
+    for h in range(Hq):
+        g = h // (Hq // Hkv)
+        assert np.array_equal(o[h], widen(V[17, g]))
+        assert lse[h] == pytest.approx(widen(q[h]) @ widen(K[17, g]) / math.sqrt(D), abs=1e-12)
+    # zero query: uniform weights -> mean of kept V rows, lse = ln |T|
+    toks = [1, 5, 6, 30, 39]
+    o, lse = oracle.attend_tokens(np.zeros((Hq, D), np.uint16), K, V, toks)
+    for h in range(Hq):
+        g = h // (Hq // Hkv)
+        assert np.allclose(o[h], widen(V[toks, g]).mean(0), atol=1e-14)
+        assert lse[h] == pytest.approx(math.log(len(toks)), abs=1e-14)
+    # constant V: output is that constant
+    Vc = np.full_like(V, bf(1.5)[()])
+    o, _ = oracle.attend_tokens(q, K, Vc, toks)
+    assert np.allclose(o, 1.5, atol=1e-14)
+
+
+def test_diagonal_block_is_causally_masked():
+    # query at t = 4j + 1: its own block contributes tokens 4j and 4j + 1 only
+    L, Hq, Hkv, D, r = 32, 2, 1, 128, 4
+    Q = gen.normal(53, 1, (L, Hq, D))
+    K = gen.normal(53, 2, (L, Hkv, D))
+    V = gen.normal(53, 3, (L, Hkv, D))
+    t = 4 * 5 + 1
+    sel = np.array([[2, 5]], np.int32)
+    cnt = np.array([2], np.int32)
+    o, lse = oracle.sparse_attn(Q[t:t + 1], K, V, t, r, sel, cnt)
+    o2, lse2 = oracle.attend_tokens(Q[t], K, V, [8, 9, 10, 11, 20, 21])
+    assert np.array_equal(o[0], o2) and np.array_equal(lse[0], lse2)
+    # and the same query through the library routine over those six tokens
+    mask = np.zeros(L, bool)
+    mask[[8, 9, 10, 11, 20, 21]] = True
+    qq = torch.from_numpy(widen(Q[t]))[None, :, None, :]
+    kk = torch.from_numpy(widen(K[:, 0]))[None, None].expand(1, Hq, L, D)
+    vv = torch.from_numpy(widen(V[:, 0]))[None, None].expand(1, Hq, L, D)
+    ref = torch.nn.functional.scaled_dot_product_attention(qq, kk, vv, attn_mask=torch.from_numpy(mask)[None, None, None])
+    assert np.abs(o[0] - ref[0, :, 0].numpy()).max() < 1e-12
