@@ -1,0 +1,220 @@
+"""QSA (Qwen Sparse Attention) hot path on AMD Instinct MI355X (gfx950).
+
+Thin Python binding of ``libqsa.so`` (C ABI in ``include/qsa.h`` and
+``include/qsa_bench.h``). Functions carry the C names and only marshal
+arguments: torch tensors in device memory become raw pointers, the current
+torch stream becomes the ``hipStream_t``, and a non-OK status raises
+``QsaError``. Every step of the path runs in the library's HIP kernels; there
+is no fallback: if the library is missing, importing this package fails.
+"""
+import ctypes
+import math
+import os
+
+import torch  # loads the HIP runtime that libqsa.so then binds to
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libqsa.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is not built; run `python -m block_sparse_long_09_amd.build` (hipcc, gfx950)")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+_vp, _i32, _i64, _sz, _f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
+
+
+class IndexDesc(ctypes.Structure):
+    _fields_ = [("block_size", _i32), ("top_k_blocks", _i32), ("n_idx_heads", _i32),
+                ("idx_head_dim", _i32), ("idx_head_weight", _f32)]
+
+
+class AttnDesc(ctypes.Structure):
+    _fields_ = [("n_q_heads", _i32), ("n_kv_heads", _i32), ("head_dim", _i32), ("softmax_scale", _f32)]
+
+
+_PI, _PA = ctypes.POINTER(IndexDesc), ctypes.POINTER(AttnDesc)
+
+
+def _sig(name, res, args):
+    f = getattr(_lib, name)
+    f.restype = res
+    f.argtypes = args
+    return f
+
+
+_sig("qsa_compress_keys", ctypes.c_int, [_vp, _i64, _i32, _i32, _i32, _i64, _i64, _vp, _i64, _vp])
+_sig("qsa_index_topk_workspace_size", _sz, [_PI, _i32, _i32, _i64])
+_sig("qsa_index_topk", ctypes.c_int, [_PI, _vp, _vp, _i64, _vp, _i64, _i32, _i32, _vp, _vp, _vp, _sz, _vp])
+_sig("qsa_sparse_attn_workspace_size", _sz, [_PA, _i32, _i32, _i32, _i32])
+_sig("qsa_sparse_attn_prefill", ctypes.c_int,
+     [_PA, _i32, _i32, _vp, _vp, _vp, _i64, _i32, _i64, _vp, _vp, _vp, _vp, _vp, _sz, _vp])
+_sig("qsa_sparse_attn_decode", ctypes.c_int,
+     [_PA, _i32, _i32, _vp, _vp, _vp, _i64, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _sz, _vp])
+_sig("qsa_dense_attn_workspace_size", _sz, [_PA, _i32, _i32, _i64])
+_sig("qsa_dense_attn_prefill", ctypes.c_int, [_PA, _vp, _vp, _vp, _i64, _i32, _i64, _vp, _vp, _vp, _sz, _vp])
+_sig("qsa_dense_attn_decode", ctypes.c_int, [_PA, _vp, _vp, _vp, _i64, _vp, _i32, _vp, _vp, _vp, _sz, _vp])
+_sig("qsa_status_string", ctypes.c_char_p, [ctypes.c_int])
+_sig("qsa_last_error_message", ctypes.c_char_p, [])
+_sig("qsa_abi_version", ctypes.c_int, [])
+
+#: every symbol the C headers declare
+EXPORTS = (
+    "qsa_compress_keys", "qsa_index_topk_workspace_size", "qsa_index_topk",
+    "qsa_sparse_attn_workspace_size", "qsa_sparse_attn_prefill", "qsa_sparse_attn_decode",
+    "qsa_status_string", "qsa_last_error_message", "qsa_abi_version",
+    "qsa_dense_attn_workspace_size", "qsa_dense_attn_prefill", "qsa_dense_attn_decode",
+)
+
+
+class QsaError(RuntimeError):
+    def __init__(self, status, message):
+        self.status = status
+        super().__init__(f"{_lib.qsa_status_string(status).decode()}: {message}")
+
+
+def _check(status):
+    if status != 0:
+        raise QsaError(status, _lib.qsa_last_error_message().decode())
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("expected a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError("tensor must be in device memory")
+    if not t.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if isinstance(stream, torch.cuda.Stream) else stream
+
+
+def _bf16(t, name):
+    if t.dtype != torch.bfloat16:
+        raise TypeError(f"{name} must be bfloat16")
+    return _ptr(t)
+
+
+def _i32t(t, name):
+    if t.dtype != torch.int32:
+        raise TypeError(f"{name} must be int32")
+    return _ptr(t)
+
+
+def index_desc(block_size, top_k_blocks, n_idx_heads, idx_head_dim=64, idx_head_weight=None):
+    w = 1.0 / n_idx_heads if idx_head_weight is None else idx_head_weight
+    return IndexDesc(block_size, top_k_blocks, n_idx_heads, idx_head_dim, w)
+
+
+def attn_desc(n_q_heads, n_kv_heads, head_dim=128, softmax_scale=None):
+    s = head_dim ** -0.5 if softmax_scale is None else softmax_scale
+    return AttnDesc(n_q_heads, n_kv_heads, head_dim, s)
+
+
+def abi_version():
+    return _lib.qsa_abi_version()
+
+
+# ----------------------------------------------------------------- method --
+def qsa_compress_keys(idx_k, cmp_k, block_size, first_block, n_blocks, stream=None):
+    """idx_k [B, L, 64] (or [L, 64]) -> cmp_k [B, N, 64] (or [N, 64]), blocks
+    [first_block, first_block + n_blocks) of every row."""
+    if idx_k.dim() == 2:
+        idx_k, cmp_k = idx_k[None], cmp_k[None]
+    B, _, d = idx_k.shape
+    _check(_lib.qsa_compress_keys(_bf16(idx_k, "idx_k"), idx_k.stride(0), B, d, block_size, first_block,
+                                  n_blocks, _bf16(cmp_k, "cmp_k"), cmp_k.stride(0), _stream(stream)))
+
+
+def qsa_index_topk_workspace_size(desc, batch, n_q, max_q_end):
+    return _lib.qsa_index_topk_workspace_size(ctypes.byref(desc), batch, n_q, max_q_end)
+
+
+def qsa_index_topk(desc, idx_q, cmp_k, q_pos0, max_q_end, sel_blocks, sel_count, workspace, stream=None):
+    """idx_q [B, n_q, H_i, 64]; cmp_k [B, N, 64]; q_pos0 int32 [B] (device);
+    sel_blocks int32 [B, n_q, k]; sel_count int32 [B, n_q]; workspace uint8."""
+    if idx_q.dim() == 3:
+        idx_q = idx_q[None]
+    if cmp_k.dim() == 2:
+        cmp_k = cmp_k[None]
+    B, n_q = idx_q.shape[0], idx_q.shape[1]
+    ws = _ptr(workspace) if workspace is not None and workspace.numel() else None
+    nbytes = workspace.numel() * workspace.element_size() if ws else 0
+    _check(_lib.qsa_index_topk(ctypes.byref(desc), _bf16(idx_q, "idx_q"), _bf16(cmp_k, "cmp_k"), cmp_k.stride(0),
+                               _i32t(q_pos0, "q_pos0"), max_q_end, B, n_q, _i32t(sel_blocks, "sel_blocks"),
+                               _i32t(sel_count, "sel_count"), ws, nbytes, _stream(stream)))
+
+
+def qsa_sparse_attn_workspace_size(desc, batch, n_q, top_k_blocks, block_size):
+    return _lib.qsa_sparse_attn_workspace_size(ctypes.byref(desc), batch, n_q, top_k_blocks, block_size)
+
+
+def qsa_sparse_attn_prefill(desc, block_size, q, k, v, q_pos0, sel_blocks, sel_count, out, lse=None,
+                            workspace=None, stream=None):
+    """q [n_q, Hq, D]; k, v [kv_len, Hkv, D]; sel_blocks [n_q, top_k]; out [n_q, Hq, D]; lse [n_q, Hq]."""
+    n_q = q.shape[0]
+    top_k = sel_blocks.shape[-1]
+    ws = _ptr(workspace) if workspace is not None and workspace.numel() else None
+    nbytes = workspace.numel() * workspace.element_size() if ws else 0
+    if lse is not None and lse.dtype != torch.float32:
+        raise TypeError("lse must be float32")
+    _check(_lib.qsa_sparse_attn_prefill(ctypes.byref(desc), block_size, top_k, _bf16(q, "q"), _bf16(k, "k"),
+                                        _bf16(v, "v"), q_pos0, n_q, k.shape[0], _i32t(sel_blocks, "sel_blocks"),
+                                        _i32t(sel_count, "sel_count"), _bf16(out, "out"), _ptr(lse), ws, nbytes,
+                                        _stream(stream)))
+
+
+def qsa_sparse_attn_decode(desc, block_size, q, k_cache, v_cache, kv_len, sel_blocks, sel_count, out, lse=None,
+                           workspace=None, stream=None):
+    """q [B, Hq, D]; caches [B, max_len, Hkv, D]; kv_len int32 [B] (device);
+    sel_blocks [B, top_k]; out [B, Hq, D]; lse [B, Hq]."""
+    B = q.shape[0]
+    top_k = sel_blocks.shape[-1]
+    ws = _ptr(workspace) if workspace is not None and workspace.numel() else None
+    nbytes = workspace.numel() * workspace.element_size() if ws else 0
+    if lse is not None and lse.dtype != torch.float32:
+        raise TypeError("lse must be float32")
+    _check(_lib.qsa_sparse_attn_decode(ctypes.byref(desc), block_size, top_k, _bf16(q, "q"),
+                                       _bf16(k_cache, "k_cache"), _bf16(v_cache, "v_cache"), k_cache.shape[1],
+                                       _i32t(kv_len, "kv_len"), B, _i32t(sel_blocks, "sel_blocks"),
+                                       _i32t(sel_count, "sel_count"), _bf16(out, "out"), _ptr(lse), ws, nbytes,
+                                       _stream(stream)))
+
+
+# ------------------------------------------------------------- comparator --
+def qsa_dense_attn_workspace_size(desc, batch, n_q, max_len):
+    return _lib.qsa_dense_attn_workspace_size(ctypes.byref(desc), batch, n_q, max_len)
+
+
+def qsa_dense_attn_prefill(desc, q, k, v, q_pos0, out, lse=None, workspace=None, stream=None):
+    ws = _ptr(workspace) if workspace is not None and workspace.numel() else None
+    nbytes = workspace.numel() * workspace.element_size() if ws else 0
+    _check(_lib.qsa_dense_attn_prefill(ctypes.byref(desc), _bf16(q, "q"), _bf16(k, "k"), _bf16(v, "v"), q_pos0,
+                                       q.shape[0], k.shape[0], _bf16(out, "out"), _ptr(lse), ws, nbytes,
+                                       _stream(stream)))
+
+
+def qsa_dense_attn_decode(desc, q, k_cache, v_cache, kv_len, out, lse=None, workspace=None, stream=None):
+    ws = _ptr(workspace) if workspace is not None and workspace.numel() else None
+    nbytes = workspace.numel() * workspace.element_size() if ws else 0
+    _check(_lib.qsa_dense_attn_decode(ctypes.byref(desc), _bf16(q, "q"), _bf16(k_cache, "k_cache"),
+                                      _bf16(v_cache, "v_cache"), k_cache.shape[1], _i32t(kv_len, "kv_len"),
+                                      q.shape[0], _bf16(out, "out"), _ptr(lse), ws, nbytes, _stream(stream)))
+
+
+# ------------------------------------------------- allocation conveniences --
+def workspace(nbytes, device="cuda"):
+    """A caller-owned scratch buffer (uint8) of at least nbytes."""
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
+def softmax_scale(head_dim=128):
+    return 1.0 / math.sqrt(head_dim)

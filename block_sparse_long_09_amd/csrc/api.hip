@@ -1,0 +1,311 @@
+// C ABI of the QSA library: host-side argument checks, workspace sizing and
+// kernel launches. Every check runs before anything is enqueued; on error
+// nothing is launched and qsa_last_error_message() says why.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "qsa.h"
+#include "qsa_bench.h"
+#include "qsa_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+qsa_status_t fail(qsa_status_t s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+qsa_status_t ok() {
+  g_err[0] = 0;
+  return QSA_OK;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+bool valid_block_size(int r) { return r == 1 || r == 2 || r == 4 || r == 8 || r == 16 || r == 32; }
+
+constexpr int kMaxK = 1024;
+constexpr int64_t kMaxPos = 0x7FFFFFFF;
+
+qsa_status_t check_index_desc(const qsa_index_desc_t* d) {
+  if (!d) return fail(QSA_ERR_INVALID_ARGUMENT, "index desc is NULL");
+  if (!valid_block_size(d->block_size))
+    return fail(QSA_ERR_UNSUPPORTED, "block_size %d not in {1,2,4,8,16,32}", d->block_size);
+  if (d->top_k_blocks < 1 || d->top_k_blocks > kMaxK)
+    return fail(QSA_ERR_UNSUPPORTED, "top_k_blocks %d not in [1, %d]", d->top_k_blocks, kMaxK);
+  const int h = d->n_idx_heads;
+  if (!(h == 1 || h == 2 || h == 4 || h == 8 || h == 16))
+    return fail(QSA_ERR_UNSUPPORTED, "n_idx_heads %d not in {1,2,4,8,16}", h);
+  if (d->idx_head_dim != 64) return fail(QSA_ERR_UNSUPPORTED, "idx_head_dim %d != 64", d->idx_head_dim);
+  if (!(d->idx_head_weight > 0.0f) || !isfinite(d->idx_head_weight))
+    return fail(QSA_ERR_INVALID_ARGUMENT, "idx_head_weight must be finite and > 0");
+  return QSA_OK;
+}
+
+qsa_status_t check_attn_desc(const qsa_attn_desc_t* d) {
+  if (!d) return fail(QSA_ERR_INVALID_ARGUMENT, "attn desc is NULL");
+  if (d->head_dim != 128) return fail(QSA_ERR_UNSUPPORTED, "head_dim %d != 128", d->head_dim);
+  const int hkv = d->n_kv_heads;
+  if (!(hkv == 1 || hkv == 2 || hkv == 4))
+    return fail(QSA_ERR_UNSUPPORTED, "n_kv_heads %d not in {1,2,4}", hkv);
+  if (d->n_q_heads < 1 || d->n_q_heads % hkv != 0)
+    return fail(QSA_ERR_INVALID_ARGUMENT, "n_q_heads %d not a positive multiple of n_kv_heads %d",
+                d->n_q_heads, hkv);
+  if (d->n_q_heads / hkv > 16)
+    return fail(QSA_ERR_UNSUPPORTED, "group size %d > 16", d->n_q_heads / hkv);
+  if (!isfinite(d->softmax_scale)) return fail(QSA_ERR_INVALID_ARGUMENT, "softmax_scale not finite");
+  return QSA_OK;
+}
+
+qsa_status_t hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(QSA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+}  // namespace
+
+extern "C" {
+
+int qsa_abi_version(void) { return QSA_ABI_VERSION; }
+
+const char* qsa_last_error_message(void) { return g_err; }
+
+const char* qsa_status_string(qsa_status_t s) {
+  switch (s) {
+    case QSA_OK: return "QSA_OK";
+    case QSA_ERR_INVALID_ARGUMENT: return "QSA_ERR_INVALID_ARGUMENT";
+    case QSA_ERR_UNSUPPORTED: return "QSA_ERR_UNSUPPORTED";
+    case QSA_ERR_MISALIGNED: return "QSA_ERR_MISALIGNED";
+    case QSA_ERR_WORKSPACE_TOO_SMALL: return "QSA_ERR_WORKSPACE_TOO_SMALL";
+    case QSA_ERR_HIP: return "QSA_ERR_HIP";
+  }
+  return "QSA_ERR_UNKNOWN";
+}
+
+qsa_status_t qsa_compress_keys(const uint16_t* idx_k, int64_t idx_k_batch_stride, int32_t batch,
+                               int32_t idx_head_dim, int32_t block_size, int64_t first_block,
+                               int64_t n_blocks, uint16_t* cmp_k, int64_t cmp_k_batch_stride,
+                               void* stream) {
+  if (batch < 0 || first_block < 0 || n_blocks < 0)
+    return fail(QSA_ERR_INVALID_ARGUMENT, "negative batch/first_block/n_blocks");
+  if (idx_head_dim != 64) return fail(QSA_ERR_UNSUPPORTED, "idx_head_dim %d != 64", idx_head_dim);
+  if (!valid_block_size(block_size))
+    return fail(QSA_ERR_UNSUPPORTED, "block_size %d not in {1,2,4,8,16,32}", block_size);
+  if (batch > 65535) return fail(QSA_ERR_UNSUPPORTED, "batch %d > 65535", batch);
+  if (batch == 0 || n_blocks == 0) return ok();
+  if (!idx_k || !cmp_k) return fail(QSA_ERR_INVALID_ARGUMENT, "NULL tensor pointer");
+  if (!aligned(idx_k, 16) || !aligned(cmp_k, 16))
+    return fail(QSA_ERR_MISALIGNED, "idx_k/cmp_k must be 16-byte aligned");
+  const int64_t end = first_block + n_blocks;
+  if (batch > 1) {
+    if (idx_k_batch_stride < end * block_size * idx_head_dim || cmp_k_batch_stride < end * idx_head_dim)
+      return fail(QSA_ERR_INVALID_ARGUMENT, "batch strides do not cover %lld blocks", (long long)end);
+    if (idx_k_batch_stride % 8 || cmp_k_batch_stride % 8)
+      return fail(QSA_ERR_MISALIGNED, "batch strides must be multiples of 8 elements");
+  }
+  return hip_status(qsa::launch_compress(idx_k, idx_k_batch_stride, batch, idx_head_dim, block_size,
+                                         first_block, n_blocks, cmp_k, cmp_k_batch_stride,
+                                         (hipStream_t)stream),
+                    "compress launch");
+}
+
+size_t qsa_index_topk_workspace_size(const qsa_index_desc_t* desc, int32_t batch, int32_t n_q,
+                                     int64_t max_q_end) {
+  if (check_index_desc(desc) != QSA_OK || batch < 0 || n_q < 0 || max_q_end < n_q ||
+      max_q_end > kMaxPos)
+    return 0;
+  if (batch == 0 || n_q == 0) return 0;
+  return qsa::plan_index(desc->n_idx_heads, desc->top_k_blocks, batch, n_q, max_q_end,
+                         desc->block_size)
+      .workspace;
+}
+
+qsa_status_t qsa_index_topk(const qsa_index_desc_t* desc, const uint16_t* idx_q,
+                            const uint16_t* cmp_k, int64_t cmp_k_batch_stride,
+                            const int32_t* q_pos0, int64_t max_q_end, int32_t batch, int32_t n_q,
+                            int32_t* sel_blocks, int32_t* sel_count, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  qsa_status_t s = check_index_desc(desc);
+  if (s != QSA_OK) return s;
+  if (batch < 0 || n_q < 0) return fail(QSA_ERR_INVALID_ARGUMENT, "negative batch or n_q");
+  if (batch > 65535) return fail(QSA_ERR_UNSUPPORTED, "batch %d > 65535", batch);
+  if (max_q_end < n_q || max_q_end > kMaxPos)
+    return fail(QSA_ERR_INVALID_ARGUMENT, "max_q_end %lld must be in [n_q, 2^31)", (long long)max_q_end);
+  if (batch == 0 || n_q == 0) return ok();
+  if (!idx_q || !cmp_k || !q_pos0 || !sel_blocks || !sel_count)
+    return fail(QSA_ERR_INVALID_ARGUMENT, "NULL pointer argument");
+  if (!aligned(idx_q, 16) || !aligned(cmp_k, 16))
+    return fail(QSA_ERR_MISALIGNED, "idx_q/cmp_k must be 16-byte aligned");
+  if (!aligned(q_pos0, 4) || !aligned(sel_blocks, 4) || !aligned(sel_count, 4))
+    return fail(QSA_ERR_MISALIGNED, "int32 arrays must be 4-byte aligned");
+  const int r = desc->block_size;
+  const int64_t need_blocks = (max_q_end - 1) / r;
+  if (batch > 1) {
+    if (cmp_k_batch_stride < need_blocks * desc->idx_head_dim)
+      return fail(QSA_ERR_INVALID_ARGUMENT, "cmp_k_batch_stride %lld < %lld blocks x 64",
+                  (long long)cmp_k_batch_stride, (long long)need_blocks);
+    if (cmp_k_batch_stride % 8) return fail(QSA_ERR_MISALIGNED, "cmp_k_batch_stride not a multiple of 8");
+  }
+  const qsa::IndexPlan p =
+      qsa::plan_index(desc->n_idx_heads, desc->top_k_blocks, batch, n_q, max_q_end, r);
+  if (workspace_bytes < p.workspace || (p.workspace && !workspace))
+    return fail(QSA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", workspace_bytes, p.workspace);
+  if (!aligned(workspace, 16)) return fail(QSA_ERR_MISALIGNED, "workspace must be 16-byte aligned");
+  return hip_status(qsa::launch_index_topk(p, idx_q, cmp_k, cmp_k_batch_stride, q_pos0, batch, n_q,
+                                           r, desc->top_k_blocks, desc->idx_head_weight,
+                                           sel_blocks, sel_count, workspace, (hipStream_t)stream),
+                    "index_topk launch");
+}
+
+size_t qsa_sparse_attn_workspace_size(const qsa_attn_desc_t* desc, int32_t batch, int32_t n_q,
+                                      int32_t top_k_blocks, int32_t block_size) {
+  if (check_attn_desc(desc) != QSA_OK || batch < 0 || n_q < 0 || top_k_blocks < 1 ||
+      top_k_blocks > kMaxK || !valid_block_size(block_size))
+    return 0;
+  // prefill (batch == 1, n_q rows) needs none; decode (n_q == 1) splits the token list
+  if (n_q == 1 && batch >= 1) {
+    const qsa::AttnPlan p = qsa::plan_attn(batch, (int64_t)top_k_blocks * block_size, true);
+    return qsa::attn_workspace_bytes(p, desc->n_q_heads);
+  }
+  return 0;
+}
+
+static qsa_status_t check_attn_common(const qsa_attn_desc_t* desc, int32_t block_size,
+                                      int32_t top_k_blocks) {
+  qsa_status_t s = check_attn_desc(desc);
+  if (s != QSA_OK) return s;
+  if (!valid_block_size(block_size))
+    return fail(QSA_ERR_UNSUPPORTED, "block_size %d not in {1,2,4,8,16,32}", block_size);
+  if (top_k_blocks < 1 || top_k_blocks > kMaxK)
+    return fail(QSA_ERR_UNSUPPORTED, "top_k_blocks %d not in [1, %d]", top_k_blocks, kMaxK);
+  return QSA_OK;
+}
+
+qsa_status_t qsa_sparse_attn_prefill(const qsa_attn_desc_t* desc, int32_t block_size,
+                                     int32_t top_k_blocks, const uint16_t* q, const uint16_t* k,
+                                     const uint16_t* v, int64_t q_pos0, int32_t n_q, int64_t kv_len,
+                                     const int32_t* sel_blocks, const int32_t* sel_count,
+                                     uint16_t* out, float* lse, void* workspace,
+                                     size_t workspace_bytes, void* stream) {
+  qsa_status_t s = check_attn_common(desc, block_size, top_k_blocks);
+  if (s != QSA_OK) return s;
+  if (q_pos0 < 0 || n_q < 0 || kv_len < q_pos0 + n_q || kv_len > kMaxPos)
+    return fail(QSA_ERR_INVALID_ARGUMENT, "need 0 <= q_pos0, q_pos0 + n_q <= kv_len < 2^31");
+  if (n_q == 0) return ok();
+  if (!q || !k || !v || !sel_blocks || !sel_count || !out)
+    return fail(QSA_ERR_INVALID_ARGUMENT, "NULL pointer argument");
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16))
+    return fail(QSA_ERR_MISALIGNED, "q/k/v/out must be 16-byte aligned");
+  if (!aligned(sel_blocks, 4) || !aligned(sel_count, 4) || !aligned(lse, 4))
+    return fail(QSA_ERR_MISALIGNED, "int32/fp32 arrays must be 4-byte aligned");
+  const qsa::AttnPlan p = qsa::plan_attn(n_q, (int64_t)top_k_blocks * block_size, false);
+  (void)workspace;
+  (void)workspace_bytes;
+  return hip_status(qsa::launch_attn(p, q, k, v, 0, q_pos0, nullptr, desc->n_q_heads,
+                                     desc->n_kv_heads, block_size, top_k_blocks, sel_blocks,
+                                     sel_count, desc->softmax_scale, out, lse, nullptr,
+                                     (hipStream_t)stream),
+                    "sparse_attn_prefill launch");
+}
+
+qsa_status_t qsa_sparse_attn_decode(const qsa_attn_desc_t* desc, int32_t block_size,
+                                    int32_t top_k_blocks, const uint16_t* q,
+                                    const uint16_t* k_cache, const uint16_t* v_cache,
+                                    int64_t max_len, const int32_t* kv_len, int32_t batch,
+                                    const int32_t* sel_blocks, const int32_t* sel_count,
+                                    uint16_t* out, float* lse, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
+  qsa_status_t s = check_attn_common(desc, block_size, top_k_blocks);
+  if (s != QSA_OK) return s;
+  if (batch < 0 || max_len < 1 || max_len > kMaxPos)
+    return fail(QSA_ERR_INVALID_ARGUMENT, "need batch >= 0 and 1 <= max_len < 2^31");
+  if (batch == 0) return ok();
+  if (!q || !k_cache || !v_cache || !kv_len || !sel_blocks || !sel_count || !out)
+    return fail(QSA_ERR_INVALID_ARGUMENT, "NULL pointer argument");
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16))
+    return fail(QSA_ERR_MISALIGNED, "q/k_cache/v_cache/out must be 16-byte aligned");
+  if (!aligned(kv_len, 4) || !aligned(sel_blocks, 4) || !aligned(sel_count, 4) || !aligned(lse, 4))
+    return fail(QSA_ERR_MISALIGNED, "int32/fp32 arrays must be 4-byte aligned");
+  const qsa::AttnPlan p = qsa::plan_attn(batch, (int64_t)top_k_blocks * block_size, true);
+  const size_t need = qsa::attn_workspace_bytes(p, desc->n_q_heads);
+  if (workspace_bytes < need || (need && !workspace))
+    return fail(QSA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", workspace_bytes, need);
+  if (!aligned(workspace, 16)) return fail(QSA_ERR_MISALIGNED, "workspace must be 16-byte aligned");
+  const int64_t stride = max_len * desc->n_kv_heads * desc->head_dim;
+  return hip_status(qsa::launch_attn(p, q, k_cache, v_cache, stride, 0, kv_len, desc->n_q_heads,
+                                     desc->n_kv_heads, block_size, top_k_blocks, sel_blocks,
+                                     sel_count, desc->softmax_scale, out, lse, workspace,
+                                     (hipStream_t)stream),
+                    "sparse_attn_decode launch");
+}
+
+/* ----------------------------------------------------------- comparator --- */
+
+size_t qsa_dense_attn_workspace_size(const qsa_attn_desc_t* desc, int32_t batch, int32_t n_q,
+                                     int64_t max_len) {
+  if (check_attn_desc(desc) != QSA_OK || batch < 0 || n_q < 0 || max_len < 1) return 0;
+  if (n_q == 1 && batch >= 1) {
+    const qsa::AttnPlan p = qsa::plan_attn(batch, max_len, true);
+    return qsa::attn_workspace_bytes(p, desc->n_q_heads);
+  }
+  return 0;
+}
+
+qsa_status_t qsa_dense_attn_prefill(const qsa_attn_desc_t* desc, const uint16_t* q,
+                                    const uint16_t* k, const uint16_t* v, int64_t q_pos0,
+                                    int32_t n_q, int64_t kv_len, uint16_t* out, float* lse,
+                                    void* workspace, size_t workspace_bytes, void* stream) {
+  qsa_status_t s = check_attn_desc(desc);
+  if (s != QSA_OK) return s;
+  if (q_pos0 < 0 || n_q < 0 || kv_len < q_pos0 + n_q || kv_len > kMaxPos)
+    return fail(QSA_ERR_INVALID_ARGUMENT, "need 0 <= q_pos0, q_pos0 + n_q <= kv_len < 2^31");
+  if (n_q == 0) return ok();
+  if (!q || !k || !v || !out) return fail(QSA_ERR_INVALID_ARGUMENT, "NULL pointer argument");
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16))
+    return fail(QSA_ERR_MISALIGNED, "q/k/v/out must be 16-byte aligned");
+  if (!aligned(lse, 4)) return fail(QSA_ERR_MISALIGNED, "lse must be 4-byte aligned");
+  (void)workspace;
+  (void)workspace_bytes;
+  const qsa::AttnPlan p = qsa::plan_attn(n_q, q_pos0 + n_q, false);
+  return hip_status(qsa::launch_attn(p, q, k, v, 0, q_pos0, nullptr, desc->n_q_heads,
+                                     desc->n_kv_heads, 1, 1, nullptr, nullptr,
+                                     desc->softmax_scale, out, lse, nullptr, (hipStream_t)stream),
+                    "dense_attn_prefill launch");
+}
+
+qsa_status_t qsa_dense_attn_decode(const qsa_attn_desc_t* desc, const uint16_t* q,
+                                   const uint16_t* k_cache, const uint16_t* v_cache,
+                                   int64_t max_len, const int32_t* kv_len, int32_t batch,
+                                   uint16_t* out, float* lse, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+  qsa_status_t s = check_attn_desc(desc);
+  if (s != QSA_OK) return s;
+  if (batch < 0 || max_len < 1 || max_len > kMaxPos)
+    return fail(QSA_ERR_INVALID_ARGUMENT, "need batch >= 0 and 1 <= max_len < 2^31");
+  if (batch == 0) return ok();
+  if (!q || !k_cache || !v_cache || !kv_len || !out)
+    return fail(QSA_ERR_INVALID_ARGUMENT, "NULL pointer argument");
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16))
+    return fail(QSA_ERR_MISALIGNED, "q/k_cache/v_cache/out must be 16-byte aligned");
+  if (!aligned(kv_len, 4) || !aligned(lse, 4))
+    return fail(QSA_ERR_MISALIGNED, "int32/fp32 arrays must be 4-byte aligned");
+  const qsa::AttnPlan p = qsa::plan_attn(batch, max_len, true);
+  const size_t need = qsa::attn_workspace_bytes(p, desc->n_q_heads);
+  if (workspace_bytes < need || (need && !workspace))
+    return fail(QSA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", workspace_bytes, need);
+  if (!aligned(workspace, 16)) return fail(QSA_ERR_MISALIGNED, "workspace must be 16-byte aligned");
+  const int64_t stride = max_len * desc->n_kv_heads * desc->head_dim;
+  return hip_status(qsa::launch_attn(p, q, k_cache, v_cache, stride, 0, kv_len, desc->n_q_heads,
+                                     desc->n_kv_heads, 1, 1, nullptr, nullptr,
+                                     desc->softmax_scale, out, lse, workspace,
+                                     (hipStream_t)stream),
+                    "dense_attn_decode launch");
+}
+
+}  // extern "C"

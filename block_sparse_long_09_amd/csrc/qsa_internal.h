@@ -1,0 +1,51 @@
+// Host-side plans and kernel launchers of the QSA library (internal).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace qsa {
+
+hipError_t launch_compress(const uint16_t* idx_k, int64_t k_stride, int batch, int d, int r,
+                           int64_t first, int64_t n, uint16_t* cmp, int64_t c_stride,
+                           hipStream_t stream);
+
+// How qsa_index_topk cuts its work: wave tasks = (query group, candidate split).
+struct IndexPlan {
+  int hi;          // indexer heads
+  int at;          // 32-row A tiles per wave (4 for prefill, 1 for few queries)
+  int qw;          // queries per wave
+  int n_qgroups;   // query groups per sequence
+  int splits;      // candidate splits
+  int split_len;   // candidates per split (multiple of 32)
+  int cap;         // buffer entries per (query, split)
+  int64_t max_cand;
+  size_t buf_bytes, cnt_bytes, workspace;
+};
+
+IndexPlan plan_index(int hi, int k, int batch, int n_q, int64_t max_q_end, int r);
+
+hipError_t launch_index_topk(const IndexPlan& p, const uint16_t* idx_q, const uint16_t* cmp_k,
+                             int64_t cmp_stride, const int32_t* q_pos0, int batch, int n_q, int r,
+                             int k, float w, int32_t* sel, int32_t* sel_cnt, void* ws,
+                             hipStream_t stream);
+
+// How the gather attention cuts its work: one workgroup per (row, split).
+struct AttnPlan {
+  int rows;
+  int splits;
+  int64_t split_tokens;
+};
+
+AttnPlan plan_attn(int batch_rows, int64_t max_tokens, bool split_kv);
+size_t attn_workspace_bytes(const AttnPlan& p, int Hq);
+
+// sel == nullptr: dense (tokens 0..t). kv_len == nullptr: prefill rows at
+// q_pos0 + row sharing one K/V; else decode rows with their own caches.
+hipError_t launch_attn(const AttnPlan& p, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                       int64_t kv_batch_stride, int64_t q_pos0, const int32_t* kv_len, int Hq,
+                       int Hkv, int r, int top_k, const int32_t* sel, const int32_t* sel_cnt,
+                       float scale, uint16_t* out, float* lse, void* ws, hipStream_t stream);
+
+}  // namespace qsa

@@ -1,0 +1,89 @@
+"""The QSA hot path as one call per prefill chunk or decode step.
+
+Sequence of library calls (every step runs in the HIP kernels of libqsa.so):
+  prefill chunk: qsa_compress_keys (the chunk's new complete blocks)
+                 -> qsa_index_topk -> qsa_sparse_attn_prefill
+  decode step:   qsa_index_topk (n_q = 1 per sequence at kv_len - 1)
+                 -> qsa_sparse_attn_decode
+The objects below only own the caller-side buffers (workspaces, selections,
+outputs) so that repeated calls allocate nothing.
+"""
+import torch
+
+from . import (attn_desc, index_desc, qsa_compress_keys, qsa_index_topk, qsa_index_topk_workspace_size,
+               qsa_sparse_attn_decode, qsa_sparse_attn_prefill, qsa_sparse_attn_workspace_size, workspace)
+
+
+class PrefillPath:
+    """Causal prefill of up to `n_q_max` queries against a prefix of at most
+    `max_len` tokens, for one sequence."""
+
+    def __init__(self, Hq, Hkv, Hi, r=4, k=512, n_q_max=8192, max_len=8192, D=128, di=64, device="cuda"):
+        self.r, self.k = r, k
+        self.idesc = index_desc(r, k, Hi, di)
+        self.adesc = attn_desc(Hq, Hkv, D)
+        self.ws_index = workspace(qsa_index_topk_workspace_size(self.idesc, 1, n_q_max, max_len), device)
+        self.ws_attn = workspace(qsa_sparse_attn_workspace_size(self.adesc, 1, n_q_max, k, r), device)
+        self.sel = torch.empty((n_q_max, k), dtype=torch.int32, device=device)
+        self.cnt = torch.empty((n_q_max,), dtype=torch.int32, device=device)
+        self.out = torch.empty((n_q_max, Hq, D), dtype=torch.bfloat16, device=device)
+        self.lse = torch.empty((n_q_max, Hq), dtype=torch.float32, device=device)
+        self.pos = torch.zeros((1,), dtype=torch.int32, device=device)
+        self.device = device
+
+    def compress(self, idx_k, cmp_k, q_pos0, n_q):
+        """Block keys of the complete blocks that end inside this chunk."""
+        first = q_pos0 // self.r
+        last = (q_pos0 + n_q) // self.r
+        qsa_compress_keys(idx_k, cmp_k, self.r, first, last - first)
+
+    def select(self, idx_q, cmp_k, q_pos0, n_q):
+        self.pos.fill_(q_pos0)
+        qsa_index_topk(self.idesc, idx_q[:n_q], cmp_k, self.pos, q_pos0 + n_q,
+                       self.sel[:n_q], self.cnt[:n_q], self.ws_index)
+        return self.sel[:n_q], self.cnt[:n_q]
+
+    def attend(self, q, k, v, q_pos0, n_q, sel=None, cnt=None):
+        sel = self.sel[:n_q] if sel is None else sel
+        cnt = self.cnt[:n_q] if cnt is None else cnt
+        qsa_sparse_attn_prefill(self.adesc, self.r, q[:n_q], k[:q_pos0 + n_q], v[:q_pos0 + n_q], q_pos0,
+                                sel, cnt, self.out[:n_q], self.lse[:n_q], self.ws_attn)
+        return self.out[:n_q], self.lse[:n_q]
+
+    def __call__(self, q, k, v, idx_q, idx_k, cmp_k, q_pos0, n_q):
+        self.compress(idx_k, cmp_k, q_pos0, n_q)
+        self.select(idx_q, cmp_k, q_pos0, n_q)
+        return self.attend(q, k, v, q_pos0, n_q)
+
+
+class DecodePath:
+    """One decode step for `batch` sequences with caches of `max_len` tokens."""
+
+    def __init__(self, Hq, Hkv, Hi, batch, max_len, r=4, k=512, D=128, di=64, device="cuda"):
+        self.r, self.k, self.batch = r, k, batch
+        self.idesc = index_desc(r, k, Hi, di)
+        self.adesc = attn_desc(Hq, Hkv, D)
+        self.ws_index = workspace(qsa_index_topk_workspace_size(self.idesc, batch, 1, max_len), device)
+        self.ws_attn = workspace(qsa_sparse_attn_workspace_size(self.adesc, batch, 1, k, r), device)
+        self.sel = torch.empty((batch, 1, k), dtype=torch.int32, device=device)
+        self.cnt = torch.empty((batch, 1), dtype=torch.int32, device=device)
+        self.out = torch.empty((batch, Hq, D), dtype=torch.bfloat16, device=device)
+        self.lse = torch.empty((batch, Hq), dtype=torch.float32, device=device)
+        self.max_len = max_len
+
+    def select(self, idx_q, cmp_k, q_pos, max_q_end=None):
+        """idx_q [B, Hi, di]; q_pos int32 [B] = kv_len - 1 (device)."""
+        qsa_index_topk(self.idesc, idx_q[:, None], cmp_k, q_pos, self.max_len if max_q_end is None else max_q_end,
+                       self.sel, self.cnt, self.ws_index)
+        return self.sel[:, 0], self.cnt[:, 0]
+
+    def attend(self, q, k_cache, v_cache, kv_len, sel=None, cnt=None):
+        sel = self.sel[:, 0] if sel is None else sel
+        cnt = self.cnt[:, 0] if cnt is None else cnt
+        qsa_sparse_attn_decode(self.adesc, self.r, q, k_cache, v_cache, kv_len, sel.contiguous(),
+                               cnt.contiguous(), self.out, self.lse, self.ws_attn)
+        return self.out, self.lse
+
+    def __call__(self, q, k_cache, v_cache, idx_q, cmp_k, kv_len, q_pos):
+        self.select(idx_q, cmp_k, q_pos)
+        return self.attend(q, k_cache, v_cache, kv_len)

@@ -1,0 +1,157 @@
+/*
+ * qsa.h — C ABI of the QSA (Qwen Sparse Attention) hot path on AMD Instinct
+ * MI355X (gfx950).
+ *
+ * The method (web pages on the Qwen3.8-Flash-Next release):
+ *   - "用125亿分之6的参数，打平3970亿的旗舰模型", section
+ *     "稀疏注意力：给检索建索引，也得先学会省纸": runs of r consecutive tokens
+ *     form micro-blocks whose indexer key is the mean of the tokens' keys; a
+ *     light multi-query indexer scores each block; the best blocks are kept,
+ *     expanded back to their tokens, and exact attention runs over those
+ *     tokens only.
+ *   - "On the Design of Qwen3.8-Next Architecture" (agihunt.info digest of
+ *     arXiv 2608.30320), token-mixing paragraph: the indexer works on
+ *     micro-blocks so its cost falls from O(n^2) to O(n^2 / r); the deployed
+ *     setting is a 2048-token budget with compression ratio 4.
+ *
+ * Conventions shared by every entry point:
+ *   - Tensor pointers are DEVICE pointers owned by the caller. bf16 tensors are
+ *     passed as uint16_t bit patterns. Layouts are row-major, innermost
+ *     dimension last, dense unless a stride argument says otherwise (strides
+ *     are in elements). Every tensor pointer must be 16-byte aligned.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     Calls only enqueue work: they never synchronise and never allocate.
+ *     Scratch memory comes from the caller's `workspace` (size from the
+ *     matching *_workspace_size query; contents need not be initialised and
+ *     are clobbered; one workspace must not be used by two calls in flight).
+ *   - Arguments are checked on the host before anything is enqueued. On any
+ *     error nothing is launched, outputs are untouched, and a detail message
+ *     is available from qsa_last_error_message() (thread-local).
+ *   - Device-side faults from bad device data (e.g. out-of-range block ids
+ *     passed to the attention calls) are not detected; they surface at the
+ *     caller's next synchronisation.
+ *   - Supported shapes: indexer dim d_i = 64, indexer heads 1..16, head dim
+ *     D = 128, Hq / Hkv in 1..16 with Hkv in {1, 2, 4}, block size r in
+ *     {1, 2, 4, 8, 16, 32}, 1 <= k <= 1024. Others return QSA_ERR_UNSUPPORTED.
+ */
+#ifndef QSA_H_
+#define QSA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define QSA_ABI_VERSION 1
+
+typedef enum {
+  QSA_OK = 0,
+  QSA_ERR_INVALID_ARGUMENT = 1, /* null pointer, negative size, inconsistent shapes */
+  QSA_ERR_UNSUPPORTED = 2,      /* a shape outside the supported set above */
+  QSA_ERR_MISALIGNED = 3,       /* a tensor pointer or stride breaks 16-byte alignment */
+  QSA_ERR_WORKSPACE_TOO_SMALL = 4,
+  QSA_ERR_HIP = 5               /* the HIP runtime reported an error at launch */
+} qsa_status_t;
+
+/* Indexer settings. */
+typedef struct {
+  int32_t block_size;      /* r: tokens per micro-block */
+  int32_t top_k_blocks;    /* k: blocks kept per query, the query's own block included */
+  int32_t n_idx_heads;     /* H_i: indexer query heads (they share one key) */
+  int32_t idx_head_dim;    /* d_i: indexer dim (64) */
+  float idx_head_weight;   /* w: weight of every indexer head (1 / H_i) */
+} qsa_index_desc_t;
+
+/* Attention settings (grouped-query attention). */
+typedef struct {
+  int32_t n_q_heads;       /* Hq */
+  int32_t n_kv_heads;      /* Hkv; query head h reads KV head h / (Hq / Hkv) */
+  int32_t head_dim;        /* D (128) */
+  float softmax_scale;     /* multiplies q.k before the softmax (1 / sqrt(D)) */
+} qsa_attn_desc_t;
+
+/* Micro-block key compression (explainer page, sparse-attention section:
+ * the block key is the mean of its r token keys).
+ *   idx_k  [batch][*][d]: token indexer keys; row b starts at idx_k + b * idx_k_batch_stride.
+ *   cmp_k  [batch][*][d]: block keys; row b starts at cmp_k + b * cmp_k_batch_stride.
+ * For every b < batch and block j in [first_block, first_block + n_blocks):
+ *   cmp_k[b][j][i] = bf16_rne( (((k[jr][i] + k[jr+1][i]) + ...) + k[jr+r-1][i]) / r ),
+ * the sum taken in fp32 left to right. Only complete blocks exist: the caller
+ * passes blocks whose r tokens are all present. d = idx_head_dim must be 64. */
+qsa_status_t qsa_compress_keys(const uint16_t* idx_k, int64_t idx_k_batch_stride, int32_t batch,
+                               int32_t idx_head_dim, int32_t block_size, int64_t first_block,
+                               int64_t n_blocks, uint16_t* cmp_k, int64_t cmp_k_batch_stride,
+                               void* stream);
+
+/* Bytes of workspace qsa_index_topk needs for these sizes (0 on bad input).
+ * max_q_end: an upper bound on q_pos0[b] + n_q over the batch. */
+size_t qsa_index_topk_workspace_size(const qsa_index_desc_t* desc, int32_t batch, int32_t n_q,
+                                     int64_t max_q_end);
+
+/* Indexer scoring + causal top-k block selection (explainer page,
+ * sparse-attention section; digest page, token-mixing paragraph).
+ *   idx_q     [batch][n_q][H_i][d_i] indexer queries; query i of row b sits at
+ *             position t = q_pos0[b] + i.
+ *   cmp_k     block keys of each row (see qsa_compress_keys); row b must hold
+ *             at least (q_pos0[b] + n_q - 1) / r blocks.
+ *   q_pos0    DEVICE int32 [batch]: position of each row's first query;
+ *             q_pos0[b] + n_q <= max_q_end must hold.
+ * For query t with own block b_t = t / r, the scored candidates are the
+ * blocks j < b_t, each with score s = w * sum_h max(0, q_h . c_j) (fp32). The
+ * min(k - 1, b_t) best candidates, ordered by (score desc, index asc), plus b_t
+ * itself are kept.
+ *   sel_blocks [batch][n_q][k] int32: kept blocks in ascending order, then -1.
+ *   sel_count  [batch][n_q] int32: number of kept blocks, min(k, b_t + 1).
+ * Decode is the case n_q = 1 with q_pos0[b] = kv_len[b] - 1. */
+qsa_status_t qsa_index_topk(const qsa_index_desc_t* desc, const uint16_t* idx_q,
+                            const uint16_t* cmp_k, int64_t cmp_k_batch_stride,
+                            const int32_t* q_pos0, int64_t max_q_end, int32_t batch, int32_t n_q,
+                            int32_t* sel_blocks, int32_t* sel_count, void* workspace,
+                            size_t workspace_bytes, void* stream);
+
+/* Bytes of workspace the sparse attention calls need (0 on bad input). */
+size_t qsa_sparse_attn_workspace_size(const qsa_attn_desc_t* desc, int32_t batch, int32_t n_q,
+                                      int32_t top_k_blocks, int32_t block_size);
+
+/* Sparse attention, prefill (news page, section 2 item 1: full-precision
+ * attention on the relevant blocks only; explainer page: kept blocks are
+ * expanded back to their tokens).
+ *   q    [n_q][Hq][D]; query i sits at position t = q_pos0 + i.
+ *   k, v [kv_len][Hkv][D]; q_pos0 + n_q <= kv_len.
+ *   sel_blocks [n_q][top_k_blocks], sel_count [n_q]: as written by qsa_index_topk.
+ * Tokens attended by query t: every s = j * r + m (m < r) of every listed
+ * block j with s <= t. o = softmax(scale * q.K^T) V, exact, fp32 accumulation.
+ *   out  [n_q][Hq][D] bf16;  lse [n_q][Hq] fp32 natural-log sum-exp of the
+ *   scaled logits (may be NULL). */
+qsa_status_t qsa_sparse_attn_prefill(const qsa_attn_desc_t* desc, int32_t block_size,
+                                     int32_t top_k_blocks, const uint16_t* q, const uint16_t* k,
+                                     const uint16_t* v, int64_t q_pos0, int32_t n_q, int64_t kv_len,
+                                     const int32_t* sel_blocks, const int32_t* sel_count,
+                                     uint16_t* out, float* lse, void* workspace,
+                                     size_t workspace_bytes, void* stream);
+
+/* Sparse attention, decode: one query per sequence at position kv_len[b] - 1.
+ *   q        [batch][Hq][D]
+ *   k_cache, v_cache [batch][max_len][Hkv][D]
+ *   kv_len   DEVICE int32 [batch], 1 <= kv_len[b] <= max_len.
+ *   sel_blocks [batch][top_k_blocks], sel_count [batch].
+ *   out [batch][Hq][D] bf16; lse [batch][Hq] fp32 (may be NULL). */
+qsa_status_t qsa_sparse_attn_decode(const qsa_attn_desc_t* desc, int32_t block_size,
+                                    int32_t top_k_blocks, const uint16_t* q,
+                                    const uint16_t* k_cache, const uint16_t* v_cache,
+                                    int64_t max_len, const int32_t* kv_len, int32_t batch,
+                                    const int32_t* sel_blocks, const int32_t* sel_count,
+                                    uint16_t* out, float* lse, void* workspace,
+                                    size_t workspace_bytes, void* stream);
+
+const char* qsa_status_string(qsa_status_t status);
+const char* qsa_last_error_message(void);
+int qsa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QSA_H_ */
