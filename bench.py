@@ -1,0 +1,435 @@
+#!/usr/bin/env python3
+"""Benchmark of the QSA hot path on one MI355X.
+
+Default workload: the 1M-token context configuration. One step =
+  prefill chunk: compress the chunk's 4096 new blocks, index + causal top-k for
+                 16384 queries at positions 1,032,192 .. 1,048,575, sparse
+                 attention over their kept tokens (Q [16384,32,128],
+                 K/V [1M,4,128], indexer 8 x 64, r = 4, budget 2048 tokens);
+  decode step:   index + top-k and sparse attention for 4 sequences whose
+                 query sits at position 1,048,575 (caches [4,1M,4,128], block
+                 keys precomputed).
+All inputs are seeded synthetic tensors resident in HBM before timing starts.
+Prints one JSON line (see README of the fields in the design doc).
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--config c5|c3|c4]
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "QSA prefill tokens/s @256K–1M ctx; decode µs/step; % of HBM/MFMA roofline"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFS = 2500.0    # MI355X dense bf16 MFMA, TFLOP/s
+PAGES_SPEEDUP = {"prefill": 7.6, "decode": 4.9, "context": "1M tokens, QSA vs GQA attention, hardware not stated"}
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+# --------------------------------------------------------------- work model --
+def prefill_work(W, q_pos0, n_q):
+    """Algorithmic bytes / flops of one prefill chunk (what the method must touch)."""
+    t = np.arange(q_pos0, q_pos0 + n_q, dtype=np.int64)
+    b = t // W.r
+    m = np.minimum(W.k - 1, b)
+    ntok = m * W.r + (t - b * W.r) + 1
+    new_blocks = (q_pos0 + n_q) // W.r - q_pos0 // W.r
+    row_kv = W.Hkv * W.D * 2
+    w = {}
+    w["compress_bytes"] = new_blocks * (W.r * W.di * 2 + W.di * 2)
+    w["index_pairs"] = int(b.sum())
+    w["index_flops"] = int(b.sum()) * W.Hi * W.di * 2
+    w["index_bytes"] = n_q * W.Hi * W.di * 2 + int(b.max()) * W.di * 2 + n_q * (W.k + 1) * 4
+    w["attn_tokens"] = int(ntok.sum())
+    w["attn_flops"] = int(ntok.sum()) * W.Hq * W.D * 4
+    w["attn_bytes"] = int(ntok.sum()) * row_kv * 2 + 2 * n_q * W.Hq * W.D * 2 + n_q * (W.k + 1) * 4
+    w["dense_flops"] = int((t + 1).sum()) * W.Hq * W.D * 4
+    return w
+
+
+def decode_work(W):
+    t = W.L - 1
+    b = t // W.r
+    m = min(W.k - 1, b)
+    ntok = m * W.r + (t - b * W.r) + 1
+    B = W.batch
+    w = {}
+    w["index_flops"] = B * b * W.Hi * W.di * 2
+    w["index_bytes"] = B * (b * W.di * 2 + W.Hi * W.di * 2 + (W.k + 1) * 4)
+    w["attn_bytes"] = B * (ntok * W.Hkv * W.D * 2 * 2 + 2 * W.Hq * W.D * 2 + (W.k + 1) * 4)
+    w["dense_bytes"] = B * ((t + 1) * W.Hkv * W.D * 2 * 2 + 2 * W.Hq * W.D * 2)
+    return w
+
+
+def source_sha(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "block_sparse_long_09_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel_key, sha):
+    """Counter-derived HBM bytes per launch from the committed profile summary,
+    if it was taken on the current kernel source; else None."""
+    p = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        d = json.load(f)
+    e = d.get(kernel_key)
+    if not e or e.get("source_sha") != sha:
+        return None
+    return e.get("bytes_per_launch")
+
+
+# ------------------------------------------------------------------ timing --
+class PhaseTimer:
+    def __init__(self, torch, names):
+        self.torch = torch
+        self.names = names
+        self.acc = {n: [] for n in names}
+
+    def run(self, fns):
+        T = self.torch
+        evs = [T.cuda.Event(enable_timing=True) for _ in range(len(fns) + 1)]
+        evs[0].record()
+        for i, f in enumerate(fns):
+            f()
+            evs[i + 1].record()
+        return evs
+
+    def collect(self, evs):
+        for i, n in enumerate(self.names):
+            self.acc[n].append(evs[i].elapsed_time(evs[i + 1]))
+
+    def mean_ms(self):
+        return {n: float(np.mean(v)) if v else None for n, v in self.acc.items()}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="c5", choices=["c5", "c3", "c4"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--dense-prefill", action="store_true", help="also time dense prefill (slow comparator)")
+    ap.add_argument("--cpu-sample", type=int, default=256, help="queries in the oracle's timed sample")
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="also run one plain device copy of this size (counter calibration runs)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU; --gpus {args.gpus} is not supported "
+              "(the path shards by sequence or query chunk, see DESIGN.md, but no multi-GPU run exists)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import block_sparse_long_09_amd as qsa
+    from block_sparse_long_09_amd.pipeline import DecodePath, PrefillPath
+    from gen.configs import CONFIGS
+    from gen.device import idx_keys_to_device, normal_to_device
+
+    torch.cuda.set_device(0)
+    dev = "cuda"
+    if args.config == "c5":
+        Wp, Wd = CONFIGS["c5a"], CONFIGS["c5b"]
+    elif args.config == "c3":
+        Wp, Wd = CONFIGS["c3"], None
+    else:
+        Wp, Wd = None, CONFIGS["c4"]
+
+    t_setup = time.time()
+    # ------------------------------------------------------------- inputs --
+    P = {}
+    if Wp is not None:
+        W = Wp
+        log(f"generating prefill inputs {W.name}")
+        P["K"] = normal_to_device(W.seed, 2, (W.L, W.Hkv, W.D))
+        P["V"] = normal_to_device(W.seed, 3, (W.L, W.Hkv, W.D))
+        P["Q"] = normal_to_device(W.seed, 1, (W.n_q, W.Hq, W.D))
+        P["iq"] = normal_to_device(W.seed, 4, (W.n_q, W.Hi, W.di))
+        P["ik"] = idx_keys_to_device(W.seed, 1, W.L, W.di, W.needle_window, W.r)[0]
+        P["cmp"] = torch.zeros((W.n_blk, W.di), dtype=torch.bfloat16, device=dev)
+        chunk = W.chunk if W.chunk else W.n_q
+        P["chunk"] = chunk
+        # blocks before the first query are cached (as the prefix KV is)
+        if W.q_pos0 // W.r:
+            qsa.qsa_compress_keys(P["ik"], P["cmp"], W.r, 0, W.q_pos0 // W.r)
+        P["path"] = PrefillPath(W.Hq, W.Hkv, W.Hi, W.r, W.k, n_q_max=chunk, max_len=W.q_pos0 + W.n_q,
+                                D=W.D, di=W.di, device=dev)
+    D = {}
+    if Wd is not None:
+        W = Wd
+        log(f"generating decode inputs {W.name}")
+        D["Kc"] = normal_to_device(W.seed, 2, (W.batch, W.L, W.Hkv, W.D))
+        D["Vc"] = normal_to_device(W.seed, 3, (W.batch, W.L, W.Hkv, W.D))
+        D["Q"] = normal_to_device(W.seed, 1, (W.batch, W.Hq, W.D))
+        D["iq"] = normal_to_device(W.seed, 4, (W.batch, W.Hi, W.di))
+        ik = idx_keys_to_device(W.seed, W.batch, W.L, W.di, W.needle_window, W.r)
+        D["cmp"] = torch.empty((W.batch, W.n_blk, W.di), dtype=torch.bfloat16, device=dev)
+        qsa.qsa_compress_keys(ik, D["cmp"], W.r, 0, W.n_blk)  # precomputed block keys
+        torch.cuda.synchronize()
+        del ik
+        D["kv_len"] = torch.full((W.batch,), W.L, dtype=torch.int32, device=dev)
+        D["q_pos"] = D["kv_len"] - 1
+        D["path"] = DecodePath(W.Hq, W.Hkv, W.Hi, W.batch, W.L, r=W.r, k=W.k, D=W.D, di=W.di, device=dev)
+    torch.cuda.synchronize()
+    log(f"setup {time.time() - t_setup:.1f}s")
+
+    # ------------------------------------------------------------ the step --
+    names = []
+    fns = []
+    if Wp is not None:
+        W, path = Wp, P["path"]
+        chunk = P["chunk"]
+        for c0 in range(0, W.n_q, chunk):
+            q0 = W.q_pos0 + c0
+            sfx = f"_{c0 // chunk}" if chunk != W.n_q else ""
+            names += [f"compress{sfx}", f"index_prefill{sfx}", f"attn_prefill{sfx}"]
+            fns += [
+                (lambda q0=q0: path.compress(P["ik"], P["cmp"], q0, chunk)),
+                (lambda q0=q0, c0=c0: path.select(P["iq"][c0:c0 + chunk], P["cmp"], q0, chunk)),
+                (lambda q0=q0, c0=c0: path.attend(P["Q"][c0:c0 + chunk], P["K"], P["V"], q0, chunk)),
+            ]
+    if Wd is not None:
+        dp = D["path"]
+        names += ["index_decode", "attn_decode"]
+        fns += [lambda: dp.select(D["iq"], D["cmp"], D["q_pos"]),
+                lambda: dp.attend(D["Q"], D["Kc"], D["Vc"], D["kv_len"])]
+    timer = PhaseTimer(torch, names)
+
+    for _ in range(args.warmup):
+        timer.run(fns)
+    torch.cuda.synchronize()
+    # phase timing (events between launches, on the launch stream)
+    recorded = [timer.run(fns) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for evs in recorded:
+        timer.collect(evs)
+    # whole-step wall clock over exactly `steps` steps
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        for f in fns:
+            f()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / args.steps
+    phase = timer.mean_ms()
+
+    def ssum(prefix):
+        v = [x for n, x in phase.items() if n.startswith(prefix)]
+        return sum(v) if v else 0.0
+
+    prefill_ms = ssum("compress") + ssum("index_prefill") + ssum("attn_prefill")
+    decode_ms = ssum("index_decode") + ssum("attn_decode")
+
+    # --------------------------------------------------------------- roofline --
+    roof = {}
+    sha_attn = source_sha("sparse_attn.hip")
+    sha_idx = source_sha("index_topk.hip")
+    if Wp is not None:
+        W = Wp
+        work = {"compress_bytes": 0, "index_flops": 0, "index_bytes": 0, "attn_bytes": 0, "attn_flops": 0,
+                "attn_tokens": 0, "index_pairs": 0, "dense_flops": 0}
+        chunk = P["chunk"]
+        for c0 in range(0, W.n_q, chunk):
+            wk = prefill_work(W, W.q_pos0 + c0, chunk)
+            for key in work:
+                work[key] += wk[key]
+        n_ch = W.n_q // chunk
+        ms_attn, ms_idx = ssum("attn_prefill"), ssum("index_prefill")
+        roof["attn_prefill"] = {
+            "bound": "hbm", "achieved": work["attn_bytes"] / (ms_attn * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "traffic": load_traffic(f"attn_prefill_{args.config}", sha_attn),
+            "bytes_per_launch": work["attn_bytes"] // n_ch, "avg_launch_ms": ms_attn / n_ch,
+            "mfma_tflops": work["attn_flops"] / (ms_attn * 1e-3) / 1e12}
+        roof["index_prefill"] = {
+            "bound": "mfma", "achieved": work["index_flops"] / (ms_idx * 1e-3) / 1e12, "peak": MFMA_BF16_PEAK_TFS,
+            "unit": "TFLOP/s", "traffic": load_traffic(f"index_prefill_{args.config}", sha_idx),
+            "flops_per_launch": work["index_flops"] // n_ch, "avg_launch_ms": ms_idx / n_ch}
+        P["work"] = work
+    if Wd is not None:
+        W = Wd
+        wd = decode_work(W)
+        ms = decode_ms
+        roof["decode"] = {"bound": "hbm", "achieved": (wd["index_bytes"] + wd["attn_bytes"]) / (ms * 1e-3) / 1e9,
+                          "peak": HBM_PEAK_GBS, "unit": "GB/s", "traffic": None,
+                          "bytes_per_step": wd["index_bytes"] + wd["attn_bytes"]}
+        D["work"] = wd
+    for v in roof.values():
+        v["frac"] = v["achieved"] / v["peak"]
+    # the dominant kernel: the phase with the largest total time
+    totals = {"attn_prefill": ssum("attn_prefill"), "index_prefill": ssum("index_prefill"), "decode": decode_ms}
+    dom = max((n for n in roof), key=lambda n: totals[n]) if roof else None
+
+    # -------------------------------------------------------------- dense ----
+    dense = None
+    if not args.no_dense:
+        dense = {}
+        if Wd is not None:
+            W = Wd
+            desc = qsa.attn_desc(W.Hq, W.Hkv, W.D)
+            ws = qsa.workspace(qsa.qsa_dense_attn_workspace_size(desc, W.batch, 1, W.L))
+            dout = torch.empty((W.batch, W.Hq, W.D), dtype=torch.bfloat16, device=dev)
+            f = lambda: qsa.qsa_dense_attn_decode(desc, D["Q"], D["Kc"], D["Vc"], D["kv_len"], dout, None, ws)
+            for _ in range(2):
+                f()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(5):
+                f()
+            e1.record()
+            torch.cuda.synchronize()
+            dms = e0.elapsed_time(e1) / 5
+            dense["decode_us"] = dms * 1e3
+            dense["decode_GBps"] = D["work"]["dense_bytes"] / (dms * 1e-3) / 1e9
+            dense["decode_speedup_sparse_vs_dense"] = dms / decode_ms
+        if Wp is not None and args.dense_prefill:
+            W = Wp
+            desc = qsa.attn_desc(W.Hq, W.Hkv, W.D)
+            dout = torch.empty((P["chunk"], W.Hq, W.D), dtype=torch.bfloat16, device=dev)
+            chunk = P["chunk"]
+
+            def fd():
+                for c0 in range(0, W.n_q, chunk):
+                    qsa.qsa_dense_attn_prefill(desc, P["Q"][c0:c0 + chunk], P["K"][:W.q_pos0 + c0 + chunk],
+                                               P["V"][:W.q_pos0 + c0 + chunk], W.q_pos0 + c0, dout)
+            fd()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fd()
+            e1.record()
+            torch.cuda.synchronize()
+            pms = e0.elapsed_time(e1)
+            dense["prefill_ms"] = pms
+            dense["prefill_TFLOPs"] = P["work"]["dense_flops"] / (pms * 1e-3) / 1e12
+            dense["prefill_speedup_sparse_vs_dense"] = pms / prefill_ms
+            dense["prefill_attention_only_speedup"] = pms / ssum("attn_prefill")
+
+    # --------------------------------------------------------- calibration ---
+    if args.calibrate_copy_mib:
+        n = args.calibrate_copy_mib << 20
+        a = torch.empty(n, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+
+    # ---------------------------------------------------------- CPU oracle ---
+    cpu = None
+    sample_parity = None
+    if not args.no_cpu_baseline and Wp is not None and P["chunk"] == Wp.n_q:
+        cpu, sample_parity = cpu_baseline(Wp, P, args.cpu_sample)
+
+    W = Wp if Wp is not None else Wd
+    value = (Wp.n_q if Wp is not None else Wd.batch) / wall
+    out = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": wall * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": (Wp.name + " + " + Wd.name) if (Wp and Wd) else W.name,
+                   "prefill_queries": Wp.n_q if Wp else 0, "context": W.L, "budget_tokens": W.k * W.r,
+                   "block_size": W.r, "heads_q_kv_idx": [W.Hq, W.Hkv, W.Hi],
+                   "decode_batch": Wd.batch if Wd else 0},
+        "prefill_ms": prefill_ms,
+        "prefill_tokens_per_s": (Wp.n_q / (prefill_ms * 1e-3)) if Wp else None,
+        "decode_us_per_step": decode_ms * 1e3 if Wd else None,
+        "phase_ms": phase,
+        "roofline": dict(roof[dom], kernel=dom) if dom else None,
+        "rooflines": roof,
+        "dense": dense,
+        "pages_speedup_context": PAGES_SPEEDUP,
+        "cpu_baseline": cpu,
+        "sample_parity": sample_parity,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(W, P, n_sample):
+    """Time the oracle on a bounded sample of the prefill chunk's queries (plus
+    the chunk's block compression) on the host cores; also compare the GPU
+    outputs of those rows."""
+    import torch
+
+    import gen
+    import oracle
+
+    n_q = W.n_q
+    run = 32  # consecutive queries per oracle call (OpenMP parallelises over them)
+    n_runs = max(1, n_sample // run)
+    starts = np.unique(np.linspace(0, n_q - run, n_runs).astype(np.int64))
+    rows = np.concatenate([np.arange(s0, s0 + run) for s0 in starts])
+    log(f"cpu baseline: generating host inputs, {len(rows)} sampled queries")
+    ik = gen.idx_keys(W.seed, 0, W.L, 0, W.L, W.di, W.needle_window, W.r)
+    K = gen.normal(W.seed, 2, (W.L, W.Hkv, W.D))
+    V = gen.normal(W.seed, 3, (W.L, W.Hkv, W.D))
+    Qr = [gen.normal(W.seed, 1, (run, W.Hq, W.D), e0=int(s0) * W.Hq * W.D) for s0 in starts]
+    iqr = [gen.normal(W.seed, 4, (run, W.Hi, W.di), e0=int(s0) * W.Hi * W.di) for s0 in starts]
+    n_prefix = W.q_pos0 // W.r
+    blocks = np.empty((W.n_blk, W.di), np.uint16)
+    blocks[:n_prefix] = oracle.compress(ik[:n_prefix * W.r], W.r)  # cached prefix, like the GPU's
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    t0 = time.perf_counter()
+    blocks[n_prefix:] = oracle.compress(ik[n_prefix * W.r:], W.r)
+    t_comp = time.perf_counter() - t0
+    sels, cnts = [], []
+    t1 = time.perf_counter()
+    for i, s0 in enumerate(starts):
+        s, c, _, _ = oracle.select(iqr[i], blocks, W.q_pos0 + int(s0), W.r, W.k, W.w)
+        sels.append(s)
+        cnts.append(c)
+    t_sel = time.perf_counter() - t1
+    t2 = time.perf_counter()
+    outs, lses = [], []
+    for i, s0 in enumerate(starts):
+        o, l = oracle.sparse_attn(Qr[i], K, V, W.q_pos0 + int(s0), W.r, sels[i], cnts[i])
+        outs.append(o)
+        lses.append(l)
+    t_att = time.perf_counter() - t2
+    sel = np.concatenate(sels)
+    outs = list(zip(np.concatenate(outs), np.concatenate(lses)))
+    # per-query time of the sample, plus the chunk compression amortised over all queries
+    per_q = (t_sel + t_att) / len(rows) + t_comp / n_q
+    cpu = {"value": 1.0 / per_q, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+           "sample": f"{len(rows)} of {n_q} prefill queries ({len(starts)} runs of {run} consecutive, evenly "
+                     f"spaced) of {W.name}, plus the chunk's block compression; select {t_sel:.2f}s, "
+                     f"attend {t_att:.2f}s, compress {t_comp:.2f}s"}
+    # parity of the sampled rows (the GPU ran the same inputs)
+    path = P["path"]
+    g_sel = path.sel.cpu().numpy()
+    g_cnt = path.cnt.cpu().numpy()
+    g_out = path.out.float().cpu().numpy()
+    g_lse = path.lse.cpu().numpy()
+    same_sel = sum(int(np.array_equal(g_sel[r_], sel[i])) for i, r_ in enumerate(rows))
+    err = max(float(np.abs(g_out[r_] - outs[i][0]).max()) for i, r_ in enumerate(rows)
+              if np.array_equal(g_sel[r_], sel[i]))
+    lerr = max(float(np.abs(g_lse[r_] - outs[i][1]).max()) for i, r_ in enumerate(rows)
+               if np.array_equal(g_sel[r_], sel[i]))
+    return cpu, {"rows": len(rows), "selection_identical_rows": same_sel, "out_max_abs": err, "lse_max_abs": lerr}
+
+
+if __name__ == "__main__":
+    main()
