@@ -9,147 +9,140 @@
 // Kept: the min(k - 1, b_t) best blocks j < b_t = t / r in (score desc,
 // index asc) order, plus b_t itself; emitted in ascending block order.
 //
-// Kernel 1, index_stream_kernel: one wave owns QW consecutive queries (128
-// indexer rows = QW x H_i) and one candidate range ("split"). It streams the
-// block keys in tiles of 32 through v_mfma_f32_32x32x16_bf16 (A = query rows
-// held in registers, B = 32 block keys loaded straight from global memory),
-// reduces the heads in-lane (the rows of one query are placed so one lane's
-// accumulators hold all its heads), and appends every candidate whose score
-// beats the query's running threshold to a per-(query, split) buffer in the
-// workspace. When a buffer nears capacity the wave radix-selects the exact
-// (k-1)-th entry, compacts the buffer stably to the k-1 survivors and raises the
-// threshold to that score. Candidates arrive in increasing block order, so a
-// later candidate that only ties the threshold can never displace a kept one:
-// the buffer always holds a superset of the split's exact top-(k-1).
+// Prefill (many queries per sequence):
+//   index_stream_kernel: one wave owns QW consecutive queries (128 indexer rows
+//   = QW x H_i) and one candidate range ("split"). It streams the block keys
+//   in tiles of 32 through v_mfma_f32_32x32x16_bf16 (A = query rows held in
+//   registers, pre-scaled by w when w is a power of two, which is exact;
+//   B = 32 block keys loaded from global memory two tiles ahead), reduces the
+//   heads in-lane (the rows of a query are placed so one lane's accumulators
+//   hold all its heads) and appends every candidate whose score beats the
+//   query's running threshold to a per-(query, split) buffer in the workspace.
+//   When a buffer nears capacity the wave stages it in LDS, radix-selects the
+//   exact (k-1)-th entry, compacts the buffer stably to k-1 entries and raises
+//   the threshold to that score. Candidates arrive in increasing block order,
+//   so a later candidate that only ties the threshold can never displace a
+//   kept one: the buffer always holds a superset of the split's exact
+//   top-(k-1). Each split ends compacted to at most k-1 entries.
+//   index_select_kernel: one workgroup per query merges the split buffers
+//   (already in block order) in LDS, selects exactly and writes the output.
 //
-// Kernel 2, index_select_kernel: one wave per query merges the split buffers
-// (already in block order), radix-selects the exact (k-1)-th score, and writes
-// the survivors in block order, then the query's own block, then -1 padding.
+// Decode (one query per sequence):
+//   index_decode_scan_kernel: one wave per 1024-candidate split of one
+//   sequence streams the block keys (HBM bound), writes every score to the
+//   workspace, and keeps the split's exact top-32 plus the key of its best
+//   omitted candidate.
+//   index_decode_select_kernel: one workgroup per sequence selects the top
+//   (k-1) of the union of the split lists. The result is exact when every
+//   split's best omitted score is below the selected threshold; otherwise the
+//   workgroup selects exactly from the stored scores of all candidates.
 #include "qsa_device.h"
 #include "qsa_internal.h"
+#include "select.h"
 
 namespace qsa {
 
 namespace {
 
-// Exact rank selection over uint32 keys (non-negative fp32 bit patterns order
-// like the floats). Finds tk, the keep-th largest key, and `need`, how many
-// entries equal to tk belong to the top `keep`. Four 8-bit digit passes with a
-// wave-private 256-bin histogram in LDS. Segments: (ptr, count) pairs produced
-// by `seg(s)` for s < nseg, scanned in order.
-template <typename SegFn>
-__device__ void wave_radix_select(SegFn seg, int nseg, int keep, uint32_t* hist, uint32_t& tk,
-                                  int& need_out) {
-  const int lane = lane_id();
-  uint32_t prefix = 0, mask = 0;
-  int need = keep;
-  for (int shift = 24; shift >= 0; shift -= 8) {
-    for (int i = lane; i < 256; i += kWave) hist[i] = 0;
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    for (int s = 0; s < nseg; ++s) {
-      const uint2* p;
-      int n;
-      seg(s, p, n);
-      for (int i = lane; i < n; i += kWave) {
-        const uint32_t key = p[i].x;
-        if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
-      }
-    }
-    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    // lane l owns bins 255-4l .. 252-4l (lane 0 holds the largest digits)
-    const int top = 255 - 4 * lane;
-    const uint32_t c0 = hist[top], c1 = hist[top - 1], c2 = hist[top - 2], c3 = hist[top - 3];
-    const uint32_t tot = c0 + c1 + c2 + c3;
-    uint32_t inc = tot;
-#pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-      const uint32_t v = __shfl_up(inc, off);
-      if (lane >= off) inc += v;
-    }
-    const uint32_t exc = inc - tot;
-    const bool hit = inc >= (uint32_t)need && exc < (uint32_t)need;
-    const int L = __ffsll((unsigned long long)ballot(hit)) - 1;
-    int dig = 0;
-    uint32_t above = 0;
-    if (lane == L) {
-      uint32_t cum = exc;
-      if (cum + c0 >= (uint32_t)need) {
-        dig = top;
-      } else {
-        cum += c0;
-        if (cum + c1 >= (uint32_t)need) {
-          dig = top - 1;
-        } else {
-          cum += c1;
-          if (cum + c2 >= (uint32_t)need) {
-            dig = top - 2;
-          } else {
-            cum += c2;
-            dig = top - 3;
-          }
-        }
-      }
-      above = cum;
-    }
-    dig = __shfl(dig, L);
-    above = __shfl(above, L);
-    prefix |= (uint32_t)dig << shift;
-    mask |= 255u << shift;
-    need -= (int)above;
-    __builtin_amdgcn_wave_barrier();
-  }
-  tk = prefix;
-  need_out = need;
-}
-
-// Keep, in order, entries with key > tk and the first `need` entries with
-// key == tk. Writes entry e (its rank among kept is `pos`) through emit(pos, e).
-template <typename SegFn, typename EmitFn>
-__device__ int wave_stable_keep(SegFn seg, int nseg, uint32_t tk, int need, EmitFn emit) {
-  const int lane = lane_id();
-  int kept = 0, ties = 0;
-  for (int s = 0; s < nseg; ++s) {
-    const uint2* p;
-    int n;
-    seg(s, p, n);
-    for (int base = 0; base < n; base += kWave) {
-      const int i = base + lane;
-      const bool in = i < n;
-      const uint2 e = in ? p[i] : make_uint2(0u, 0u);
-      const bool gt = in && e.x > tk;
-      const bool eq = in && e.x == tk;
-      const uint64_t me = ballot(eq);
-      const int tie_rank = ties + __popcll(lanes_below(me));
-      const bool keep = gt || (eq && tie_rank < need);
-      const uint64_t mk = ballot(keep);
-      if (keep) emit(kept + __popcll(lanes_below(mk)), e);
-      kept += __popcll(mk);
-      ties += __popcll(me);
-    }
-  }
-  return kept;
-}
+constexpr int kDecodeSplit = 1024;  // candidates per decode split
+constexpr int kDecodeLocal = 32;    // entries kept per decode split
+constexpr int kDecodeMaxSplits = 256;  // splits one select workgroup can stage in LDS
 
 __device__ __forceinline__ float relu_bits(float x) {
   // max on the integer view: negative values and -0.0 become +0.0
   return __int_as_float(max(__float_as_int(x), 0));
 }
 
+__device__ __forceinline__ u32x4 scale_bf16x8(u32x4 v, float s) {
+  u32x4 o;
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    o[e] = pack_bf16x2(bf16_bits_to_f32(v[e] & 0xFFFFu) * s, bf16_bits_to_f32(v[e] >> 16) * s);
+  return o;
+}
+
 // Reduce one query's buffer of n entries (block order) to its exact top `keep`
 // in place, keeping block order; returns the new threshold score.
-__device__ __forceinline__ float compact_buffer(uint2* p, int n, int keep, uint32_t* hist) {
+__device__ __forceinline__ float compact_buffer(uint2* p, int n, int keep, uint32_t* hist, uint2* stage) {
+  const int lane = lane_id();
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
-  auto seg = [&](int, const uint2*& sp, int& sn) {
-    sp = p;
-    sn = n;
-  };
+  for (int base = 0; base < n; base += 8 * kWave) {
+    uint2 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int i = base + u * kWave + lane;
+      if (i < n) v[u] = p[i];
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int i = base + u * kWave + lane;
+      if (i < n) stage[i] = v[u];
+    }
+  }
+  wave_sync();
   uint32_t tk;
   int need;
-  wave_radix_select(seg, 1, keep, hist, tk, need);
-  wave_stable_keep(seg, 1, tk, need, [&](int pos, uint2 e) { p[pos] = e; });
+  wave_select([&](int i) { return stage[i].x; }, n, keep, hist, tk, need);
+  wave_stable_keep([&](int i) { return stage[i]; }, n, tk, need, [&](int pos, uint2 e) { p[pos] = e; });
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+  wave_sync();
+  return __uint_as_float(tk);
+}
+
+typedef __attribute__((address_space(3))) uint32_t lds_u32;
+typedef __attribute__((address_space(1))) unsigned long long glb_u64;
+
+// Same as compact_buffer, staging only the keys in LDS (cap words) and
+// streaming the entries from global memory eight chunks at a time. Not
+// inlined (one copy serves every call site); its operands are typed with
+// their address spaces so LDS is addressed with ds_* and the buffer with
+// global_* instructions. An entry is one 64-bit word: key low, block high.
+__device__ __noinline__ float compact_keys_staged(glb_u64* p, int n, int keep, lds_u32* hist,
+                                                  lds_u32* kstage) {
+  const int lane = lane_id();
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+  for (int base = 0; base < n; base += 8 * kWave) {
+    uint32_t v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int i = base + u * kWave + lane;
+      v[u] = i < n ? (uint32_t)p[i] : 0u;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int i = base + u * kWave + lane;
+      if (i < n) kstage[i] = v[u];
+    }
+  }
+  wave_sync();
+  uint32_t tk;
+  int need;
+  wave_select([&](int i) { return (uint32_t)kstage[i]; }, n, keep, hist, tk, need);
+  int kept = 0, ties = 0;
+  for (int base = 0; base < n; base += 8 * kWave) {
+    unsigned long long e[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int i = base + u * kWave + lane;
+      e[u] = i < n ? p[i] : 0ull;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int i = base + u * kWave + lane;
+      const bool in = i < n;
+      const uint32_t key = (uint32_t)e[u];
+      const bool gt = in && key > tk;
+      const bool eq = in && key == tk;
+      const uint64_t me = ballot(eq);
+      const bool keep_it = gt || (eq && ties + __popcll(lanes_below(me)) < need);
+      const uint64_t mk = ballot(keep_it);
+      if (keep_it) p[kept + __popcll(lanes_below(mk))] = e[u];
+      kept += __popcll(mk);
+      ties += __popcll(me);
+    }
+  }
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+  wave_sync();
   return __uint_as_float(tk);
 }
 
@@ -158,13 +151,15 @@ __device__ __forceinline__ float compact_buffer(uint2* p, int n, int keep, uint3
 template <int HI, int AT>
 __global__ __launch_bounds__(256) void index_stream_kernel(
     const uint16_t* __restrict__ idx_q, const uint16_t* __restrict__ cmp_k, int64_t cmp_stride,
-    const int32_t* __restrict__ q_pos0, int n_q, int r, int keep, float w, int n_qgroups,
-    int splits, int split_len, int cap, uint2* __restrict__ buf, int* __restrict__ buf_cnt) {
+    const int32_t* __restrict__ q_pos0, int n_q, int r, int keep, float a_scale, float w_epi,
+    int n_qgroups, int splits, int split_len, int cap, uint2* __restrict__ buf,
+    int* __restrict__ buf_cnt) {
   constexpr int QPH = 16 / HI;    // queries per lane-half per A tile
   constexpr int QPT = 32 / HI;    // queries per A tile
   constexpr int QW = AT * QPT;    // queries per wave
   constexpr int NS = AT * QPH;    // score slots per lane
   __shared__ uint32_t hist_all[4][256];
+  extern __shared__ uint2 stage_all[];
 
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
@@ -176,6 +171,7 @@ __global__ __launch_bounds__(256) void index_stream_kernel(
   const int split = task / n_qgroups;
   const int b = blockIdx.y;
   uint32_t* hist = hist_all[wave];
+  uint2* stage = stage_all + (size_t)wave * cap;
 
   const int64_t pos0 = q_pos0[b];
   const int sbeg = split * split_len;
@@ -190,7 +186,7 @@ __global__ __launch_bounds__(256) void index_stream_kernel(
   int lim[NS];
   float tau[NS];
   int cnt[NS];
-  int maxlim = 0;
+  int maxlim = 0, minlim = 0x7FFFFFFF;
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
     const int qi = slot_query(s, half);
@@ -198,17 +194,21 @@ __global__ __launch_bounds__(256) void index_stream_kernel(
     if (qi < n_q) {
       const int64_t bt = (pos0 + qi) / r;
       l = (int)(bt < (int64_t)send ? bt : (int64_t)send);
+      minlim = min(minlim, l);
     }
     lim[s] = l;
-    tau[s] = -1.0f;
+    tau[s] = qi < n_q ? -1.0f : INFINITY;  // an absent query never takes a candidate
     cnt[s] = 0;
     maxlim = max(maxlim, l);
   }
 #pragma unroll
-  for (int off = 32; off > 0; off >>= 1) maxlim = max(maxlim, __shfl_xor(maxlim, off));
+  for (int off = 32; off > 0; off >>= 1) {
+    maxlim = max(maxlim, __shfl_xor(maxlim, off));
+    minlim = min(minlim, __shfl_xor(minlim, off));
+  }
 
   if (keep > 0 && maxlim > sbeg) {
-    // A operand: row m = col of each A tile; lane-half picks k-offset 8*half.
+    // A operand: row m = col of each A tile; the lane-half picks k-offset 8*half.
     u32x4 A[AT][4];
     {
       const int m = col;
@@ -222,7 +222,8 @@ __global__ __launch_bounds__(256) void index_stream_kernel(
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
           if (qi < n_q) {
-            A[a][ks] = ld16(idx_q + (((int64_t)b * n_q + qi) * HI + head) * 64 + 16 * ks + 8 * half);
+            const u32x4 v = ld16(idx_q + (((int64_t)b * n_q + qi) * HI + head) * 64 + 16 * ks + 8 * half);
+            A[a][ks] = a_scale == 1.0f ? v : scale_bf16x8(v, a_scale);
           } else {
             A[a][ks] = u32x4{0u, 0u, 0u, 0u};
           }
@@ -235,13 +236,17 @@ __global__ __launch_bounds__(256) void index_stream_kernel(
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) B[ks] = ld16(kb + (int64_t)j * 64 + 16 * ks);
     };
-    u32x4 Bn[4];
-    load_b(sbeg, Bn);
+    u32x4 B0[4], B1[4];
+    load_b(sbeg, B0);
+    load_b(sbeg + 32, B1);
     for (int c = sbeg; c < maxlim; c += 32) {
       u32x4 B[4];
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) B[ks] = Bn[ks];
-      if (c + 32 < maxlim) load_b(c + 32, Bn);
+      for (int ks = 0; ks < 4; ++ks) {
+        B[ks] = B0[ks];
+        B0[ks] = B1[ks];
+      }
+      if (c + 64 < maxlim) load_b(c + 64, B1);
       f32x16 acc[AT];
 #pragma unroll
       for (int a = 0; a < AT; ++a) {
@@ -251,14 +256,15 @@ __global__ __launch_bounds__(256) void index_stream_kernel(
       }
       const int j = c + col;
       const uint32_t below = (1u << col) - 1u;
+      const bool interior = c + 32 <= minlim;  // every query of the wave sees the whole tile
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
         const int a = s / QPH, qq = s % QPH;
         float sum = 0.0f;
 #pragma unroll
         for (int hd = 0; hd < HI; ++hd) sum += relu_bits(acc[a][qq * HI + hd]);
-        const float sc = sum * w;
-        const bool pass = (j < lim[s]) && (sc > tau[s]);
+        const float sc = sum * w_epi;
+        const bool pass = (interior || j < lim[s]) && (sc > tau[s]);
         const uint64_t m64 = ballot(pass);
         if (m64) {
           const uint32_t mh = (uint32_t)(m64 >> (32 * half));
@@ -269,31 +275,60 @@ __global__ __launch_bounds__(256) void index_stream_kernel(
           cnt[s] += __popc(mh);
         }
       }
-      uint32_t need_mask = 0;  // bit 2s+hh: slot s of lane-half hh must be compacted
+      bool over = false;
 #pragma unroll
-      for (int s = 0; s < NS; ++s) {
+      for (int s = 0; s < NS; ++s) over |= cnt[s] > cap - 32;
+      if (ballot(over)) {
+        uint32_t need_mask = 0;  // bit 2s+hh: slot s of lane-half hh must be compacted
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh)
-          if (__shfl(cnt[s], 32 * hh) > cap - 32) need_mask |= 1u << (2 * s + hh);
-      }
-      while (need_mask) {
-        const int bit = __ffs(need_mask) - 1;
-        need_mask &= need_mask - 1;
-        const int s = bit >> 1, hh = bit & 1;
-        int cs = 0;
+        for (int s = 0; s < NS; ++s) {
 #pragma unroll
-        for (int s2 = 0; s2 < NS; ++s2)
-          if (s2 == s) cs = cnt[s2];
-        const int ch = __shfl(cs, 32 * hh);
-        const float nt = compact_buffer(buf_of(slot_query(s, hh)), ch, keep, hist);
-        if (half == hh) {
+          for (int hh = 0; hh < 2; ++hh)
+            if (__builtin_amdgcn_readlane(cnt[s], 32 * hh) > cap - 32) need_mask |= 1u << (2 * s + hh);
+        }
+        while (need_mask) {
+          const int bit = __ffs(need_mask) - 1;
+          need_mask &= need_mask - 1;
+          const int s = bit >> 1, hh = bit & 1;
+          int cs = 0;
 #pragma unroll
           for (int s2 = 0; s2 < NS; ++s2)
-            if (s2 == s) {
-              cnt[s2] = keep;
-              tau[s2] = nt;
-            }
+            if (s2 == s) cs = cnt[s2];
+          const int ch = __builtin_amdgcn_readlane(cs, 32 * hh);
+          const float nt = compact_buffer(buf_of(slot_query(s, hh)), ch, keep, hist, stage);
+          if (half == hh) {
+#pragma unroll
+            for (int s2 = 0; s2 < NS; ++s2)
+              if (s2 == s) {
+                cnt[s2] = keep;
+                tau[s2] = nt;
+              }
+          }
         }
+      }
+    }
+    // leave every split buffer at most `keep` long
+    uint32_t need_mask = 0;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+        if (__builtin_amdgcn_readlane(cnt[s], 32 * hh) > keep) need_mask |= 1u << (2 * s + hh);
+    }
+    while (need_mask) {
+      const int bit = __ffs(need_mask) - 1;
+      need_mask &= need_mask - 1;
+      const int s = bit >> 1, hh = bit & 1;
+      int cs = 0;
+#pragma unroll
+      for (int s2 = 0; s2 < NS; ++s2)
+        if (s2 == s) cs = cnt[s2];
+      const int ch = __builtin_amdgcn_readlane(cs, 32 * hh);
+      compact_buffer(buf_of(slot_query(s, hh)), ch, keep, hist, stage);
+      if (half == hh) {
+#pragma unroll
+        for (int s2 = 0; s2 < NS; ++s2)
+          if (s2 == s) cnt[s2] = keep;
       }
     }
   }
@@ -306,74 +341,527 @@ __global__ __launch_bounds__(256) void index_stream_kernel(
   }
 }
 
+// Prefill indexer for many queries per sequence (n_q >= 64): a workgroup of 4
+// waves (4 x QW queries) shares one candidate split. Block keys travel
+// HBM -> registers (three 64-candidate tiles ahead) -> a 3-slot LDS ring
+// (XOR-swizzled 16-byte parts so the B-fragment reads hit distinct banks) ->
+// B fragments; one barrier per tile. The per-query threshold / append /
+// compaction logic is the same as in index_stream_kernel.
+template <int HI, int AT>
+__global__ __launch_bounds__(256, 2) void index_prefill_kernel(
+    const uint16_t* __restrict__ idx_q, const uint16_t* __restrict__ cmp_k, int64_t cmp_stride,
+    const int32_t* __restrict__ q_pos0, int n_q, int r, int keep, float a_scale, float w_epi,
+    int n_qgroups, int splits, int split_len, int cap, uint2* __restrict__ buf,
+    int* __restrict__ buf_cnt) {
+  constexpr int QPH = 16 / HI;
+  constexpr int QPT = 32 / HI;
+  constexpr int QW = AT * QPT;
+  constexpr int NS = AT * QPH;
+  constexpr int TILE = 64;                       // candidates per LDS tile
+  constexpr int TILE_BYTES = TILE * 128;         // 8 KiB
+  constexpr int NSLOT = 2;
+  __shared__ uint32_t hist_all[4][256];
+  __shared__ int wg_lim[2][4];
+  extern __shared__ __attribute__((aligned(16))) unsigned char dyn[];
+  unsigned char* ring = dyn;                                   // NSLOT * 8 KiB
+  uint32_t* kstage_all = reinterpret_cast<uint32_t*>(dyn + NSLOT * TILE_BYTES);  // 4 * cap words
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int half = lane >> 5;
+  const int col = lane & 31;
+  const int qg = blockIdx.x * 4 + wave;
+  const int split = blockIdx.y;
+  const int b = blockIdx.z;
+  uint32_t* hist = hist_all[wave];
+  uint32_t* kstage = kstage_all + (size_t)wave * cap;
+
+  const int64_t pos0 = q_pos0[b];
+  const int sbeg = split * split_len;
+  const int send = sbeg + split_len;
+  auto slot_query = [&](int s, int hh) { return qg * QW + (s / QPH) * QPT + hh * QPH + (s % QPH); };
+  auto buf_of = [&](int qi) {
+    return buf + (((int64_t)b * n_q + qi) * splits + split) * (int64_t)cap;
+  };
+  const bool wave_live = qg < n_qgroups;
+
+  // candidates of query qi in this split: [sbeg, lim_of(qi))
+  auto lim_of = [&](int qi) {
+    const int64_t bt = (pos0 + qi) / r;
+    return (int)(bt < (int64_t)send ? bt : (int64_t)send);
+  };
+  float tau[NS];
+  int cnt[NS];
+  int maxlim = 0, minlim = 0x7FFFFFFF;
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    const int qi = slot_query(s, half);
+    int l = 0;
+    if (wave_live && qi < n_q) {
+      l = lim_of(qi);
+      minlim = min(minlim, l);
+    }
+    tau[s] = (wave_live && qi < n_q) ? -1.0f : INFINITY;
+    cnt[s] = 0;
+    maxlim = max(maxlim, l);
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    maxlim = max(maxlim, __shfl_xor(maxlim, off));
+    minlim = min(minlim, __shfl_xor(minlim, off));
+  }
+  if (lane == 0) {
+    wg_lim[0][wave] = maxlim;
+  }
+  __syncthreads();
+  const int wg_max = max(max(wg_lim[0][0], wg_lim[0][1]), max(wg_lim[0][2], wg_lim[0][3]));
+
+  if (keep > 0 && wg_max > sbeg) {
+    u32x4 A[AT][4];
+    {
+      const int m = col;
+      const int i = 4 * (m >> 3) + (m & 3);
+      const int hh = (m >> 2) & 1;
+      const int qs = hh * QPH + i / HI;
+      const int head = i % HI;
+#pragma unroll
+      for (int a = 0; a < AT; ++a) {
+        const int qi = qg * QW + a * QPT + qs;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          if (wave_live && qi < n_q) {
+            const u32x4 v = ld16(idx_q + (((int64_t)b * n_q + qi) * HI + head) * 64 + 16 * ks + 8 * half);
+            A[a][ks] = a_scale == 1.0f ? v : scale_bf16x8(v, a_scale);
+          } else {
+            A[a][ks] = u32x4{0u, 0u, 0u, 0u};
+          }
+        }
+      }
+    }
+    const unsigned char* kb = reinterpret_cast<const unsigned char*>(cmp_k + (int64_t)b * cmp_stride);
+    const int ntiles = (wg_max - sbeg + TILE - 1) / TILE;
+    lds_u32* hist_l = (lds_u32*)hist;
+    lds_u32* kstage_l = (lds_u32*)kstage;
+    // this thread's two 16-byte parts of every tile: chunk c = tid + 256u,
+    // candidate row c / 8, part c % 8, stored at part (c % 8) ^ (row % 8)
+    auto load_tile = [&](int t, u32x4* R) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int c = tid + 256 * u;
+        const int row = min(sbeg + t * TILE + (c >> 3), wg_max - 1);
+        R[u] = *reinterpret_cast<const u32x4*>(kb + (int64_t)row * 128 + (c & 7) * 16);
+      }
+    };
+    auto store_tile = [&](int slot, const u32x4* R) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int c = tid + 256 * u;
+        const int row = c >> 3;
+        *reinterpret_cast<u32x4*>(ring + slot * TILE_BYTES + row * 128 + (((c & 7) ^ (row & 7)) * 16)) = R[u];
+      }
+    };
+    // compact every buffer of this wave that holds more than `limit` entries
+    auto compact_over = [&](int limit, bool raise) {
+      uint32_t need_mask = 0;  // bit 2s+hh: slot s of lane-half hh
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+          if (__builtin_amdgcn_readlane(cnt[s], 32 * hh) > limit) need_mask |= 1u << (2 * s + hh);
+      }
+      while (need_mask) {
+        const int bit = __ffs(need_mask) - 1;
+        need_mask &= need_mask - 1;
+        const int s = bit >> 1, hh = bit & 1;
+        int cs = 0;
+#pragma unroll
+        for (int s2 = 0; s2 < NS; ++s2)
+          if (s2 == s) cs = cnt[s2];
+        const int ch = __builtin_amdgcn_readlane(cs, 32 * hh);
+        const float ntau = compact_keys_staged((glb_u64*)buf_of(slot_query(s, hh)), ch, keep, hist_l, kstage_l);
+        if (half == hh) {
+#pragma unroll
+          for (int s2 = 0; s2 < NS; ++s2)
+            if (s2 == s) {
+              cnt[s2] = keep;
+              if (raise) tau[s2] = ntau;
+            }
+        }
+      }
+    };
+    auto process = [&](int t, int slot) {
+      const unsigned char* sl = ring + slot * TILE_BYTES;
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        const int c = sbeg + t * TILE + nt * 32;
+        const int row = nt * 32 + col;
+        u32x4 B[4];
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          const int part = 2 * ks + half;
+          B[ks] = *reinterpret_cast<const u32x4*>(sl + row * 128 + ((part ^ (row & 7)) * 16));
+        }
+        f32x16 acc[AT];
+#pragma unroll
+        for (int a = 0; a < AT; ++a) {
+          acc[a] = f32x16{};
+#pragma unroll
+          for (int ks = 0; ks < 4; ++ks) acc[a] = mfma32x32x16(A[a][ks], B[ks], acc[a]);
+        }
+        const int j = c + col;
+        const uint32_t below = (1u << col) - 1u;
+        const bool interior = c + 32 <= minlim;
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+          const int a = s / QPH, qq = s % QPH;
+          float sum = 0.0f;
+#pragma unroll
+          for (int hd = 0; hd < HI; ++hd) sum += relu_bits(acc[a][qq * HI + hd]);
+          const float sc = sum * w_epi;
+          const bool pass = (interior || j < lim_of(slot_query(s, half))) && (sc > tau[s]);
+          const uint64_t m64 = ballot(pass);
+          if (m64) {
+            const uint32_t mh = (uint32_t)(m64 >> (32 * half));
+            if (pass) {
+              const int pos = cnt[s] + __popc(mh & below);
+              buf_of(slot_query(s, half))[pos] = make_uint2(__float_as_uint(sc), (uint32_t)j);
+            }
+            cnt[s] += __popc(mh);
+          }
+        }
+      }
+      // at most 64 appends per buffer per tile: keep room for the next tile
+      bool over = false;
+#pragma unroll
+      for (int s = 0; s < NS; ++s) over |= cnt[s] > cap - TILE;
+      if (ballot(over)) compact_over(cap - TILE, true);
+    };
+    // two register sets (tiles t and t + 1 in flight) and two LDS slots:
+    // iteration t stores tile t + 1, loads tile t + 2, computes tile t
+    u32x4 R0[2], R1[2];
+    load_tile(0, R0);
+    if (ntiles > 1) load_tile(1, R1);
+    store_tile(0, R0);
+    for (int t = 0; t < ntiles; t += 2) {
+      __syncthreads();
+      if (t + 1 < ntiles) store_tile(1, R1);
+      if (t + 2 < ntiles) load_tile(t + 2, R0);
+      process(t, 0);
+      if (t + 1 < ntiles) {
+        __syncthreads();
+        if (t + 2 < ntiles) store_tile(0, R0);
+        if (t + 3 < ntiles) load_tile(t + 3, R1);
+        process(t + 1, 1);
+      }
+    }
+    // leave every split buffer at most `keep` long
+    compact_over(keep, false);
+  }
+  if (wave_live && col == 0) {
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const int qi = slot_query(s, half);
+      if (qi < n_q) buf_cnt[((int64_t)b * n_q + qi) * splits + split] = cnt[s];
+    }
+  }
+}
+
+// One workgroup (256 threads) per query: merge the split buffers in LDS.
 __global__ __launch_bounds__(256) void index_select_kernel(
     const uint2* __restrict__ buf, const int* __restrict__ buf_cnt, const int32_t* __restrict__ q_pos0,
-    int batch, int n_q, int r, int k, int splits, int cap, int32_t* __restrict__ sel,
+    int n_q, int r, int k, int splits, int cap, int32_t* __restrict__ sel,
     int32_t* __restrict__ sel_cnt) {
-  __shared__ uint32_t hist_all[4][256];
-  const int wave = threadIdx.x >> 6;
-  const int lane = threadIdx.x & 63;
-  const int64_t gw = (int64_t)blockIdx.x * 4 + wave;
-  if (gw >= (int64_t)batch * n_q) return;
-  const int b = (int)(gw / n_q);
-  const int qi = (int)(gw % n_q);
-  uint32_t* hist = hist_all[wave];
+  __shared__ uint32_t hist[256];
+  __shared__ uint32_t bc[2 + 8];
+  __shared__ int seg_off[9];
+  extern __shared__ uint2 stage[];
+  const int tid = threadIdx.x;
+  const int64_t gq = blockIdx.x;  // b * n_q + qi
+  const int b = (int)(gq / n_q);
+  const int qi = (int)(gq % n_q);
   const int64_t t = (int64_t)q_pos0[b] + qi;
   const int64_t bt = t / r;
   const int keep = (int)((int64_t)(k - 1) < bt ? (int64_t)(k - 1) : bt);
-  const uint2* qb = buf + gw * splits * (int64_t)cap;
-  const int* qc = buf_cnt + gw * splits;
-  int32_t* out = sel + gw * k;
+  const uint2* qb = buf + gq * splits * (int64_t)cap;
+  const int* qc = buf_cnt + gq * splits;
+  int32_t* out = sel + gq * k;
 
-  auto seg = [&](int s, const uint2*& sp, int& sn) {
-    sp = qb + (int64_t)s * cap;
-    sn = qc[s];
-  };
-  int total = 0;
-  for (int s = lane; s < splits; s += kWave) total += qc[s];
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) total += __shfl_xor(total, off);
-
+  // segment offsets (at most 8 splits, each at most keep entries)
+  if (tid == 0) {
+    int acc = 0;
+    for (int s = 0; s < splits; ++s) {
+      seg_off[s] = acc;
+      acc += qc[s];
+    }
+    seg_off[splits] = acc;
+  }
+  __syncthreads();
+  const int total = seg_off[splits];
+  for (int s = 0; s < splits; ++s) {
+    const int n = seg_off[s + 1] - seg_off[s];
+    const uint2* p = qb + (int64_t)s * cap;
+    for (int i = tid; i < n; i += 256) stage[seg_off[s] + i] = p[i];
+  }
+  __syncthreads();
   if (keep > 0) {
     uint32_t tk = 0;
     int need = 0x7FFFFFFF;
-    if (total > keep) wave_radix_select(seg, splits, keep, hist, tk, need);
-    wave_stable_keep(seg, splits, tk, need, [&](int pos, uint2 e) { out[pos] = (int32_t)e.y; });
+    if (total > keep) block_select<256>([&](int i) { return stage[i].x; }, total, keep, hist, bc, tk, need);
+    block_stable_keep<256>([&](int i) { return stage[i]; }, total, tk, need, bc + 2,
+                           [&](int pos, uint2 e) { out[pos] = (int32_t)e.y; });
   }
-  if (lane == 0) {
+  if (tid == 0) {
     out[keep] = (int32_t)bt;
-    sel_cnt[gw] = keep + 1;
+    sel_cnt[gq] = keep + 1;
   }
-  for (int i = keep + 1 + lane; i < k; i += kWave) out[i] = -1;
+  for (int i = keep + 1 + tid; i < k; i += 256) out[i] = -1;
+}
+
+// ------------------------------------------------------------------ decode --
+template <int HI>
+__global__ __launch_bounds__(256) void index_decode_scan_kernel(
+    const uint16_t* __restrict__ idx_q, const uint16_t* __restrict__ cmp_k, int64_t cmp_stride,
+    const int32_t* __restrict__ q_pos0, int r, float a_scale, float w_epi, int splits,
+    float* __restrict__ scores, int64_t score_stride, uint2* __restrict__ local,
+    int2* __restrict__ meta) {
+  __shared__ uint32_t hist_all[4][256];
+  __shared__ float sc_all[4][kDecodeSplit];
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int half = lane >> 5;
+  const int col = lane & 31;
+  const int split = blockIdx.x * 4 + wave;
+  if (split >= splits) return;
+  const int b = blockIdx.y;
+  uint32_t* hist = hist_all[wave];
+  float* sc = sc_all[wave];
+  const int64_t bt = (int64_t)q_pos0[b] / r;
+  const int sbeg = split * kDecodeSplit;
+  const int send = (int)min((int64_t)sbeg + kDecodeSplit, bt);
+  const int n = max(send - sbeg, 0);
+  uint2* lout = local + ((int64_t)b * splits + split) * kDecodeLocal;
+  int2* mout = meta + (int64_t)b * splits + split;
+  if (n == 0) {
+    if (lane == 0) *mout = make_int2(0, -1);
+    return;
+  }
+  // A: 32 rows; the query's H_i heads sit at the rows of slot 0 of lane-half 0
+  u32x4 A[4];
+  {
+    const int m = col;
+    const int i = 4 * (m >> 3) + (m & 3);
+    const int hh = (m >> 2) & 1;
+    const bool mine = hh == 0 && i < HI;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      if (mine) {
+        const u32x4 v = ld16(idx_q + ((int64_t)b * HI + i) * 64 + 16 * ks + 8 * half);
+        A[ks] = a_scale == 1.0f ? v : scale_bf16x8(v, a_scale);
+      } else {
+        A[ks] = u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+  }
+  const uint16_t* kb = cmp_k + (int64_t)b * cmp_stride + 8 * half;
+  const int last = send - 1;
+  constexpr int PF = 4;  // tiles in flight
+  u32x4 Bq[PF][4];
+#pragma unroll
+  for (int p = 0; p < PF; ++p) {
+    const int j = min(sbeg + 32 * p + col, last);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) Bq[p][ks] = ld16(kb + (int64_t)j * 64 + 16 * ks);
+  }
+  float* srow = scores + (int64_t)b * score_stride;
+  const int ntiles = (n + 31) / 32;
+  for (int tb = 0; tb < ntiles; tb += PF) {
+#pragma unroll
+    for (int p = 0; p < PF; ++p) {
+      const int tile = tb + p;
+      if (tile < ntiles) {
+        f32x16 acc = f32x16{};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) acc = mfma32x32x16(A[ks], Bq[p][ks], acc);
+        const int nt = tile + PF;
+        if (nt < ntiles) {
+          const int j = min(sbeg + 32 * nt + col, last);
+#pragma unroll
+          for (int ks = 0; ks < 4; ++ks) Bq[p][ks] = ld16(kb + (int64_t)j * 64 + 16 * ks);
+        }
+        float sum = 0.0f;
+#pragma unroll
+        for (int hd = 0; hd < HI; ++hd) sum += relu_bits(acc[hd]);
+        const float s = sum * w_epi;
+        const int jj = 32 * tile + col;
+        if (half == 0 && jj < n) {
+          sc[jj] = s;
+          srow[sbeg + jj] = s;
+        }
+      }
+    }
+  }
+  wave_sync();
+  int count = n;
+  int omitted = -1;
+  if (n > kDecodeLocal) {
+    uint32_t tk, ties;
+    int need;
+    wave_select([&](int i) { return __float_as_uint(sc[i]); }, n, kDecodeLocal, hist, tk, need, &ties);
+    wave_stable_keep([&](int i) { return make_uint2(__float_as_uint(sc[i]), (uint32_t)(sbeg + i)); }, n, tk,
+                     need, [&](int pos, uint2 e) { lout[pos] = e; });
+    if (ties > (uint32_t)need) {
+      omitted = (int)tk;
+    } else {
+      int mx = -1;
+      for (int i = lane; i < n; i += kWave) {
+        const uint32_t key = __float_as_uint(sc[i]);
+        if (key < tk) mx = max(mx, (int)key);
+      }
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) mx = max(mx, __shfl_xor(mx, off));
+      omitted = mx;
+    }
+    count = kDecodeLocal;
+  } else {
+    for (int i = lane; i < n; i += kWave) lout[i] = make_uint2(__float_as_uint(sc[i]), (uint32_t)(sbeg + i));
+  }
+  if (lane == 0) *mout = make_int2(count, omitted);
+}
+
+__global__ __launch_bounds__(256) void index_decode_select_kernel(
+    const float* __restrict__ scores, int64_t score_stride, const uint2* __restrict__ local,
+    const int2* __restrict__ meta, const int32_t* __restrict__ q_pos0, int r, int k, int splits,
+    int32_t* __restrict__ sel, int32_t* __restrict__ sel_cnt) {
+  __shared__ uint32_t hist[256];
+  __shared__ uint32_t bc[2 + 8];
+  __shared__ int s_max;
+  __shared__ int s_off[kDecodeMaxSplits + 1];
+  extern __shared__ uint2 stage[];
+  const int tid = threadIdx.x;
+  const int b = blockIdx.x;
+  const int64_t bt = (int64_t)q_pos0[b] / r;
+  const int keep = (int)((int64_t)(k - 1) < bt ? (int64_t)(k - 1) : bt);
+  int32_t* out = sel + (int64_t)b * k;
+  const int used = (int)min((int64_t)splits, (bt + kDecodeSplit - 1) / kDecodeSplit);
+  const uint2* lb = local + (int64_t)b * splits * kDecodeLocal;
+  const int2* mb = meta + (int64_t)b * splits;
+
+  // union of the split lists, in block order, staged in LDS
+  if (tid == 0) {
+    s_max = -1;
+    int acc = 0;
+    for (int s = 0; s < used; ++s) {
+      s_off[s] = acc;
+      acc += mb[s].x;
+    }
+    s_off[used] = acc;
+  }
+  __syncthreads();
+  for (int s = tid; s < used; s += 256) atomicMax(&s_max, mb[s].y);
+  const int total = s_off[used];
+  for (int i = tid; i < used * kDecodeLocal; i += 256) {
+    const int s = i / kDecodeLocal, e = i % kDecodeLocal;
+    if (e < s_off[s + 1] - s_off[s]) stage[s_off[s] + e] = lb[i];
+  }
+  __syncthreads();
+  const int max_omitted = s_max;
+  if (keep > 0) {
+    uint32_t tk = 0;
+    int need = 0x7FFFFFFF;
+    bool exact;
+    if (total > keep) {
+      block_select<256>([&](int i) { return stage[i].x; }, total, keep, hist, bc, tk, need);
+      exact = max_omitted < 0 || (uint32_t)max_omitted < tk;
+    } else {
+      exact = max_omitted < 0;  // the union holds every candidate
+    }
+    if (exact) {
+      block_stable_keep<256>([&](int i) { return stage[i]; }, total, tk, need, bc + 2,
+                             [&](int pos, uint2 e) { out[pos] = (int32_t)e.y; });
+    } else {
+      // exact selection over the stored scores of every candidate
+      const float* srow = scores + (int64_t)b * score_stride;
+      const int n = (int)bt;
+      tk = 0;
+      need = 0x7FFFFFFF;
+      block_select<256>([&](int i) { return __float_as_uint(srow[i]); }, n, keep, hist, bc, tk, need);
+      block_stable_keep<256>([&](int i) { return make_uint2(__float_as_uint(srow[i]), (uint32_t)i); }, n, tk,
+                             need, bc + 2, [&](int pos, uint2 e) { out[pos] = (int32_t)e.y; });
+    }
+  }
+  if (tid == 0) {
+    out[keep] = (int32_t)bt;
+    sel_cnt[b] = keep + 1;
+  }
+  for (int i = keep + 1 + tid; i < k; i += 256) out[i] = -1;
+}
+
+// ----------------------------------------------------------------- planning --
+static bool pow2_float(float w) {
+  int e;
+  const float m = frexpf(w, &e);
+  return m == 0.5f;
 }
 
 IndexPlan plan_index(int hi, int k, int batch, int n_q, int64_t max_q_end, int r) {
   IndexPlan p{};
   p.hi = hi;
-  p.at = n_q >= 64 ? 4 : 1;
-  p.qw = p.at * 32 / hi;
-  p.n_qgroups = (n_q + p.qw - 1) / p.qw;
   const int64_t max_cand = max_q_end > 0 ? (max_q_end - 1) / r : 0;
   p.max_cand = max_cand;
-  // enough wave tasks to give every SIMD a few waves; splits no shorter than 256
-  const int64_t waves = (int64_t)batch * p.n_qgroups;
-  int64_t splits = (4096 + waves - 1) / waves;
-  const int64_t max_splits = (max_cand + 255) / 256;
-  if (splits > max_splits) splits = max_splits;
+  const int keep = k - 1;
+  const int64_t dsplits = (max_cand + kDecodeSplit - 1) / kDecodeSplit;
+  if (n_q == 1 && dsplits <= kDecodeMaxSplits) {
+    p.decode = true;
+    p.splits = dsplits < 1 ? 1 : (int)dsplits;
+    p.score_stride = (max_cand + 63) / 64 * 64;
+    const size_t sc = (size_t)batch * p.score_stride * sizeof(float);
+    const size_t lc = (size_t)batch * p.splits * kDecodeLocal * sizeof(uint2);
+    const size_t mc = (size_t)batch * p.splits * sizeof(int2);
+    p.buf_bytes = (sc + 255) / 256 * 256;
+    p.local_off = p.buf_bytes;
+    p.meta_off = p.local_off + (lc + 255) / 256 * 256;
+    p.workspace = p.meta_off + (mc + 255) / 256 * 256;
+    p.select_lds = (size_t)p.splits * kDecodeLocal * sizeof(uint2);
+    return p;
+  }
+  p.decode = false;
+  p.wide = n_q >= 64;
+  // A tiles per wave in the LDS-pipelined kernel: 8 query slots per lane
+  p.at = p.wide ? (hi >= 8 ? 4 : (hi == 4 ? 2 : 1)) : 1;
+  p.qw = p.at * 32 / hi;
+  p.n_qgroups = (n_q + p.qw - 1) / p.qw;
+  int64_t splits;
+  if (p.wide) {
+    // workgroups of 4 query groups; about two workgroups per CU in one round
+    const int64_t n_wg = ((int64_t)p.n_qgroups + 3) / 4;
+    splits = (512 + batch * n_wg - 1) / (batch * n_wg);
+    const int64_t max_splits = (max_cand + 1023) / 1024;
+    if (splits > max_splits) splits = max_splits;
+  } else {
+    const int64_t waves = (int64_t)batch * p.n_qgroups;
+    splits = (4096 + waves - 1) / waves;
+    const int64_t max_splits = (max_cand + 255) / 256;
+    if (splits > max_splits) splits = max_splits;
+  }
+  if (splits > 8) splits = 8;
   if (splits < 1) splits = 1;
   int64_t split_len = (max_cand + splits - 1) / splits;
-  split_len = (split_len + 31) / 32 * 32;
-  if (split_len < 32) split_len = 32;
+  split_len = (split_len + 63) / 64 * 64;
+  if (split_len < 64) split_len = 64;
   p.splits = (int)splits;
   p.split_len = (int)split_len;
-  const int keep = k - 1;
   int cap = 2048;
   if (cap < 2 * keep + 64) cap = (2 * keep + 64 + 63) / 64 * 64;
-  if ((int64_t)split_len + 32 <= cap) cap = (int)split_len + 32;
+  if (cap < keep + 2 * 64) cap = keep + 2 * 64;
+  if ((int64_t)split_len + 64 <= cap) cap = (int)split_len + 64;
   p.cap = cap;
   p.buf_bytes = (size_t)batch * n_q * p.splits * (size_t)cap * sizeof(uint2);
   p.cnt_bytes = (size_t)batch * n_q * p.splits * sizeof(int);
   p.workspace = p.buf_bytes + ((p.cnt_bytes + 255) / 256 * 256);
+  p.stream_lds = p.wide ? (size_t)2 * 64 * 128 + (size_t)4 * cap * sizeof(uint32_t)
+                           : (size_t)4 * cap * sizeof(uint2);
+  p.select_lds = (size_t)p.splits * (keep > 0 ? keep : 1) * sizeof(uint2);
   return p;
 }
 
@@ -381,33 +869,73 @@ hipError_t launch_index_topk(const IndexPlan& p, const uint16_t* idx_q, const ui
                              int64_t cmp_stride, const int32_t* q_pos0, int batch, int n_q, int r,
                              int k, float w, int32_t* sel, int32_t* sel_cnt, void* ws,
                              hipStream_t stream) {
-  uint2* buf = reinterpret_cast<uint2*>(ws);
-  int* cnt = reinterpret_cast<int*>(reinterpret_cast<char*>(ws) + p.buf_bytes);
-  const int tasks = p.n_qgroups * p.splits;
-  const dim3 g1((tasks + 3) / 4, batch);
-#define QSA_LAUNCH_STREAM(HI_, AT_)                                                               \
-  hipLaunchKernelGGL((index_stream_kernel<HI_, AT_>), g1, dim3(256), 0, stream, idx_q, cmp_k,     \
-                     cmp_stride, q_pos0, n_q, r, k - 1, w, p.n_qgroups, p.splits, p.split_len,   \
-                     p.cap, buf, cnt)
-  switch (p.hi * 10 + p.at) {
-    case 14: QSA_LAUNCH_STREAM(1, 4); break;
-    case 11: QSA_LAUNCH_STREAM(1, 1); break;
-    case 24: QSA_LAUNCH_STREAM(2, 4); break;
-    case 21: QSA_LAUNCH_STREAM(2, 1); break;
-    case 44: QSA_LAUNCH_STREAM(4, 4); break;
-    case 41: QSA_LAUNCH_STREAM(4, 1); break;
-    case 84: QSA_LAUNCH_STREAM(8, 4); break;
-    case 81: QSA_LAUNCH_STREAM(8, 1); break;
-    case 164: QSA_LAUNCH_STREAM(16, 4); break;
-    case 161: QSA_LAUNCH_STREAM(16, 1); break;
-    default: return hipErrorInvalidValue;
+  const bool exact_scale = pow2_float(w);
+  const float a_scale = exact_scale ? w : 1.0f;
+  const float w_epi = exact_scale ? 1.0f : w;
+  char* wsb = reinterpret_cast<char*>(ws);
+  if (p.decode) {
+    float* scores = reinterpret_cast<float*>(wsb);
+    uint2* local = reinterpret_cast<uint2*>(wsb + p.local_off);
+    int2* meta = reinterpret_cast<int2*>(wsb + p.meta_off);
+    const dim3 g1((p.splits + 3) / 4, batch);
+#define QSA_LAUNCH_DSCAN(HI_)                                                                      \
+  hipLaunchKernelGGL(index_decode_scan_kernel<HI_>, g1, dim3(256), 0, stream, idx_q, cmp_k,       \
+                     cmp_stride, q_pos0, r, a_scale, w_epi, p.splits, scores, p.score_stride, local, \
+                     meta)
+    switch (p.hi) {
+      case 1: QSA_LAUNCH_DSCAN(1); break;
+      case 2: QSA_LAUNCH_DSCAN(2); break;
+      case 4: QSA_LAUNCH_DSCAN(4); break;
+      case 8: QSA_LAUNCH_DSCAN(8); break;
+      case 16: QSA_LAUNCH_DSCAN(16); break;
+      default: return hipErrorInvalidValue;
+    }
+#undef QSA_LAUNCH_DSCAN
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(index_decode_select_kernel, dim3(batch), dim3(256), p.select_lds, stream, scores,
+                       p.score_stride, local, meta, q_pos0, r, k, p.splits, sel, sel_cnt);
+    return hipGetLastError();
   }
+  uint2* buf = reinterpret_cast<uint2*>(wsb);
+  int* cnt = reinterpret_cast<int*>(wsb + p.buf_bytes);
+  if (p.wide) {
+    const dim3 g1((p.n_qgroups + 3) / 4, p.splits, batch);
+#define QSA_LAUNCH_PREFILL(HI_, AT_)                                                               \
+  hipLaunchKernelGGL((index_prefill_kernel<HI_, AT_>), g1, dim3(256), p.stream_lds, stream, idx_q, cmp_k,  \
+                     cmp_stride, q_pos0, n_q, r, k - 1, a_scale, w_epi, p.n_qgroups, p.splits,     \
+                     p.split_len, p.cap, buf, cnt)
+    switch (p.hi) {
+      case 1: QSA_LAUNCH_PREFILL(1, 1); break;
+      case 2: QSA_LAUNCH_PREFILL(2, 1); break;
+      case 4: QSA_LAUNCH_PREFILL(4, 2); break;
+      case 8: QSA_LAUNCH_PREFILL(8, 4); break;
+      case 16: QSA_LAUNCH_PREFILL(16, 4); break;
+      default: return hipErrorInvalidValue;
+    }
+#undef QSA_LAUNCH_PREFILL
+  } else {
+    const int tasks = p.n_qgroups * p.splits;
+    const dim3 g1((tasks + 3) / 4, batch);
+#define QSA_LAUNCH_STREAM(HI_)                                                                     \
+  hipLaunchKernelGGL((index_stream_kernel<HI_, 1>), g1, dim3(256), p.stream_lds, stream, idx_q,    \
+                     cmp_k, cmp_stride, q_pos0, n_q, r, k - 1, a_scale, w_epi, p.n_qgroups,        \
+                     p.splits, p.split_len, p.cap, buf, cnt)
+    switch (p.hi) {
+      case 1: QSA_LAUNCH_STREAM(1); break;
+      case 2: QSA_LAUNCH_STREAM(2); break;
+      case 4: QSA_LAUNCH_STREAM(4); break;
+      case 8: QSA_LAUNCH_STREAM(8); break;
+      case 16: QSA_LAUNCH_STREAM(16); break;
+      default: return hipErrorInvalidValue;
+    }
 #undef QSA_LAUNCH_STREAM
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t nw = (int64_t)batch * n_q;
-  hipLaunchKernelGGL(index_select_kernel, dim3((unsigned)((nw + 3) / 4)), dim3(256), 0, stream,
-                     buf, cnt, q_pos0, batch, n_q, r, k, p.splits, p.cap, sel, sel_cnt);
+  hipLaunchKernelGGL(index_select_kernel, dim3((unsigned)nw), dim3(256), p.select_lds, stream, buf, cnt,
+                     q_pos0, n_q, r, k, p.splits, p.cap, sel, sel_cnt);
   return hipGetLastError();
 }
 

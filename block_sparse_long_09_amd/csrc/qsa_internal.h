@@ -13,6 +13,8 @@ hipError_t launch_compress(const uint16_t* idx_k, int64_t k_stride, int batch, i
 
 // How qsa_index_topk cuts its work: wave tasks = (query group, candidate split).
 struct IndexPlan {
+  bool decode;     // one query per sequence: split scan + verified merge
+  bool wide;       // >= 64 queries per sequence: LDS-pipelined workgroup kernel
   int hi;          // indexer heads
   int at;          // 32-row A tiles per wave (4 for prefill, 1 for few queries)
   int qw;          // queries per wave
@@ -21,7 +23,10 @@ struct IndexPlan {
   int split_len;   // candidates per split (multiple of 32)
   int cap;         // buffer entries per (query, split)
   int64_t max_cand;
+  int64_t score_stride;             // decode: floats per sequence in the score array
+  size_t local_off, meta_off;       // decode: workspace offsets
   size_t buf_bytes, cnt_bytes, workspace;
+  size_t stream_lds, select_lds;    // dynamic LDS bytes of the two kernels
 };
 
 IndexPlan plan_index(int hi, int k, int batch, int n_q, int64_t max_q_end, int r);

@@ -1,0 +1,187 @@
+// Exact rank selection building blocks (wave and workgroup level).
+//
+// Keys are uint32: the bit patterns of non-negative fp32 scores, which order
+// like the scores. "Select" finds tk, the keep-th largest key, and `need`, how
+// many entries equal to tk belong to the top `keep` (the first ones in list
+// order). Four most-significant-digit-first passes of 8 bits with a 256-bin LDS
+// histogram. "Stable keep" then emits, in list order, every entry with key > tk
+// and the first `need` entries with key == tk; lists are kept in increasing
+// block index, so this realises the (score desc, index asc) order exactly.
+#pragma once
+
+#include "qsa_device.h"
+
+namespace qsa {
+
+// One wave reads the histogram and finds the digit where the count from the
+// top reaches `need`; `above` is the count of strictly larger digits.
+template <typename HistPtr>
+__device__ __forceinline__ void wave_find_digit(HistPtr hist, uint32_t need, int& dig, uint32_t& above) {
+  const int lane = lane_id();
+  const int top = 255 - 4 * lane;  // lane 0 owns the largest digits
+  const uint32_t c0 = hist[top], c1 = hist[top - 1], c2 = hist[top - 2], c3 = hist[top - 3];
+  const uint32_t tot = c0 + c1 + c2 + c3;
+  uint32_t inc = tot;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const uint32_t v = __shfl_up(inc, off);
+    if (lane >= off) inc += v;
+  }
+  const uint32_t exc = inc - tot;
+  const bool hit = inc >= need && exc < need;
+  const int L = __ffsll((unsigned long long)ballot(hit)) - 1;
+  int d = 0;
+  uint32_t cum = exc;
+  if (cum + c0 >= need) {
+    d = top;
+  } else {
+    cum += c0;
+    if (cum + c1 >= need) {
+      d = top - 1;
+    } else {
+      cum += c1;
+      if (cum + c2 >= need) {
+        d = top - 2;
+      } else {
+        cum += c2;
+        d = top - 3;
+      }
+    }
+  }
+  dig = __shfl(d, L);
+  above = __shfl(cum, L);
+}
+
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+}
+
+// Wave-level select over n keys given by key(i) (cheap to read, e.g. LDS).
+template <typename KeyFn, typename HistPtr>
+__device__ void wave_select(KeyFn key, int n, int keep, HistPtr hist, uint32_t& tk, int& need_out,
+                            uint32_t* ties_out = nullptr) {
+  const int lane = lane_id();
+  uint32_t prefix = 0, mask = 0;
+  uint32_t need = (uint32_t)keep;
+  uint32_t ties = 0;
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    for (int i = lane; i < 256; i += kWave) hist[i] = 0;
+    wave_sync();
+    for (int i = lane; i < n; i += kWave) {
+      const uint32_t k = key(i);
+      if ((k & mask) == prefix) __atomic_fetch_add(&hist[(k >> shift) & 255u], 1u, __ATOMIC_RELAXED);
+    }
+    wave_sync();
+    int dig;
+    uint32_t above;
+    wave_find_digit(hist, need, dig, above);
+    if (shift == 0) ties = hist[dig];
+    prefix |= (uint32_t)dig << shift;
+    mask |= 255u << shift;
+    need -= above;
+    wave_sync();
+  }
+  tk = prefix;
+  need_out = (int)need;
+  if (ties_out) *ties_out = ties;
+}
+
+// Wave-level stable keep over entries get(i), i < n, emitting emit(pos, e).
+template <typename GetFn, typename EmitFn>
+__device__ int wave_stable_keep(GetFn get, int n, uint32_t tk, int need, EmitFn emit) {
+  const int lane = lane_id();
+  int kept = 0, ties = 0;
+  for (int base = 0; base < n; base += kWave) {
+    const int i = base + lane;
+    const bool in = i < n;
+    const uint2 e = in ? get(i) : make_uint2(0u, 0u);
+    const bool gt = in && e.x > tk;
+    const bool eq = in && e.x == tk;
+    const uint64_t me = ballot(eq);
+    const int tie_rank = ties + __popcll(lanes_below(me));
+    const bool keep = gt || (eq && tie_rank < need);
+    const uint64_t mk = ballot(keep);
+    if (keep) emit(kept + __popcll(lanes_below(mk)), e);
+    kept += __popcll(mk);
+    ties += __popcll(me);
+  }
+  return kept;
+}
+
+// Workgroup-level (NT threads) select; hist: 256 bins, bc: 2 words, both LDS.
+template <int NT, typename KeyFn>
+__device__ void block_select(KeyFn key, int n, int keep, uint32_t* hist, uint32_t* bc, uint32_t& tk,
+                             int& need_out) {
+  const int tid = threadIdx.x;
+  uint32_t prefix = 0, mask = 0;
+  uint32_t need = (uint32_t)keep;
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    for (int i = tid; i < 256; i += NT) hist[i] = 0;
+    __syncthreads();
+    for (int i = tid; i < n; i += NT) {
+      const uint32_t k = key(i);
+      if ((k & mask) == prefix) atomicAdd(&hist[(k >> shift) & 255u], 1u);
+    }
+    __syncthreads();
+    if (tid < kWave) {
+      int dig;
+      uint32_t above;
+      wave_find_digit(hist, need, dig, above);
+      if (tid == 0) {
+        bc[0] = (uint32_t)dig;
+        bc[1] = above;
+      }
+    }
+    __syncthreads();
+    prefix |= bc[0] << shift;
+    mask |= 255u << shift;
+    need -= bc[1];
+    __syncthreads();
+  }
+  tk = prefix;
+  need_out = (int)need;
+}
+
+// Workgroup-level stable keep; cnt: 2 * (NT / 64) words of LDS.
+template <int NT, typename GetFn, typename EmitFn>
+__device__ int block_stable_keep(GetFn get, int n, uint32_t tk, int need, uint32_t* cnt, EmitFn emit) {
+  constexpr int NW = NT / kWave;
+  const int tid = threadIdx.x;
+  const int w = tid / kWave;
+  int kept = 0, ties = 0;
+  for (int base = 0; base < n; base += NT) {
+    const int i = base + tid;
+    const bool in = i < n;
+    const uint2 e = in ? get(i) : make_uint2(0u, 0u);
+    const bool gt = in && e.x > tk;
+    const bool eq = in && e.x == tk;
+    const uint64_t me = ballot(eq);
+    if (lane_id() == 0) cnt[w] = (uint32_t)__popcll(me);
+    __syncthreads();
+    int eq_before = 0, eq_all = 0;
+#pragma unroll
+    for (int v = 0; v < NW; ++v) {
+      eq_before += v < w ? (int)cnt[v] : 0;
+      eq_all += (int)cnt[v];
+    }
+    const int tie_rank = ties + eq_before + __popcll(lanes_below(me));
+    const bool keep = gt || (eq && tie_rank < need);
+    const uint64_t mk = ballot(keep);
+    if (lane_id() == 0) cnt[NW + w] = (uint32_t)__popcll(mk);
+    __syncthreads();
+    int k_before = 0, k_all = 0;
+#pragma unroll
+    for (int v = 0; v < NW; ++v) {
+      k_before += v < w ? (int)cnt[NW + v] : 0;
+      k_all += (int)cnt[NW + v];
+    }
+    if (keep) emit(kept + k_before + __popcll(lanes_below(mk)), e);
+    kept += k_all;
+    ties += eq_all;
+    __syncthreads();
+  }
+  return kept;
+}
+
+}  // namespace qsa

@@ -276,27 +276,56 @@ __global__ __launch_bounds__(256) void attn_gather_kernel(
   }
 }
 
-// Merge split-KV partials: one workgroup (128 threads = head dim) per (row, head).
+// Merge split-KV partials: one workgroup (128 threads = head dim) per (row,
+// head). The per-split (m, l) pairs are read in parallel into LDS, reduced,
+// and turned into weights; each thread then sums its dimension over the
+// splits with independent loads.
+constexpr int kMaxMergeSplits = 1024;
+
 __global__ __launch_bounds__(128) void attn_merge_kernel(const float* __restrict__ part_o,
                                                          const float2* __restrict__ part_ml,
                                                          int n_splits, int Hq,
                                                          uint16_t* __restrict__ out,
                                                          float* __restrict__ lse) {
+  __shared__ float wsplit[kMaxMergeSplits];
+  __shared__ float red[2][2];
   const int64_t row = blockIdx.x;
   const int h = blockIdx.y;
   const int d = threadIdx.x;
-  float M = -INFINITY;
-  for (int s = 0; s < n_splits; ++s) M = fmaxf(M, part_ml[(row * n_splits + s) * Hq + h].x);
-  float L = 0.0f, acc = 0.0f;
-  for (int s = 0; s < n_splits; ++s) {
-    const int64_t idx = (row * n_splits + s) * Hq + h;
-    const float2 ml = part_ml[idx];
-    if (ml.y > 0.0f) {
-      const float f = exp2f(ml.x - M);
-      L += ml.y * f;
-      acc += part_o[idx * kD + d] * f;
-    }
+  const int64_t base = row * n_splits * (int64_t)Hq + h;  // index of split 0
+  float m_loc = -INFINITY;
+  for (int s = d; s < n_splits; s += 128) {
+    const float2 ml = part_ml[base + (int64_t)s * Hq];
+    wsplit[s] = ml.x;
+    if (ml.y > 0.0f) m_loc = fmaxf(m_loc, ml.x);
   }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) m_loc = fmaxf(m_loc, __shfl_xor(m_loc, off));
+  if ((d & 63) == 0) red[0][d >> 6] = m_loc;
+  __syncthreads();
+  const float M = fmaxf(red[0][0], red[0][1]);
+  float l_loc = 0.0f;
+  for (int s = d; s < n_splits; s += 128) {
+    const float2 ml = part_ml[base + (int64_t)s * Hq];
+    const float w = ml.y > 0.0f ? exp2f(wsplit[s] - M) : 0.0f;
+    wsplit[s] = w;
+    l_loc += ml.y * w;
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) l_loc += __shfl_xor(l_loc, off);
+  if ((d & 63) == 0) red[1][d >> 6] = l_loc;
+  __syncthreads();
+  const float L = red[1][0] + red[1][1];
+  float acc = 0.0f;
+  int s = 0;
+  for (; s + 8 <= n_splits; s += 8) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = part_o[(base + (int64_t)(s + u) * Hq) * kD + d];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc += v[u] * wsplit[s + u];
+  }
+  for (; s < n_splits; ++s) acc += part_o[(base + (int64_t)s * Hq) * kD + d] * wsplit[s];
   out[(row * Hq + h) * kD + d] = (uint16_t)f32_to_bf16_bits(acc / L);
   if (lse && d == 0) lse[row * Hq + h] = (M + log2f(L)) * 0.69314718055994531f;
 }
@@ -307,6 +336,7 @@ AttnPlan plan_attn(int batch_rows, int64_t max_tokens, bool split_kv) {
   int64_t splits = 1;
   if (split_kv) {
     splits = (1024 + batch_rows - 1) / batch_rows;
+    if (splits > kMaxMergeSplits) splits = kMaxMergeSplits;
     const int64_t max_splits = (max_tokens + kChunk - 1) / kChunk;
     if (splits > max_splits) splits = max_splits;
     if (splits < 1) splits = 1;
