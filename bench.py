@@ -126,7 +126,6 @@ def main():
     ap.add_argument("--config", default="c5", choices=["c5", "c3", "c4"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
-    ap.add_argument("--dense-prefill", action="store_true", help="also time dense prefill (slow comparator)")
     ap.add_argument("--cpu-sample", type=int, default=256, help="queries in the oracle's timed sample")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="also run one plain device copy of this size (counter calibration runs)")
@@ -298,7 +297,7 @@ def main():
             dense["decode_us"] = dms * 1e3
             dense["decode_GBps"] = D["work"]["dense_bytes"] / (dms * 1e-3) / 1e9
             dense["decode_speedup_sparse_vs_dense"] = dms / decode_ms
-        if Wp is not None and args.dense_prefill:
+        if Wp is not None:
             W = Wp
             desc = qsa.attn_desc(W.Hq, W.Hkv, W.D)
             dout = torch.empty((P["chunk"], W.Hq, W.D), dtype=torch.bfloat16, device=dev)

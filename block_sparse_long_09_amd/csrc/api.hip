@@ -270,12 +270,12 @@ qsa_status_t qsa_dense_attn_prefill(const qsa_attn_desc_t* desc, const uint16_t*
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16))
     return fail(QSA_ERR_MISALIGNED, "q/k/v/out must be 16-byte aligned");
   if (!aligned(lse, 4)) return fail(QSA_ERR_MISALIGNED, "lse must be 4-byte aligned");
+  if (32 % (desc->n_q_heads / desc->n_kv_heads))
+    return fail(QSA_ERR_UNSUPPORTED, "dense prefill needs a group size dividing 32");
   (void)workspace;
   (void)workspace_bytes;
-  const qsa::AttnPlan p = qsa::plan_attn(n_q, q_pos0 + n_q, false);
-  return hip_status(qsa::launch_attn(p, q, k, v, 0, q_pos0, nullptr, desc->n_q_heads,
-                                     desc->n_kv_heads, 1, 1, nullptr, nullptr,
-                                     desc->softmax_scale, out, lse, nullptr, (hipStream_t)stream),
+  return hip_status(qsa::launch_dense_prefill(q, k, v, q_pos0, n_q, desc->n_q_heads, desc->n_kv_heads,
+                                              desc->softmax_scale, out, lse, (hipStream_t)stream),
                     "dense_attn_prefill launch");
 }
 

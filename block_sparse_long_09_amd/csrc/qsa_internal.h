@@ -53,4 +53,9 @@ hipError_t launch_attn(const AttnPlan& p, const uint16_t* q, const uint16_t* k, 
                        int Hkv, int r, int top_k, const int32_t* sel, const int32_t* sel_cnt,
                        float scale, uint16_t* out, float* lse, void* ws, hipStream_t stream);
 
+// Dense causal GQA flash attention (comparator), prefill rows at q_pos0 + i.
+hipError_t launch_dense_prefill(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t q_pos0,
+                                int n_q, int Hq, int Hkv, float scale, uint16_t* out, float* lse,
+                                hipStream_t stream);
+
 }  // namespace qsa
