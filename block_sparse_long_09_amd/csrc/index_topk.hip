@@ -146,6 +146,74 @@ __device__ __noinline__ float compact_keys_staged(glb_u64* p, int n, int keep, l
   return __uint_as_float(tk);
 }
 
+// Approximate in-loop compaction: keep, in block order, every entry whose key
+// is at least L, where L is the lower edge of the 16-bit key bucket that holds
+// the keep-th largest key (two 8-bit histogram passes over keys staged in
+// LDS). At least `keep` entries survive, so the buffer stays a superset of
+// the exact top `keep`; a later candidate with key <= L can never enter it (at
+// least `keep` entries with key >= L and a smaller block index precede it).
+// Returns L; *kept_out receives the number of entries kept.
+__device__ __noinline__ uint32_t compact_keys_approx(glb_u64* p, int n, int keep, lds_u32* hist,
+                                                     lds_u32* kstage, int* kept_out) {
+  const int lane = lane_id();
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+  for (int base = 0; base < n; base += 16 * kWave) {
+    uint32_t v[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int i = base + u * kWave + lane;
+      v[u] = i < n ? (uint32_t)p[i] : 0u;
+    }
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int i = base + u * kWave + lane;
+      if (i < n) kstage[i] = v[u];
+    }
+  }
+  wave_sync();
+  uint32_t prefix = 0, mask = 0, need = (uint32_t)keep;
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+    const int shift = pass == 0 ? 24 : 16;
+    for (int i = lane; i < 256; i += kWave) hist[i] = 0;
+    wave_sync();
+    for (int i = lane; i < n; i += kWave) {
+      const uint32_t k = kstage[i];
+      if ((k & mask) == prefix) __atomic_fetch_add(&hist[(k >> shift) & 255u], 1u, __ATOMIC_RELAXED);
+    }
+    wave_sync();
+    int dig;
+    uint32_t above;
+    wave_find_digit(hist, need, dig, above);
+    prefix |= (uint32_t)dig << shift;
+    mask |= 255u << shift;
+    need -= above;
+    wave_sync();
+  }
+  const uint32_t L = prefix;
+  int kept = 0;
+  for (int base = 0; base < n; base += 16 * kWave) {
+    unsigned long long e[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int i = base + u * kWave + lane;
+      e[u] = i < n ? p[i] : 0ull;
+    }
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int i = base + u * kWave + lane;
+      const bool keep_it = i < n && (uint32_t)e[u] >= L;
+      const uint64_t mk = ballot(keep_it);
+      if (keep_it) p[kept + __popcll(lanes_below(mk))] = e[u];
+      kept += __popcll(mk);
+    }
+  }
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+  wave_sync();
+  *kept_out = kept;
+  return L;
+}
+
 }  // namespace
 
 template <int HI, int AT>
@@ -343,11 +411,16 @@ __global__ __launch_bounds__(256) void index_stream_kernel(
 
 // Prefill indexer for many queries per sequence (n_q >= 64): a workgroup of 4
 // waves (4 x QW queries) shares one candidate split. Block keys travel
-// HBM -> registers (three 64-candidate tiles ahead) -> a 3-slot LDS ring
+// HBM -> registers (one 64-candidate tile ahead) -> a 2-slot LDS ring
 // (XOR-swizzled 16-byte parts so the B-fragment reads hit distinct banks) ->
-// B fragments; one barrier per tile. The per-query threshold / append /
-// compaction logic is the same as in index_stream_kernel.
-template <int HI, int AT>
+// B fragments; one barrier per tile. Per query: running exact threshold and a
+// (score, block) buffer as in index_stream_kernel; a wave compacts its own
+// buffers (keys staged in its LDS area) when one nears capacity. Splits end
+// with at most `cap` entries; the select kernel takes them as they are.
+#ifndef QSA_PREFILL_PREFETCH
+#define QSA_PREFILL_PREFETCH 2  // 64-candidate tiles in flight in registers
+#endif
+template <int HI, int AT, bool SCALE_EPI>
 __global__ __launch_bounds__(256, 2) void index_prefill_kernel(
     const uint16_t* __restrict__ idx_q, const uint16_t* __restrict__ cmp_k, int64_t cmp_stride,
     const int32_t* __restrict__ q_pos0, int n_q, int r, int keep, float a_scale, float w_epi,
@@ -359,12 +432,13 @@ __global__ __launch_bounds__(256, 2) void index_prefill_kernel(
   constexpr int NS = AT * QPH;
   constexpr int TILE = 64;                       // candidates per LDS tile
   constexpr int TILE_BYTES = TILE * 128;         // 8 KiB
-  constexpr int NSLOT = 2;
+  constexpr int PF = QSA_PREFILL_PREFETCH;
+  static_assert(PF >= 2, "the LDS ring needs two slots at least");
+  constexpr int NSLOT = PF;                      // LDS slots
+  __shared__ __attribute__((aligned(16))) unsigned char ring[NSLOT * TILE_BYTES];
   __shared__ uint32_t hist_all[4][256];
-  __shared__ int wg_lim[2][4];
-  extern __shared__ __attribute__((aligned(16))) unsigned char dyn[];
-  unsigned char* ring = dyn;                                   // NSLOT * 8 KiB
-  uint32_t* kstage_all = reinterpret_cast<uint32_t*>(dyn + NSLOT * TILE_BYTES);  // 4 * cap words
+  __shared__ int wg_lim[4];
+  extern __shared__ uint32_t kstage_all[];  // 4 x cap keys: each wave's compaction stage
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -374,8 +448,8 @@ __global__ __launch_bounds__(256, 2) void index_prefill_kernel(
   const int qg = blockIdx.x * 4 + wave;
   const int split = blockIdx.y;
   const int b = blockIdx.z;
-  uint32_t* hist = hist_all[wave];
-  uint32_t* kstage = kstage_all + (size_t)wave * cap;
+  lds_u32* hist_l = (lds_u32*)hist_all[wave];
+  lds_u32* kstage_l = (lds_u32*)(kstage_all + wave * cap);
 
   const int64_t pos0 = q_pos0[b];
   const int sbeg = split * split_len;
@@ -385,12 +459,12 @@ __global__ __launch_bounds__(256, 2) void index_prefill_kernel(
     return buf + (((int64_t)b * n_q + qi) * splits + split) * (int64_t)cap;
   };
   const bool wave_live = qg < n_qgroups;
-
   // candidates of query qi in this split: [sbeg, lim_of(qi))
   auto lim_of = [&](int qi) {
     const int64_t bt = (pos0 + qi) / r;
     return (int)(bt < (int64_t)send ? bt : (int64_t)send);
   };
+
   float tau[NS];
   int cnt[NS];
   int maxlim = 0, minlim = 0x7FFFFFFF;
@@ -402,7 +476,7 @@ __global__ __launch_bounds__(256, 2) void index_prefill_kernel(
       l = lim_of(qi);
       minlim = min(minlim, l);
     }
-    tau[s] = (wave_live && qi < n_q) ? -1.0f : INFINITY;
+    tau[s] = (wave_live && qi < n_q) ? -1.0f : INFINITY;  // an absent query takes nothing
     cnt[s] = 0;
     maxlim = max(maxlim, l);
   }
@@ -411,11 +485,9 @@ __global__ __launch_bounds__(256, 2) void index_prefill_kernel(
     maxlim = max(maxlim, __shfl_xor(maxlim, off));
     minlim = min(minlim, __shfl_xor(minlim, off));
   }
-  if (lane == 0) {
-    wg_lim[0][wave] = maxlim;
-  }
+  if (lane == 0) wg_lim[wave] = maxlim;
   __syncthreads();
-  const int wg_max = max(max(wg_lim[0][0], wg_lim[0][1]), max(wg_lim[0][2], wg_lim[0][3]));
+  const int wg_max = max(max(wg_lim[0], wg_lim[1]), max(wg_lim[2], wg_lim[3]));
 
   if (keep > 0 && wg_max > sbeg) {
     u32x4 A[AT][4];
@@ -441,8 +513,6 @@ __global__ __launch_bounds__(256, 2) void index_prefill_kernel(
     }
     const unsigned char* kb = reinterpret_cast<const unsigned char*>(cmp_k + (int64_t)b * cmp_stride);
     const int ntiles = (wg_max - sbeg + TILE - 1) / TILE;
-    lds_u32* hist_l = (lds_u32*)hist;
-    lds_u32* kstage_l = (lds_u32*)kstage;
     // this thread's two 16-byte parts of every tile: chunk c = tid + 256u,
     // candidate row c / 8, part c % 8, stored at part (c % 8) ^ (row % 8)
     auto load_tile = [&](int t, u32x4* R) {
@@ -461,8 +531,8 @@ __global__ __launch_bounds__(256, 2) void index_prefill_kernel(
         *reinterpret_cast<u32x4*>(ring + slot * TILE_BYTES + row * 128 + (((c & 7) ^ (row & 7)) * 16)) = R[u];
       }
     };
-    // compact every buffer of this wave that holds more than `limit` entries
-    auto compact_over = [&](int limit, bool raise) {
+    // compact this wave's buffers holding more than `limit` entries
+    auto compact_over = [&](int limit) {
       uint32_t need_mask = 0;  // bit 2s+hh: slot s of lane-half hh
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
@@ -479,19 +549,27 @@ __global__ __launch_bounds__(256, 2) void index_prefill_kernel(
         for (int s2 = 0; s2 < NS; ++s2)
           if (s2 == s) cs = cnt[s2];
         const int ch = __builtin_amdgcn_readlane(cs, 32 * hh);
-        const float ntau = compact_keys_staged((glb_u64*)buf_of(slot_query(s, hh)), ch, keep, hist_l, kstage_l);
+        glb_u64* bp = (glb_u64*)buf_of(slot_query(s, hh));
+        int kept;
+        uint32_t L = compact_keys_approx(bp, ch, keep, hist_l, kstage_l, &kept);
+        if (kept > cap - 2 * TILE) {
+          // the threshold's bucket is too full (many equal keys): compact exactly
+          L = __float_as_uint(compact_keys_staged(bp, kept, keep, hist_l, kstage_l));
+          kept = keep;
+        }
         if (half == hh) {
 #pragma unroll
           for (int s2 = 0; s2 < NS; ++s2)
             if (s2 == s) {
-              cnt[s2] = keep;
-              if (raise) tau[s2] = ntau;
+              cnt[s2] = kept;
+              tau[s2] = __uint_as_float(L);
             }
         }
       }
     };
     auto process = [&](int t, int slot) {
       const unsigned char* sl = ring + slot * TILE_BYTES;
+      bool appended = false;
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) {
         const int c = sbeg + t * TILE + nt * 32;
@@ -510,53 +588,65 @@ __global__ __launch_bounds__(256, 2) void index_prefill_kernel(
           for (int ks = 0; ks < 4; ++ks) acc[a] = mfma32x32x16(A[a][ks], B[ks], acc[a]);
         }
         const int j = c + col;
-        const uint32_t below = (1u << col) - 1u;
-        const bool interior = c + 32 <= minlim;
+        const bool interior = c + 32 <= minlim;  // every query of the wave sees the whole tile
+        float sc[NS];
+        uint64_t m64[NS];
+        uint64_t any = 0;
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
           const int a = s / QPH, qq = s % QPH;
-          float sum = 0.0f;
+          float sum = relu_bits(acc[a][qq * HI]);
 #pragma unroll
-          for (int hd = 0; hd < HI; ++hd) sum += relu_bits(acc[a][qq * HI + hd]);
-          const float sc = sum * w_epi;
-          const bool pass = (interior || j < lim_of(slot_query(s, half))) && (sc > tau[s]);
-          const uint64_t m64 = ballot(pass);
-          if (m64) {
-            const uint32_t mh = (uint32_t)(m64 >> (32 * half));
-            if (pass) {
-              const int pos = cnt[s] + __popc(mh & below);
-              buf_of(slot_query(s, half))[pos] = make_uint2(__float_as_uint(sc), (uint32_t)j);
+          for (int hd = 1; hd < HI; ++hd) sum += relu_bits(acc[a][qq * HI + hd]);
+          sc[s] = SCALE_EPI ? sum * w_epi : sum;
+          m64[s] = ballot(sc[s] > tau[s]);
+          any |= m64[s];
+        }
+        if (any) {
+          const uint32_t below = (1u << col) - 1u;
+#pragma unroll
+          for (int s = 0; s < NS; ++s) {
+            bool pass = sc[s] > tau[s];
+            uint64_t mm = m64[s];
+            if (!interior) {
+              pass = pass && j < lim_of(slot_query(s, half));
+              mm = ballot(pass);
             }
-            cnt[s] += __popc(mh);
+            if (mm) {
+              appended = true;
+              const uint32_t mh = (uint32_t)(mm >> (32 * half));
+              if (pass) {
+                const int pos = cnt[s] + __popc(mh & below);
+                buf_of(slot_query(s, half))[pos] = make_uint2(__float_as_uint(sc[s]), (uint32_t)j);
+              }
+              cnt[s] += __popc(mh);
+            }
           }
         }
       }
       // at most 64 appends per buffer per tile: keep room for the next tile
-      bool over = false;
-#pragma unroll
-      for (int s = 0; s < NS; ++s) over |= cnt[s] > cap - TILE;
-      if (ballot(over)) compact_over(cap - TILE, true);
+      if (appended) compact_over(cap - TILE);
     };
-    // two register sets (tiles t and t + 1 in flight) and two LDS slots:
-    // iteration t stores tile t + 1, loads tile t + 2, computes tile t
-    u32x4 R0[2], R1[2];
-    load_tile(0, R0);
-    if (ntiles > 1) load_tile(1, R1);
-    store_tile(0, R0);
-    for (int t = 0; t < ntiles; t += 2) {
-      __syncthreads();
-      if (t + 1 < ntiles) store_tile(1, R1);
-      if (t + 2 < ntiles) load_tile(t + 2, R0);
-      process(t, 0);
-      if (t + 1 < ntiles) {
-        __syncthreads();
-        if (t + 2 < ntiles) store_tile(0, R0);
-        if (t + 3 < ntiles) load_tile(t + 3, R1);
-        process(t + 1, 1);
+    // PF register sets and PF LDS slots: iteration t stores tile t + 1 (loaded
+    // PF - 1 iterations earlier), issues the load of tile t + PF and computes
+    // tile t; slot / set of tile t = t % PF, one barrier per iteration.
+    u32x4 R[PF][2];
+#pragma unroll
+    for (int p = 0; p < PF; ++p)
+      if (p < ntiles) load_tile(p, R[p]);
+    store_tile(0, R[0]);
+    for (int t0 = 0; t0 < ntiles; t0 += PF) {
+#pragma unroll
+      for (int ph = 0; ph < PF; ++ph) {
+        const int t = t0 + ph;
+        if (t < ntiles) {
+          __syncthreads();
+          if (t + 1 < ntiles) store_tile((ph + 1) % PF, R[(ph + 1) % PF]);
+          if (t + PF < ntiles) load_tile(t + PF, R[ph]);
+          process(t, ph);
+        }
       }
     }
-    // leave every split buffer at most `keep` long
-    compact_over(keep, false);
   }
   if (wave_live && col == 0) {
 #pragma unroll
@@ -827,8 +917,9 @@ IndexPlan plan_index(int hi, int k, int batch, int n_q, int64_t max_q_end, int r
   }
   p.decode = false;
   p.wide = n_q >= 64;
-  // A tiles per wave in the LDS-pipelined kernel: 8 query slots per lane
-  p.at = p.wide ? (hi >= 8 ? 4 : (hi == 4 ? 2 : 1)) : 1;
+  // A tiles per wave in the LDS-pipelined kernel (8 query slots per lane, or
+  // 4 at 8 heads: 144 VGPRs instead of 219 lets 3 workgroups share a CU)
+  p.at = p.wide ? (hi == 16 ? 4 : (hi == 8 ? 2 : (hi == 4 ? 2 : 1))) : 1;
   p.qw = p.at * 32 / hi;
   p.n_qgroups = (n_q + p.qw - 1) / p.qw;
   int64_t splits;
@@ -859,9 +950,10 @@ IndexPlan plan_index(int hi, int k, int batch, int n_q, int64_t max_q_end, int r
   p.buf_bytes = (size_t)batch * n_q * p.splits * (size_t)cap * sizeof(uint2);
   p.cnt_bytes = (size_t)batch * n_q * p.splits * sizeof(int);
   p.workspace = p.buf_bytes + ((p.cnt_bytes + 255) / 256 * 256);
-  p.stream_lds = p.wide ? (size_t)2 * 64 * 128 + (size_t)4 * cap * sizeof(uint32_t)
-                           : (size_t)4 * cap * sizeof(uint2);
-  p.select_lds = (size_t)p.splits * (keep > 0 ? keep : 1) * sizeof(uint2);
+  // LDS per workgroup: the wide kernel stages 4 x cap keys, the other 4 x cap entries
+  p.stream_lds = (size_t)4 * cap * (p.wide ? sizeof(uint32_t) : sizeof(uint2));
+  // the wide kernel leaves up to `cap` entries per split; the other at most `keep`
+  p.select_lds = (size_t)p.splits * (p.wide ? cap : (keep > 0 ? keep : 1)) * sizeof(uint2);
   return p;
 }
 
@@ -902,14 +994,15 @@ hipError_t launch_index_topk(const IndexPlan& p, const uint16_t* idx_q, const ui
   if (p.wide) {
     const dim3 g1((p.n_qgroups + 3) / 4, p.splits, batch);
 #define QSA_LAUNCH_PREFILL(HI_, AT_)                                                               \
-  hipLaunchKernelGGL((index_prefill_kernel<HI_, AT_>), g1, dim3(256), p.stream_lds, stream, idx_q, cmp_k,  \
+  hipLaunchKernelGGL((exact_scale ? index_prefill_kernel<HI_, AT_, false>                        \
+                                  : index_prefill_kernel<HI_, AT_, true>), g1, dim3(256), p.stream_lds, stream, idx_q, cmp_k,  \
                      cmp_stride, q_pos0, n_q, r, k - 1, a_scale, w_epi, p.n_qgroups, p.splits,     \
                      p.split_len, p.cap, buf, cnt)
     switch (p.hi) {
       case 1: QSA_LAUNCH_PREFILL(1, 1); break;
       case 2: QSA_LAUNCH_PREFILL(2, 1); break;
       case 4: QSA_LAUNCH_PREFILL(4, 2); break;
-      case 8: QSA_LAUNCH_PREFILL(8, 4); break;
+      case 8: QSA_LAUNCH_PREFILL(8, 2); break;
       case 16: QSA_LAUNCH_PREFILL(16, 4); break;
       default: return hipErrorInvalidValue;
     }
