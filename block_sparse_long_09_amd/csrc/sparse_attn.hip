@@ -34,6 +34,7 @@ namespace {
 constexpr int kD = 128;        // head dim
 constexpr int kChunk = 32;     // tokens per chunk
 constexpr int kVPitch = 132;   // LDS row pitch of the V tile (elements)
+constexpr int kSelLds = 1024;  // kept block ids per split staged in LDS (top_k <= 1024)
 }  // namespace
 
 template <int HKV>
@@ -47,6 +48,7 @@ __global__ __launch_bounds__(256) void attn_gather_kernel(
   constexpr int WPH = 4 / HKV;  // waves per KV head
   __shared__ uint16_t vtile[4][kChunk * kVPitch];
   __shared__ float xm[4][16], xl[4][16];
+  __shared__ int32_t sblk[kSelLds];
 
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
@@ -73,6 +75,17 @@ __global__ __launch_bounds__(256) void attn_gather_kernel(
     for (int ks = 0; ks < 4; ++ks) Qf[ks] = l16 < G ? ld16(qp + 32 * ks) : u32x4{0u, 0u, 0u, 0u};
   }
 
+  // This split's kept block ids, staged in LDS once: the token gathers then
+  // never wait on a global load of the selection.
+  const int lr = __builtin_ctz((unsigned)r);  // r is a power of two
+  const int jb0 = (int)(p_beg >> lr);
+  if (srow) {
+    const int jb1 = p_end > p_beg ? (int)((p_end - 1) >> lr) + 1 : jb0;
+    const int nb = min(jb1 - jb0, kSelLds);
+    for (int i = threadIdx.x; i < nb; i += 256) sblk[i] = srow[jb0 + i];
+  }
+  __syncthreads();
+
   // Token of list position p, and whether it is attended.
   auto token_of = [&](int64_t p, bool& valid) -> int64_t {
     int64_t s;
@@ -81,8 +94,8 @@ __global__ __launch_bounds__(256) void attn_gather_kernel(
       return t;
     }
     if (srow) {
-      const int64_t j = srow[p / r];
-      s = j * r + (p % r);
+      const int j = sblk[(int)(p >> lr) - jb0];
+      s = ((int64_t)j << lr) + (p & (r - 1));
     } else {
       s = p;
     }
@@ -362,6 +375,7 @@ hipError_t launch_attn(const AttnPlan& p, const uint16_t* q, const uint16_t* k, 
                        int Hkv, int r, int top_k, const int32_t* sel, const int32_t* sel_cnt,
                        float scale, uint16_t* out, float* lse, void* ws, hipStream_t stream) {
   const int G = Hq / Hkv;
+  if (sel && top_k > kSelLds) return hipErrorInvalidValue;
   const float scale_log2 = scale * 1.4426950408889634f;
   float* part_o = nullptr;
   float2* part_ml = nullptr;
