@@ -467,6 +467,8 @@ __global__ __launch_bounds__(256, 2) void index_prefill_kernel(
 
   float tau[NS];
   int cnt[NS];
+  int lim[NS];        // candidate bound of this lane's query in slot s
+  glb_u64* bp[NS];    // its buffer
   int maxlim = 0, minlim = 0x7FFFFFFF;
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
@@ -478,6 +480,8 @@ __global__ __launch_bounds__(256, 2) void index_prefill_kernel(
     }
     tau[s] = (wave_live && qi < n_q) ? -1.0f : INFINITY;  // an absent query takes nothing
     cnt[s] = 0;
+    lim[s] = l;
+    bp[s] = (glb_u64*)buf_of(wave_live && qi < n_q ? qi : 0);
     maxlim = max(maxlim, l);
   }
 #pragma unroll
@@ -485,6 +489,7 @@ __global__ __launch_bounds__(256, 2) void index_prefill_kernel(
     maxlim = max(maxlim, __shfl_xor(maxlim, off));
     minlim = min(minlim, __shfl_xor(minlim, off));
   }
+  minlim = __builtin_amdgcn_readfirstlane(minlim);  // wave-uniform after the reduction
   if (lane == 0) wg_lim[wave] = maxlim;
   __syncthreads();
   const int wg_max = max(max(wg_lim[0], wg_lim[1]), max(wg_lim[2], wg_lim[3]));
@@ -549,12 +554,12 @@ __global__ __launch_bounds__(256, 2) void index_prefill_kernel(
         for (int s2 = 0; s2 < NS; ++s2)
           if (s2 == s) cs = cnt[s2];
         const int ch = __builtin_amdgcn_readlane(cs, 32 * hh);
-        glb_u64* bp = (glb_u64*)buf_of(slot_query(s, hh));
+        glb_u64* cb = (glb_u64*)buf_of(slot_query(s, hh));
         int kept;
-        uint32_t L = compact_keys_approx(bp, ch, keep, hist_l, kstage_l, &kept);
+        uint32_t L = compact_keys_approx(cb, ch, keep, hist_l, kstage_l, &kept);
         if (kept > cap - 2 * TILE) {
           // the threshold's bucket is too full (many equal keys): compact exactly
-          L = __float_as_uint(compact_keys_staged(bp, kept, keep, hist_l, kstage_l));
+          L = __float_as_uint(compact_keys_staged(cb, kept, keep, hist_l, kstage_l));
           kept = keep;
         }
         if (half == hh) {
@@ -603,29 +608,38 @@ __global__ __launch_bounds__(256, 2) void index_prefill_kernel(
           any |= m64[s];
         }
         if (any) {
+          // append each passing (score, block) to its query's buffer: lanes of
+          // one half share a query, so the ballot's half gives the positions
           const uint32_t below = (1u << col) - 1u;
-#pragma unroll
-          for (int s = 0; s < NS; ++s) {
-            bool pass = sc[s] > tau[s];
-            uint64_t mm = m64[s];
-            if (!interior) {
-              pass = pass && j < lim_of(slot_query(s, half));
-              mm = ballot(pass);
-            }
+          auto append = [&](int s, uint64_t mm, bool pass) {
             if (mm) {
-              appended = true;
-              const uint32_t mh = (uint32_t)(mm >> (32 * half));
-              if (pass) {
-                const int pos = cnt[s] + __popc(mh & below);
-                buf_of(slot_query(s, half))[pos] = make_uint2(__float_as_uint(sc[s]), (uint32_t)j);
-              }
+              const uint32_t mh = half ? (uint32_t)(mm >> 32) : (uint32_t)mm;
+              if (pass)
+                bp[s][cnt[s] + __popc(mh & below)] =
+                    (unsigned long long)__float_as_uint(sc[s]) | ((unsigned long long)(uint32_t)j << 32);
               cnt[s] += __popc(mh);
             }
+          };
+          if (interior) {
+#pragma unroll
+            for (int s = 0; s < NS; ++s) append(s, m64[s], sc[s] > tau[s]);
+          } else {
+#pragma unroll
+            for (int s = 0; s < NS; ++s) {
+              const bool pass = sc[s] > tau[s] && j < lim[s];
+              append(s, ballot(pass), pass);
+            }
           }
+          appended = true;
         }
       }
       // at most 64 appends per buffer per tile: keep room for the next tile
-      if (appended) compact_over(cap - TILE);
+      if (appended) {
+        bool over = false;
+#pragma unroll
+        for (int s = 0; s < NS; ++s) over |= cnt[s] > cap - TILE;
+        if (ballot(over)) compact_over(cap - TILE);
+      }
     };
     // PF register sets and PF LDS slots: iteration t stores tile t + 1 (loaded
     // PF - 1 iterations earlier), issues the load of tile t + PF and computes
