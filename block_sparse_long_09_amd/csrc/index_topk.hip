@@ -44,9 +44,11 @@ namespace qsa {
 
 namespace {
 
-constexpr int kDecodeSplit = 1024;  // candidates per decode split
-constexpr int kDecodeLocal = 32;    // entries kept per decode split
-constexpr int kDecodeMaxSplits = 256;  // splits one select workgroup can stage in LDS
+constexpr int kScanThreads = 512;              // decode split scan: 256 candidates per wave
+constexpr int kDecodeSplit = kScanThreads * 4;  // candidates per decode split
+constexpr int kMergeThreads = 1024;             // decode merge
+constexpr int kDecodeMaxSplits = 1024;  // decode splits per sequence
+constexpr size_t kMergeMaxLds = 144 * 1024;  // merge LDS for the staged split lists
 
 __device__ __forceinline__ float relu_bits(float x) {
   // max on the integer view: negative values and -0.0 become +0.0
@@ -147,16 +149,19 @@ __device__ __noinline__ float compact_keys_staged(glb_u64* p, int n, int keep, l
 }
 
 // Approximate in-loop compaction: keep, in block order, every entry whose key
-// is at least L, where L is the lower edge of the 16-bit key bucket that holds
-// the keep-th largest key (two 8-bit histogram passes over keys staged in
-// LDS). At least `keep` entries survive, so the buffer stays a superset of
-// the exact top `keep`; a later candidate with key <= L can never enter it (at
-// least `keep` entries with key >= L and a smaller block index precede it).
-// Returns L; *kept_out receives the number of entries kept.
-__device__ __noinline__ uint32_t compact_keys_approx(glb_u64* p, int n, int keep, lds_u32* hist,
-                                                     lds_u32* kstage, int* kept_out) {
+// is at least L, where L is the lower edge of the histogram bucket that holds
+// the keep-th largest key. The keys are staged in LDS and bucketed by their
+// offset from the smallest key (8 bits per pass below the offsets' leading
+// zeros); a second pass refines the bucket only if more than `limit` entries
+// would survive. At least `keep` entries survive, so the buffer stays a
+// superset of the exact top `keep`; a later candidate with key <= L can never
+// enter it (at least `keep` entries with key >= L and a smaller block index
+// precede it). Returns L; *kept_out receives the number of entries kept.
+__device__ __noinline__ uint32_t compact_keys_approx(glb_u64* p, int n, int keep, int limit,
+                                                     lds_u32* hist, lds_u32* kstage, int* kept_out) {
   const int lane = lane_id();
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
   for (int base = 0; base < n; base += 16 * kWave) {
     uint32_t v[16];
 #pragma unroll
@@ -167,30 +172,47 @@ __device__ __noinline__ uint32_t compact_keys_approx(glb_u64* p, int n, int keep
 #pragma unroll
     for (int u = 0; u < 16; ++u) {
       const int i = base + u * kWave + lane;
-      if (i < n) kstage[i] = v[u];
+      if (i < n) {
+        kstage[i] = v[u];
+        kmin = min(kmin, v[u]);
+        kmax = max(kmax, v[u]);
+      }
     }
   }
-  wave_sync();
-  uint32_t prefix = 0, mask = 0, need = (uint32_t)keep;
 #pragma unroll
-  for (int pass = 0; pass < 2; ++pass) {
-    const int shift = pass == 0 ? 24 : 16;
+  for (int off = 32; off > 0; off >>= 1) {
+    kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, off));
+    kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, off));
+  }
+  wave_sync();
+  // radix passes on key - kmin: the bucket [kbase, kbase + 2^hi) holds the
+  // keep-th largest key
+  uint32_t kbase = kmin;
+  int hi = range_bits(kmin, kmax);
+  uint32_t need = (uint32_t)keep;
+  uint32_t above_all = 0;        // entries above the bucket
+  uint32_t ge = (uint32_t)n;     // entries with key >= kbase
+  for (int pass = 0; pass < 2 && hi > 0 && ge > (uint32_t)limit; ++pass) {
+    const int lo = hi > 8 ? hi - 8 : 0;
     for (int i = lane; i < 256; i += kWave) hist[i] = 0;
     wave_sync();
     for (int i = lane; i < n; i += kWave) {
-      const uint32_t k = kstage[i];
-      if ((k & mask) == prefix) __atomic_fetch_add(&hist[(k >> shift) & 255u], 1u, __ATOMIC_RELAXED);
+      const int d = range_digit(kstage[i], kbase, hi, lo);
+      if (d >= 0) __atomic_fetch_add(&hist[d], 1u, __ATOMIC_RELAXED);
     }
     wave_sync();
     int dig;
     uint32_t above;
     wave_find_digit(hist, need, dig, above);
-    prefix |= (uint32_t)dig << shift;
-    mask |= 255u << shift;
-    need -= above;
+    const uint32_t in_bucket = hist[dig];
     wave_sync();
+    kbase += (uint32_t)dig << lo;
+    need -= above;
+    above_all += above;
+    ge = above_all + in_bucket;
+    hi = lo;
   }
-  const uint32_t L = prefix;
+  const uint32_t L = kbase;
   int kept = 0;
   for (int base = 0; base < n; base += 16 * kWave) {
     unsigned long long e[16];
@@ -556,7 +578,7 @@ __global__ __launch_bounds__(256, 2) void index_prefill_kernel(
         const int ch = __builtin_amdgcn_readlane(cs, 32 * hh);
         glb_u64* cb = (glb_u64*)buf_of(slot_query(s, hh));
         int kept;
-        uint32_t L = compact_keys_approx(cb, ch, keep, hist_l, kstage_l, &kept);
+        uint32_t L = compact_keys_approx(cb, ch, keep, cap - 2 * TILE, hist_l, kstage_l, &kept);
         if (kept > cap - 2 * TILE) {
           // the threshold's bucket is too full (many equal keys): compact exactly
           L = __float_as_uint(compact_keys_staged(cb, kept, keep, hist_l, kstage_l));
@@ -723,31 +745,44 @@ __global__ __launch_bounds__(256) void index_select_kernel(
 }
 
 // ------------------------------------------------------------------ decode --
+// Split scan: one workgroup (8 waves) per (split of kDecodeSplit candidates,
+// sequence). Each wave scores 256 candidates (8 tiles of 32, 4 in flight) into
+// LDS and into the score row (kept for the exact fallback). The workgroup then
+// lists, in block order, the split's entries with key >= Ls, where Ls is the
+// lower edge of the histogram bucket holding the split's list_min-th largest
+// key, refined (8 bits per pass, below the bits common to all keys) until at
+// most list_cap entries remain; only when those are all equal to one key is
+// the list cut, in block order. The list goes to list_cap slots with keys
+// shifted by one (0 marks an empty slot); meta = {entries, largest key left
+// out or -1}.
 template <int HI>
-__global__ __launch_bounds__(256) void index_decode_scan_kernel(
+__global__ __launch_bounds__(kScanThreads) void index_decode_scan_kernel(
     const uint16_t* __restrict__ idx_q, const uint16_t* __restrict__ cmp_k, int64_t cmp_stride,
-    const int32_t* __restrict__ q_pos0, int r, float a_scale, float w_epi, int splits,
-    float* __restrict__ scores, int64_t score_stride, uint2* __restrict__ local,
+    const int32_t* __restrict__ q_pos0, int r, float a_scale, float w_epi, int splits, int list_min,
+    int list_cap, float* __restrict__ scores, int64_t score_stride, uint2* __restrict__ local,
     int2* __restrict__ meta) {
-  __shared__ uint32_t hist_all[4][256];
-  __shared__ float sc_all[4][kDecodeSplit];
-  const int wave = threadIdx.x >> 6;
-  const int lane = threadIdx.x & 63;
+  constexpr int NT = kScanThreads;
+  constexpr int NW = NT / kWave;
+  __shared__ uint32_t hist[256];
+  __shared__ uint32_t bc[2 + 2 * NW];
+  __shared__ float sc[kDecodeSplit];
+  __shared__ uint32_t red[3][NW];
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
   const int half = lane >> 5;
   const int col = lane & 31;
-  const int split = blockIdx.x * 4 + wave;
-  if (split >= splits) return;
+  const int split = blockIdx.x;
   const int b = blockIdx.y;
-  uint32_t* hist = hist_all[wave];
-  float* sc = sc_all[wave];
   const int64_t bt = (int64_t)q_pos0[b] / r;
   const int sbeg = split * kDecodeSplit;
   const int send = (int)min((int64_t)sbeg + kDecodeSplit, bt);
   const int n = max(send - sbeg, 0);
-  uint2* lout = local + ((int64_t)b * splits + split) * kDecodeLocal;
+  uint2* lout = local + ((int64_t)b * splits + split) * list_cap;
   int2* mout = meta + (int64_t)b * splits + split;
   if (n == 0) {
-    if (lane == 0) *mout = make_int2(0, -1);
+    for (int i = tid; i < list_cap; i += NT) lout[i] = make_uint2(0u, 0u);
+    if (tid == 0) *mout = make_int2(0, -1);
     return;
   }
   // A: 32 rows; the query's H_i heads sit at the rows of slot 0 of lane-half 0
@@ -769,78 +804,132 @@ __global__ __launch_bounds__(256) void index_decode_scan_kernel(
   }
   const uint16_t* kb = cmp_k + (int64_t)b * cmp_stride + 8 * half;
   const int last = send - 1;
-  constexpr int PF = 4;  // tiles in flight
-  u32x4 Bq[PF][4];
-#pragma unroll
-  for (int p = 0; p < PF; ++p) {
-    const int j = min(sbeg + 32 * p + col, last);
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) Bq[p][ks] = ld16(kb + (int64_t)j * 64 + 16 * ks);
-  }
   float* srow = scores + (int64_t)b * score_stride;
-  const int ntiles = (n + 31) / 32;
-  for (int tb = 0; tb < ntiles; tb += PF) {
+  const int wbeg = wave * 256;  // this wave's 256 candidates
+  if (wbeg < n) {
+    constexpr int NTILE = 8, PF = 4;  // a ring of 4 tiles in flight
+    u32x4 Bq[PF][4];
+    auto load = [&](int p) {
+      const int j = min(sbeg + wbeg + 32 * p + col, last);
 #pragma unroll
-    for (int p = 0; p < PF; ++p) {
-      const int tile = tb + p;
-      if (tile < ntiles) {
-        f32x16 acc = f32x16{};
+      for (int ks = 0; ks < 4; ++ks) Bq[p % PF][ks] = ld16(kb + (int64_t)j * 64 + 16 * ks);
+    };
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) acc = mfma32x32x16(A[ks], Bq[p][ks], acc);
-        const int nt = tile + PF;
-        if (nt < ntiles) {
-          const int j = min(sbeg + 32 * nt + col, last);
+    for (int p = 0; p < PF; ++p) load(p);
 #pragma unroll
-          for (int ks = 0; ks < 4; ++ks) Bq[p][ks] = ld16(kb + (int64_t)j * 64 + 16 * ks);
-        }
-        float sum = 0.0f;
+    for (int p = 0; p < NTILE; ++p) {
+      f32x16 acc = f32x16{};
 #pragma unroll
-        for (int hd = 0; hd < HI; ++hd) sum += relu_bits(acc[hd]);
-        const float s = sum * w_epi;
-        const int jj = 32 * tile + col;
-        if (half == 0 && jj < n) {
-          sc[jj] = s;
-          srow[sbeg + jj] = s;
-        }
+      for (int ks = 0; ks < 4; ++ks) acc = mfma32x32x16(A[ks], Bq[p % PF][ks], acc);
+      if (p + PF < NTILE) load(p + PF);
+      float sum = 0.0f;
+#pragma unroll
+      for (int hd = 0; hd < HI; ++hd) sum += relu_bits(acc[hd]);
+      const int jj = wbeg + 32 * p + col;
+      if (half == 0 && jj < n) {
+        const float sv = sum * w_epi;
+        sc[jj] = sv;
+        srow[sbeg + jj] = sv;
       }
     }
   }
-  wave_sync();
-  int count = n;
-  int omitted = -1;
-  if (n > kDecodeLocal) {
-    uint32_t tk, ties;
-    int need;
-    wave_select([&](int i) { return __float_as_uint(sc[i]); }, n, kDecodeLocal, hist, tk, need, &ties);
-    wave_stable_keep([&](int i) { return make_uint2(__float_as_uint(sc[i]), (uint32_t)(sbeg + i)); }, n, tk,
-                     need, [&](int pos, uint2 e) { lout[pos] = e; });
-    if (ties > (uint32_t)need) {
-      omitted = (int)tk;
-    } else {
-      int mx = -1;
-      for (int i = lane; i < n; i += kWave) {
-        const uint32_t key = __float_as_uint(sc[i]);
-        if (key < tk) mx = max(mx, (int)key);
-      }
+  // key range of the split
+  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+  __syncthreads();
+  for (int i = tid; i < n; i += NT) {
+    const uint32_t key = __float_as_uint(sc[i]);
+    kmin = min(kmin, key);
+    kmax = max(kmax, key);
+  }
 #pragma unroll
-      for (int off = 32; off > 0; off >>= 1) mx = max(mx, __shfl_xor(mx, off));
-      omitted = mx;
+  for (int off = 32; off > 0; off >>= 1) {
+    kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, off));
+    kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, off));
+  }
+  if (lane == 0) {
+    red[0][wave] = kmin;
+    red[1][wave] = kmax;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    kmin = min(kmin, red[0][w]);
+    kmax = max(kmax, red[1][w]);
+  }
+  uint32_t base = kmin;
+  int hi = range_bits(kmin, kmax);
+  uint32_t need = (uint32_t)min(list_min, n);
+  uint32_t above_all = 0, ge = (uint32_t)n;
+  while (hi > 0 && ge > (uint32_t)list_cap) {
+    const int lo = hi > 8 ? hi - 8 : 0;
+    if (tid < 256) hist[tid] = 0;
+    __syncthreads();
+    for (int i = tid; i < n; i += NT) {
+      const int d = range_digit(__float_as_uint(sc[i]), base, hi, lo);
+      if (d >= 0) atomicAdd(&hist[d], 1u);
     }
-    count = kDecodeLocal;
+    __syncthreads();
+    if (tid < kWave) {
+      int dig;
+      uint32_t above;
+      wave_find_digit(hist, need, dig, above);
+      if (tid == 0) {
+        bc[0] = (uint32_t)dig;
+        bc[1] = above;
+        bc[2] = hist[dig];
+      }
+    }
+    __syncthreads();
+    base += bc[0] << lo;
+    need -= bc[1];
+    above_all += bc[1];
+    ge = above_all + bc[2];
+    hi = lo;
+  }
+  const uint32_t Ls = base;
+  // all entries >= Ls, or (many equal keys) the first slots' worth of them
+  const int take = ge <= (uint32_t)list_cap ? 0x7FFFFFFF : list_cap - (int)above_all;
+  const int kept = block_stable_keep<NT>(
+      [&](int i) { return make_uint2(__float_as_uint(sc[i]), (uint32_t)(sbeg + i)); }, n, Ls, take, bc + 2,
+      [&](int pos, uint2 e) { lout[pos] = make_uint2(e.x + 1u, e.y); });
+  for (int i = kept + tid; i < list_cap; i += NT) lout[i] = make_uint2(0u, 0u);
+  // largest key left out: Ls itself when equal keys were cut, else the
+  // largest key below Ls
+  int below = -1;
+  if (take == 0x7FFFFFFF) {
+    for (int i = tid; i < n; i += NT) {
+      const uint32_t key = __float_as_uint(sc[i]);
+      if (key < Ls) below = max(below, (int)key);
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) below = max(below, __shfl_xor(below, off));
   } else {
-    for (int i = lane; i < n; i += kWave) lout[i] = make_uint2(__float_as_uint(sc[i]), (uint32_t)(sbeg + i));
+    below = (int)Ls;
   }
-  if (lane == 0) *mout = make_int2(count, omitted);
+  if (lane == 0) red[2][wave] = (uint32_t)below;
+  __syncthreads();
+  if (tid == 0) {
+    int b_all = -1;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) b_all = max(b_all, (int)red[2][w]);
+    *mout = make_int2(kept, b_all);
+  }
 }
 
-__global__ __launch_bounds__(256) void index_decode_select_kernel(
+// Merge: one workgroup (1024 threads) per sequence. The split lists are
+// staged slot by slot (block order; empty slots have key 0, the others their
+// key plus one) and the top `keep` of their union is selected exactly. It is
+// the exact top `keep` of all candidates when every key left out of a list is
+// below the selected threshold; otherwise the stored scores of all
+// candidates are selected instead.
+__global__ __launch_bounds__(kMergeThreads) void index_decode_select_kernel(
     const float* __restrict__ scores, int64_t score_stride, const uint2* __restrict__ local,
     const int2* __restrict__ meta, const int32_t* __restrict__ q_pos0, int r, int k, int splits,
-    int32_t* __restrict__ sel, int32_t* __restrict__ sel_cnt) {
+    int list_cap, int32_t* __restrict__ sel, int32_t* __restrict__ sel_cnt) {
+  constexpr int NT = kMergeThreads;
   __shared__ uint32_t hist[256];
-  __shared__ uint32_t bc[2 + 8];
-  __shared__ int s_max;
-  __shared__ int s_off[kDecodeMaxSplits + 1];
+  __shared__ uint32_t bc[2 + 2 * (NT / kWave)];
+  __shared__ int s_max, s_total;
   extern __shared__ uint2 stage[];
   const int tid = threadIdx.x;
   const int b = blockIdx.x;
@@ -848,57 +937,53 @@ __global__ __launch_bounds__(256) void index_decode_select_kernel(
   const int keep = (int)((int64_t)(k - 1) < bt ? (int64_t)(k - 1) : bt);
   int32_t* out = sel + (int64_t)b * k;
   const int used = (int)min((int64_t)splits, (bt + kDecodeSplit - 1) / kDecodeSplit);
-  const uint2* lb = local + (int64_t)b * splits * kDecodeLocal;
+  const uint2* lb = local + (int64_t)b * splits * list_cap;
   const int2* mb = meta + (int64_t)b * splits;
-
-  // union of the split lists, in block order, staged in LDS
   if (tid == 0) {
     s_max = -1;
-    int acc = 0;
-    for (int s = 0; s < used; ++s) {
-      s_off[s] = acc;
-      acc += mb[s].x;
-    }
-    s_off[used] = acc;
+    s_total = 0;
   }
+  const int slots = used * list_cap;
+#pragma unroll 8
+  for (int i = tid; i < slots; i += NT) stage[i] = lb[i];
   __syncthreads();
-  for (int s = tid; s < used; s += 256) atomicMax(&s_max, mb[s].y);
-  const int total = s_off[used];
-  for (int i = tid; i < used * kDecodeLocal; i += 256) {
-    const int s = i / kDecodeLocal, e = i % kDecodeLocal;
-    if (e < s_off[s + 1] - s_off[s]) stage[s_off[s] + e] = lb[i];
+  for (int s2 = tid; s2 < used; s2 += NT) {
+    const int2 m = mb[s2];
+    atomicMax(&s_max, m.y);
+    atomicAdd(&s_total, m.x);
   }
   __syncthreads();
   const int max_omitted = s_max;
+  const int total = s_total;
   if (keep > 0) {
-    uint32_t tk = 0;
+    uint32_t tk = 1u;  // shifted: every listed entry
     int need = 0x7FFFFFFF;
     bool exact;
-    if (total > keep) {
-      block_select<256>([&](int i) { return stage[i].x; }, total, keep, hist, bc, tk, need);
-      exact = max_omitted < 0 || (uint32_t)max_omitted < tk;
+    if (total >= keep) {
+      block_select<NT>([&](int i) { return stage[i].x; }, slots, keep, hist, bc, tk, need);
+      exact = max_omitted < 0 || (uint32_t)max_omitted < tk - 1u;
     } else {
-      exact = max_omitted < 0;  // the union holds every candidate
+      exact = max_omitted < 0;  // the lists hold every candidate
     }
     if (exact) {
-      block_stable_keep<256>([&](int i) { return stage[i]; }, total, tk, need, bc + 2,
-                             [&](int pos, uint2 e) { out[pos] = (int32_t)e.y; });
+      block_stable_keep<NT>([&](int i) { return stage[i]; }, slots, tk, need, bc + 2,
+                            [&](int pos, uint2 e) { out[pos] = (int32_t)e.y; });
     } else {
       // exact selection over the stored scores of every candidate
       const float* srow = scores + (int64_t)b * score_stride;
       const int n = (int)bt;
       tk = 0;
       need = 0x7FFFFFFF;
-      block_select<256>([&](int i) { return __float_as_uint(srow[i]); }, n, keep, hist, bc, tk, need);
-      block_stable_keep<256>([&](int i) { return make_uint2(__float_as_uint(srow[i]), (uint32_t)i); }, n, tk,
-                             need, bc + 2, [&](int pos, uint2 e) { out[pos] = (int32_t)e.y; });
+      block_select<NT>([&](int i) { return __float_as_uint(srow[i]); }, n, keep, hist, bc, tk, need);
+      block_stable_keep<NT>([&](int i) { return make_uint2(__float_as_uint(srow[i]), (uint32_t)i); }, n, tk,
+                            need, bc + 2, [&](int pos, uint2 e) { out[pos] = (int32_t)e.y; });
     }
   }
   if (tid == 0) {
     out[keep] = (int32_t)bt;
     sel_cnt[b] = keep + 1;
   }
-  for (int i = keep + 1 + tid; i < k; i += 256) out[i] = -1;
+  for (int i = keep + 1 + tid; i < k; i += NT) out[i] = -1;
 }
 
 // ----------------------------------------------------------------- planning --
@@ -915,18 +1000,31 @@ IndexPlan plan_index(int hi, int k, int batch, int n_q, int64_t max_q_end, int r
   p.max_cand = max_cand;
   const int keep = k - 1;
   const int64_t dsplits = (max_cand + kDecodeSplit - 1) / kDecodeSplit;
-  if (n_q == 1 && dsplits <= kDecodeMaxSplits) {
+  // list sizes: a split of the full range holds on average mu of the top
+  // `keep`; lists take at least mu + 4 sqrt(mu) + 8 entries (so that the
+  // merge rarely needs the exact fallback) and have half as much room again
+  const double mu = max_cand > 0 ? (double)keep * (double)kDecodeSplit / (double)max_cand : 0.0;
+  int lmin = (int)ceil(mu + 4.0 * sqrt(mu) + 8.0);
+  if (lmin > keep + 8) lmin = keep + 8;
+  lmin = (lmin + 7) / 8 * 8;
+  if (lmin < 16) lmin = 16;
+  if (lmin > 1024) lmin = 1024;
+  const int lcap = (lmin + max(16, lmin / 2) + 7) / 8 * 8;
+  const int64_t nsplit = dsplits < 1 ? 1 : dsplits;
+  if (n_q == 1 && nsplit <= kDecodeMaxSplits && (size_t)nsplit * lcap * sizeof(uint2) <= kMergeMaxLds) {
     p.decode = true;
-    p.splits = dsplits < 1 ? 1 : (int)dsplits;
+    p.splits = (int)nsplit;
+    p.list_min = lmin;
+    p.list_cap = lcap;
     p.score_stride = (max_cand + 63) / 64 * 64;
     const size_t sc = (size_t)batch * p.score_stride * sizeof(float);
-    const size_t lc = (size_t)batch * p.splits * kDecodeLocal * sizeof(uint2);
+    const size_t lc = (size_t)batch * p.splits * p.list_cap * sizeof(uint2);
     const size_t mc = (size_t)batch * p.splits * sizeof(int2);
     p.buf_bytes = (sc + 255) / 256 * 256;
     p.local_off = p.buf_bytes;
     p.meta_off = p.local_off + (lc + 255) / 256 * 256;
     p.workspace = p.meta_off + (mc + 255) / 256 * 256;
-    p.select_lds = (size_t)p.splits * kDecodeLocal * sizeof(uint2);
+    p.select_lds = (size_t)p.splits * p.list_cap * sizeof(uint2);
     return p;
   }
   p.decode = false;
@@ -983,11 +1081,11 @@ hipError_t launch_index_topk(const IndexPlan& p, const uint16_t* idx_q, const ui
     float* scores = reinterpret_cast<float*>(wsb);
     uint2* local = reinterpret_cast<uint2*>(wsb + p.local_off);
     int2* meta = reinterpret_cast<int2*>(wsb + p.meta_off);
-    const dim3 g1((p.splits + 3) / 4, batch);
+    const dim3 g1(p.splits, batch);
 #define QSA_LAUNCH_DSCAN(HI_)                                                                      \
-  hipLaunchKernelGGL(index_decode_scan_kernel<HI_>, g1, dim3(256), 0, stream, idx_q, cmp_k,       \
-                     cmp_stride, q_pos0, r, a_scale, w_epi, p.splits, scores, p.score_stride, local, \
-                     meta)
+  hipLaunchKernelGGL(index_decode_scan_kernel<HI_>, g1, dim3(kScanThreads), 0, stream, idx_q,    \
+                     cmp_k, cmp_stride, q_pos0, r, a_scale, w_epi, p.splits, p.list_min, p.list_cap,  \
+                     scores, p.score_stride, local, meta)
     switch (p.hi) {
       case 1: QSA_LAUNCH_DSCAN(1); break;
       case 2: QSA_LAUNCH_DSCAN(2); break;
@@ -999,8 +1097,8 @@ hipError_t launch_index_topk(const IndexPlan& p, const uint16_t* idx_q, const ui
 #undef QSA_LAUNCH_DSCAN
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(index_decode_select_kernel, dim3(batch), dim3(256), p.select_lds, stream, scores,
-                       p.score_stride, local, meta, q_pos0, r, k, p.splits, sel, sel_cnt);
+    hipLaunchKernelGGL(index_decode_select_kernel, dim3(batch), dim3(kMergeThreads), p.select_lds, stream,
+                       scores, p.score_stride, local, meta, q_pos0, r, k, p.splits, p.list_cap, sel, sel_cnt);
     return hipGetLastError();
   }
   uint2* buf = reinterpret_cast<uint2*>(wsb);

@@ -24,6 +24,7 @@ struct IndexPlan {
   int cap;         // buffer entries per (query, split)
   int64_t max_cand;
   int64_t score_stride;             // decode: floats per sequence in the score array
+  int list_min, list_cap;           // decode: entries per split list (at least / room)
   size_t local_off, meta_off;       // decode: workspace offsets
   size_t buf_bytes, cnt_bytes, workspace;
   size_t stream_lds, select_lds;    // dynamic LDS bytes of the two kernels

@@ -3,8 +3,13 @@
 // Keys are uint32: the bit patterns of non-negative fp32 scores, which order
 // like the scores. "Select" finds tk, the keep-th largest key, and `need`, how
 // many entries equal to tk belong to the top `keep` (the first ones in list
-// order). Four most-significant-digit-first passes of 8 bits with a 256-bin LDS
-// histogram. "Stable keep" then emits, in list order, every entry with key > tk
+// order). Radix select on the offset key - kmin, where kmin and kmax are the
+// smallest and largest key: the offsets' leading zero bits are skipped, and
+// the rest are resolved most-significant first, 8 per pass, with a 256-bin LDS
+// histogram, so even the first pass spreads the keys over the bins (fp32
+// keys of similar magnitude share their top bits, and keys on both sides of
+// a power of two differ in bit 30, so a plain bit prefix would not). "Stable
+// keep" then emits, in list order, every entry with key > tk
 // and the first `need` entries with key == tk; lists are kept in increasing
 // block index, so this realises the (score desc, index asc) order exactly.
 #pragma once
@@ -57,32 +62,59 @@ __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_wave_barrier();
 }
 
+// Width in bits of the offset range [0, kmax - kmin].
+__device__ __forceinline__ int range_bits(uint32_t kmin, uint32_t kmax) {
+  return kmax == kmin ? 0 : 32 - __builtin_clz(kmax - kmin);
+}
+
+// Histogram digit of key k for the range [base, base + 2^w), digit bits
+// [lo, w) of the offset; -1 when k is outside the range. Keys are below 2^31
+// (non-negative fp32 bit patterns), so a key below base wraps to an offset of
+// at least 2^31, out of every range.
+__device__ __forceinline__ int range_digit(uint32_t k, uint32_t base, int w, int lo) {
+  const uint32_t d = (k - base) >> lo;  // wraps to a large value below base
+  return d < (1u << (w - lo)) ? (int)d : -1;
+}
+
 // Wave-level select over n keys given by key(i) (cheap to read, e.g. LDS).
 template <typename KeyFn, typename HistPtr>
 __device__ void wave_select(KeyFn key, int n, int keep, HistPtr hist, uint32_t& tk, int& need_out,
                             uint32_t* ties_out = nullptr) {
   const int lane = lane_id();
-  uint32_t prefix = 0, mask = 0;
+  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+  for (int i = lane; i < n; i += kWave) {
+    const uint32_t k = key(i);
+    kmin = min(kmin, k);
+    kmax = max(kmax, k);
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, off));
+    kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, off));
+  }
+  uint32_t base = kmin;
+  int w = range_bits(kmin, kmax);
   uint32_t need = (uint32_t)keep;
-  uint32_t ties = 0;
-  for (int shift = 24; shift >= 0; shift -= 8) {
+  uint32_t ties = (uint32_t)n;  // every key equals kmin when the range is empty
+  while (w > 0) {
+    const int lo = w > 8 ? w - 8 : 0;
     for (int i = lane; i < 256; i += kWave) hist[i] = 0;
     wave_sync();
     for (int i = lane; i < n; i += kWave) {
-      const uint32_t k = key(i);
-      if ((k & mask) == prefix) __atomic_fetch_add(&hist[(k >> shift) & 255u], 1u, __ATOMIC_RELAXED);
+      const int d = range_digit(key(i), base, w, lo);
+      if (d >= 0) __atomic_fetch_add(&hist[d], 1u, __ATOMIC_RELAXED);
     }
     wave_sync();
     int dig;
     uint32_t above;
     wave_find_digit(hist, need, dig, above);
-    if (shift == 0) ties = hist[dig];
-    prefix |= (uint32_t)dig << shift;
-    mask |= 255u << shift;
+    if (lo == 0) ties = hist[dig];
+    base += (uint32_t)dig << lo;
     need -= above;
+    w = lo;
     wave_sync();
   }
-  tk = prefix;
+  tk = base;
   need_out = (int)need;
   if (ties_out) *ties_out = ties;
 }
@@ -113,15 +145,41 @@ __device__ int wave_stable_keep(GetFn get, int n, uint32_t tk, int need, EmitFn 
 template <int NT, typename KeyFn>
 __device__ void block_select(KeyFn key, int n, int keep, uint32_t* hist, uint32_t* bc, uint32_t& tk,
                              int& need_out) {
+  constexpr int NW = NT / kWave;
   const int tid = threadIdx.x;
-  uint32_t prefix = 0, mask = 0;
+  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+  for (int i = tid; i < n; i += NT) {
+    const uint32_t k = key(i);
+    kmin = min(kmin, k);
+    kmax = max(kmax, k);
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, off));
+    kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, off));
+  }
+  __syncthreads();  // hist may still be read by a previous call
+  if (lane_id() == 0) {
+    hist[tid / kWave] = kmin;
+    hist[NW + tid / kWave] = kmax;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    kmin = min(kmin, hist[w]);
+    kmax = max(kmax, hist[NW + w]);
+  }
+  uint32_t base = kmin;
+  int w = range_bits(kmin, kmax);
   uint32_t need = (uint32_t)keep;
-  for (int shift = 24; shift >= 0; shift -= 8) {
+  while (w > 0) {
+    const int lo = w > 8 ? w - 8 : 0;
+    __syncthreads();
     for (int i = tid; i < 256; i += NT) hist[i] = 0;
     __syncthreads();
     for (int i = tid; i < n; i += NT) {
-      const uint32_t k = key(i);
-      if ((k & mask) == prefix) atomicAdd(&hist[(k >> shift) & 255u], 1u);
+      const int d = range_digit(key(i), base, w, lo);
+      if (d >= 0) atomicAdd(&hist[d], 1u);
     }
     __syncthreads();
     if (tid < kWave) {
@@ -134,12 +192,12 @@ __device__ void block_select(KeyFn key, int n, int keep, uint32_t* hist, uint32_
       }
     }
     __syncthreads();
-    prefix |= bc[0] << shift;
-    mask |= 255u << shift;
+    base += bc[0] << lo;
     need -= bc[1];
-    __syncthreads();
+    w = lo;
   }
-  tk = prefix;
+  __syncthreads();
+  tk = base;
   need_out = (int)need;
 }
 
