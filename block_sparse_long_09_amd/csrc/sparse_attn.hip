@@ -348,7 +348,9 @@ AttnPlan plan_attn(int batch_rows, int64_t max_tokens, bool split_kv) {
   p.rows = batch_rows;
   int64_t splits = 1;
   if (split_kv) {
-    splits = (1024 + batch_rows - 1) / batch_rows;
+    // about 256 workgroups: enough to spread the gathers over the chip while
+    // keeping the partial (m, l, O) traffic of the merge small
+    splits = (256 + batch_rows - 1) / batch_rows;
     if (splits > kMaxMergeSplits) splits = kMaxMergeSplits;
     const int64_t max_splits = (max_tokens + kChunk - 1) / kChunk;
     if (splits > max_splits) splits = max_splits;
