@@ -183,3 +183,47 @@ def test_decode_many_splits_normal_inputs_match(qsa):
         o_sel, o_cnt, band, _ = oracle.select(iq[b][None], blocks, t, r, k, 1.0 / Hi)
         check_selection(g_sel[b:b + 1], g_cnt[b:b + 1], o_sel, o_cnt, band,
                         lambda _: oracle.scores(iq[b], blocks[: t // r], 1.0 / Hi))
+
+
+def _bf16_bits(x):
+    """float32 array -> bf16 bit patterns (round to nearest even)."""
+    u = np.ascontiguousarray(x, np.float32).view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return u.astype(np.uint16)
+
+
+def _bf16_float(bits):
+    return (bits.astype(np.uint32) << 16).view(np.float32)
+
+
+@pytest.mark.parametrize("k", [16, 512, 1024])
+def test_decode_clustered_selection(qsa, k):
+    # sequence 0 has a run of 1200 blocks whose keys lean towards the query, so
+    # the whole top-k falls into one or two splits, overflows their lists and
+    # the merge must fall back to the stored scores; sequence 1 is plain
+    from block_sparse_long_09_amd.pipeline import DecodePath
+    B, L, Hq, Hkv, Hi, r = 2, 300003, 32, 4, 8, 4
+    _say("decode clustered", k)
+    kv_len = np.array([300003, 299999], np.int32)
+    iq = gen.normal(51, 4, (B, Hi, 64))
+    ik = np.stack([gen.normal(51 + b, 5, (L, 64)) for b in range(B)])
+    lean = _bf16_float(iq[0]).mean(axis=0)  # mean query direction of sequence 0
+    c0 = 100000
+    ik[0, c0:c0 + 4800] = _bf16_bits(_bf16_float(ik[0, c0:c0 + 4800]) + 1.5 * lean[None, :])
+    cmp = torch.empty((B, L // r, 64), dtype=torch.bfloat16, device="cuda")
+    qsa.qsa_compress_keys(dev(ik), cmp, r, 0, L // r)
+    path = DecodePath(Hq, Hkv, Hi, B, L, r=r, k=k)
+    kvl = torch.from_numpy(kv_len).cuda()
+    path.select(dev(iq), cmp, kvl - 1)
+    torch.cuda.synchronize()
+    g_sel = path.sel[:, 0].cpu().numpy()
+    g_cnt = path.cnt[:, 0].cpu().numpy()
+    for b in range(B):
+        t = int(kv_len[b]) - 1
+        blocks = oracle.compress(ik[b], r)
+        o_sel, o_cnt, band, _ = oracle.select(iq[b][None], blocks, t, r, k, 1.0 / Hi)
+        if b == 0:  # the cluster really holds the selection
+            inside = np.count_nonzero((o_sel[0] >= c0 // r) & (o_sel[0] < (c0 + 4800) // r))
+            assert inside >= min(k - 1, 1200) * 0.9, inside
+        check_selection(g_sel[b:b + 1], g_cnt[b:b + 1], o_sel, o_cnt, band,
+                        lambda _: oracle.scores(iq[b], blocks[: t // r], 1.0 / Hi))
