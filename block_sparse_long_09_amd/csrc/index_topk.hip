@@ -47,8 +47,9 @@ namespace {
 constexpr int kScanThreads = 512;              // decode split scan: 256 candidates per wave
 constexpr int kDecodeSplit = kScanThreads * 4;  // candidates per decode split
 constexpr int kMergeThreads = 1024;             // decode merge
+constexpr int kSelScratch = 1024;               // keys a workgroup select gathers for its last passes
 constexpr int kDecodeMaxSplits = 1024;  // decode splits per sequence
-constexpr size_t kMergeMaxLds = 144 * 1024;  // merge LDS for the staged split lists
+constexpr size_t kMergeMaxLds = 140 * 1024;  // merge LDS for the staged split lists
 
 __device__ __forceinline__ float relu_bits(float x) {
   // max on the integer view: negative values and -0.0 become +0.0
@@ -700,6 +701,7 @@ __global__ __launch_bounds__(256) void index_select_kernel(
     int32_t* __restrict__ sel_cnt) {
   __shared__ uint32_t hist[256];
   __shared__ uint32_t bc[2 + 8];
+  __shared__ uint32_t scratch[kSelScratch];
   __shared__ int seg_off[9];
   extern __shared__ uint2 stage[];
   const int tid = threadIdx.x;
@@ -733,7 +735,8 @@ __global__ __launch_bounds__(256) void index_select_kernel(
   if (keep > 0) {
     uint32_t tk = 0;
     int need = 0x7FFFFFFF;
-    if (total > keep) block_select<256>([&](int i) { return stage[i].x; }, total, keep, hist, bc, tk, need);
+    if (total > keep)
+      block_select<256>([&](int i) { return stage[i].x; }, total, keep, hist, bc, scratch, kSelScratch, tk, need);
     block_stable_keep<256>([&](int i) { return stage[i]; }, total, tk, need, bc + 2,
                            [&](int pos, uint2 e) { out[pos] = (int32_t)e.y; });
   }
@@ -929,6 +932,7 @@ __global__ __launch_bounds__(kMergeThreads) void index_decode_select_kernel(
   constexpr int NT = kMergeThreads;
   __shared__ uint32_t hist[256];
   __shared__ uint32_t bc[2 + 2 * (NT / kWave)];
+  __shared__ uint32_t scratch[kSelScratch];
   __shared__ int s_max, s_total;
   extern __shared__ uint2 stage[];
   const int tid = threadIdx.x;
@@ -960,7 +964,8 @@ __global__ __launch_bounds__(kMergeThreads) void index_decode_select_kernel(
     int need = 0x7FFFFFFF;
     bool exact;
     if (total >= keep) {
-      block_select<NT>([&](int i) { return stage[i].x; }, slots, keep, hist, bc, tk, need);
+      block_select<NT, true>([&](int i) { return stage[i].x; }, slots, keep, hist, bc, scratch, kSelScratch, tk,
+                             need);
       exact = max_omitted < 0 || (uint32_t)max_omitted < tk - 1u;
     } else {
       exact = max_omitted < 0;  // the lists hold every candidate
@@ -974,7 +979,8 @@ __global__ __launch_bounds__(kMergeThreads) void index_decode_select_kernel(
       const int n = (int)bt;
       tk = 0;
       need = 0x7FFFFFFF;
-      block_select<NT>([&](int i) { return __float_as_uint(srow[i]); }, n, keep, hist, bc, tk, need);
+      block_select<NT>([&](int i) { return __float_as_uint(srow[i]); }, n, keep, hist, bc, scratch, kSelScratch,
+                       tk, need);
       block_stable_keep<NT>([&](int i) { return make_uint2(__float_as_uint(srow[i]), (uint32_t)i); }, n, tk,
                             need, bc + 2, [&](int pos, uint2 e) { out[pos] = (int32_t)e.y; });
     }

@@ -141,16 +141,22 @@ __device__ int wave_stable_keep(GetFn get, int n, uint32_t tk, int need, EmitFn 
   return kept;
 }
 
-// Workgroup-level (NT threads) select; hist: 256 bins, bc: 2 words, both LDS.
-template <int NT, typename KeyFn>
-__device__ void block_select(KeyFn key, int n, int keep, uint32_t* hist, uint32_t* bc, uint32_t& tk,
-                             int& need_out) {
+// Workgroup-level (NT threads) select. LDS: hist 256 bins, bc 3 words,
+// scratch `scratch_cap` keys. One radix pass over all n keys finds the bucket
+// of the keep-th largest; when the bucket holds at most scratch_cap keys they
+// are gathered into scratch and the first wave finishes the selection alone
+// (a few short passes, no workgroup barriers); otherwise workgroup passes
+// continue. SKIP_ZERO leaves keys equal to 0 out of the key range (they mark
+// empty slots and must never be the keep-th largest).
+template <int NT, bool SKIP_ZERO = false, typename KeyFn>
+__device__ void block_select(KeyFn key, int n, int keep, uint32_t* hist, uint32_t* bc, uint32_t* scratch,
+                             int scratch_cap, uint32_t& tk, int& need_out) {
   constexpr int NW = NT / kWave;
   const int tid = threadIdx.x;
   uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
   for (int i = tid; i < n; i += NT) {
     const uint32_t k = key(i);
-    kmin = min(kmin, k);
+    if (!SKIP_ZERO || k != 0u) kmin = min(kmin, k);
     kmax = max(kmax, k);
   }
 #pragma unroll
@@ -169,6 +175,7 @@ __device__ void block_select(KeyFn key, int n, int keep, uint32_t* hist, uint32_
     kmin = min(kmin, hist[w]);
     kmax = max(kmax, hist[NW + w]);
   }
+  if (kmin > kmax) kmin = kmax;  // every key skipped
   uint32_t base = kmin;
   int w = range_bits(kmin, kmax);
   uint32_t need = (uint32_t)keep;
@@ -189,57 +196,96 @@ __device__ void block_select(KeyFn key, int n, int keep, uint32_t* hist, uint32_
       if (tid == 0) {
         bc[0] = (uint32_t)dig;
         bc[1] = above;
+        bc[2] = hist[dig];
       }
     }
     __syncthreads();
     base += bc[0] << lo;
     need -= bc[1];
     w = lo;
+    const uint32_t in_bucket = bc[2];
+    if (w > 0 && in_bucket <= (uint32_t)scratch_cap) {
+      // gather the bucket [base, base + 2^w) and finish in one wave
+      __syncthreads();
+      if (tid == 0) bc[2] = 0;
+      __syncthreads();
+      for (int i = tid; i < n; i += NT) {
+        const uint32_t k = key(i);
+        if (range_digit(k, base, w, 0) >= 0) scratch[atomicAdd(&bc[2], 1u)] = k;
+      }
+      __syncthreads();
+      if (tid < kWave) {
+        uint32_t t2;
+        int n2;
+        wave_select([&](int i) { return scratch[i]; }, (int)in_bucket, (int)need, hist, t2, n2);
+        if (tid == 0) {
+          bc[0] = t2;
+          bc[1] = (uint32_t)n2;
+        }
+      }
+      __syncthreads();
+      base = bc[0];
+      need = bc[1];
+      w = 0;
+    }
   }
   __syncthreads();
   tk = base;
   need_out = (int)need;
 }
 
-// Workgroup-level stable keep; cnt: 2 * (NT / 64) words of LDS.
+// Workgroup-level stable keep: thread t handles the consecutive entries
+// [t * ipt, (t + 1) * ipt); one exclusive scan of its (> tk, == tk) counts
+// gives every thread its output position. cnt: 2 * (NT / 64) words of LDS.
 template <int NT, typename GetFn, typename EmitFn>
 __device__ int block_stable_keep(GetFn get, int n, uint32_t tk, int need, uint32_t* cnt, EmitFn emit) {
   constexpr int NW = NT / kWave;
   const int tid = threadIdx.x;
+  const int lane = lane_id();
   const int w = tid / kWave;
-  int kept = 0, ties = 0;
-  for (int base = 0; base < n; base += NT) {
-    const int i = base + tid;
-    const bool in = i < n;
-    const uint2 e = in ? get(i) : make_uint2(0u, 0u);
-    const bool gt = in && e.x > tk;
-    const bool eq = in && e.x == tk;
-    const uint64_t me = ballot(eq);
-    if (lane_id() == 0) cnt[w] = (uint32_t)__popcll(me);
-    __syncthreads();
-    int eq_before = 0, eq_all = 0;
-#pragma unroll
-    for (int v = 0; v < NW; ++v) {
-      eq_before += v < w ? (int)cnt[v] : 0;
-      eq_all += (int)cnt[v];
-    }
-    const int tie_rank = ties + eq_before + __popcll(lanes_below(me));
-    const bool keep = gt || (eq && tie_rank < need);
-    const uint64_t mk = ballot(keep);
-    if (lane_id() == 0) cnt[NW + w] = (uint32_t)__popcll(mk);
-    __syncthreads();
-    int k_before = 0, k_all = 0;
-#pragma unroll
-    for (int v = 0; v < NW; ++v) {
-      k_before += v < w ? (int)cnt[NW + v] : 0;
-      k_all += (int)cnt[NW + v];
-    }
-    if (keep) emit(kept + k_before + __popcll(lanes_below(mk)), e);
-    kept += k_all;
-    ties += eq_all;
-    __syncthreads();
+  const int ipt = (n + NT - 1) / NT;
+  const int i0 = min(tid * ipt, n), i1 = min(i0 + ipt, n);
+  int gt = 0, eq = 0;
+  for (int i = i0; i < i1; ++i) {
+    const uint32_t k = get(i).x;
+    gt += k > tk;
+    eq += k == tk;
   }
-  return kept;
+  int gi = gt, ei = eq;  // inclusive scans within the wave
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int g2 = __shfl_up(gi, off), e2 = __shfl_up(ei, off);
+    if (lane >= off) {
+      gi += g2;
+      ei += e2;
+    }
+  }
+  __syncthreads();  // cnt may still be read by a previous call
+  if (lane == kWave - 1) {
+    cnt[w] = (uint32_t)gi;
+    cnt[NW + w] = (uint32_t)ei;
+  }
+  __syncthreads();
+  int g_before = gi - gt, e_before = ei - eq, g_all = 0, e_all = 0;
+#pragma unroll
+  for (int v = 0; v < NW; ++v) {
+    const int gv = (int)cnt[v], ev = (int)cnt[NW + v];
+    if (v < w) {
+      g_before += gv;
+      e_before += ev;
+    }
+    g_all += gv;
+    e_all += ev;
+  }
+  int pos = g_before + min(e_before, need);
+  int er = e_before;
+  for (int i = i0; i < i1; ++i) {
+    const uint2 e = get(i);
+    const bool is_eq = e.x == tk;
+    if (e.x > tk || (is_eq && er < need)) emit(pos++, e);
+    er += is_eq;
+  }
+  return g_all + min(e_all, need);
 }
 
 }  // namespace qsa
