@@ -13,10 +13,15 @@
 //                 cross-half exchange;
 //   O  += P V     (32 rows x 128 dims): P leaves the S^T accumulators already in
 //                 A-operand layout (the chunk's token order is permuted
-//                 consistently for P and for V); V fragments are read from LDS
-//                 2 bytes per lane.
-// Online softmax in fp32 with base-2 exponents; the per-row rescale factor is
-// passed from the S^T layout to the O layout through LDS.
+//                 consistently for P and for V); the V operand is read from the
+//                 row-major LDS tile with ds_read_b64_tr_b16, which hands each
+//                 lane 4 consecutive tokens of one dimension (two reads per
+//                 MFMA).
+// Online softmax in fp32 with base-2 exponents and a lazy rescale: a row's
+// reference maximum moves (and its O and l are rescaled) only when a chunk's
+// maximum exceeds it by more than 2^8, so P stays below 256 and most chunks
+// skip the rescale; the per-row factor goes from the S^T layout to the O
+// layout through LDS.
 #include "qsa_device.h"
 #include "qsa_internal.h"
 
@@ -26,7 +31,17 @@ namespace {
 constexpr int kFD = 128;           // head dim
 constexpr int kFTile = 64;         // tokens per LDS tile
 constexpr int kFRows = 128;        // query rows per workgroup
-constexpr int kKPitch = 128 + 8;   // LDS row pitch (elements) of K and V tiles
+constexpr int kKPitch = 128 + 16;  // LDS row pitch (elements): 288 B, conflict-free for both read forms
+constexpr float kLazy = 8.0f;      // log2 headroom before a row's reference maximum moves
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+
+// 4 consecutive tokens of one dimension per lane (see the header comment).
+__device__ __forceinline__ uint2 ld_tr16(const uint16_t* p) {
+  const v4i16 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)p);
+  return __builtin_bit_cast(uint2, v);
+}
 }  // namespace
 
 __global__ __launch_bounds__(256, 2) void dense_prefill_kernel(
@@ -85,8 +100,13 @@ __global__ __launch_bounds__(256, 2) void dense_prefill_kernel(
       *reinterpret_cast<u32x4*>(&vt[buf][row * kKPitch + part * 8]) = RV[u];
     }
   };
+  // transposed V reads: lane group gr = lane / 16 covers dims +16 (gr % 2) of
+  // an n-tile and token half gr / 2; within the group, source lane 4j + qd
+  // addresses token j, dims 4qd .. 4qd+3
+  const int gr = lane >> 4, sl = lane & 15;
+  const int tr_off = ((gr >> 1) * 4 + (sl >> 2)) * kKPitch + 16 * (gr & 1) + 4 * (sl & 3);
 
-  float m_run = -INFINITY;  // this lane's row: running max (log2 units)
+  float m_run = -INFINITY;  // this lane's row: reference maximum (log2 units)
   float l_run = 0.0f;       // this lane's share of the row sum
   f32x16 O[4];
 #pragma unroll
@@ -118,65 +138,65 @@ __global__ __launch_bounds__(256, 2) void dense_prefill_kernel(
         S = mfma32x32x16(a, Qf[ks], S);
       }
       // this lane: row `col`, tokens c0 + 8(i/4) + 4half + i%4
-      const bool need_mask = c0 + 31 > wave_tmin;
-      float x[16];
-      float cmax = -INFINITY;
+      if (c0 + 31 > wave_tmin) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int64_t s = c0 + 8 * (i >> 2) + 4 * half + (i & 3);
-        float xv = S[i] * scale_log2;
-        if (need_mask && s > my_t) xv = -INFINITY;
-        x[i] = xv;
-        cmax = fmaxf(cmax, xv);
+        for (int i = 0; i < 16; ++i) {
+          const int64_t s = c0 + 8 * (i >> 2) + 4 * half + (i & 3);
+          if (s > my_t) S[i] = -INFINITY;
+        }
       }
-      cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
-      const float m_new = fmaxf(m_run, cmax);
-      const float m_use = m_new == -INFINITY ? 0.0f : m_new;
-      const float alpha = exp2f(m_run - m_use);
-      m_run = m_new;
+      float cmax = S[0];
+#pragma unroll
+      for (int i = 1; i < 16; ++i) cmax = fmaxf(cmax, S[i]);
+      cmax = fmaxf(cmax, __shfl_xor(cmax, 32)) * scale_log2;
+      const bool up = cmax > m_run + kLazy;
+      if (ballot(up)) {
+        const float m_new = up ? cmax : m_run;
+        const float alpha = up ? exp2f(m_run - m_new) : 1.0f;
+        m_run = m_new;
+        l_run *= alpha;
+        // alpha of row `col` -> O layout (rows 8(i/4) + 4half + i%4)
+        if (half == 0) alpha_x[wave][col] = alpha;
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float a = alpha_x[wave][8 * (i >> 2) + 4 * half + (i & 3)];
+#pragma unroll
+          for (int nt = 0; nt < 4; ++nt) O[nt][i] *= a;
+        }
+        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+      }
       float psum = 0.0f;
       uint32_t pk[8];
 #pragma unroll
       for (int i = 0; i < 16; i += 2) {
-        const float p0 = exp2f(x[i] - m_use), p1 = exp2f(x[i + 1] - m_use);
+        const float p0 = fast_exp2(fmaf(S[i], scale_log2, -m_run));
+        const float p1 = fast_exp2(fmaf(S[i + 1], scale_log2, -m_run));
         psum += p0 + p1;
-        pk[i >> 1] = pack_bf16x2(p0, p1);
+        pk[i >> 1] = pack_bf16x2_hw(p0, p1);
       }
-      l_run = l_run * alpha + psum;
-      // alpha of row `col` -> O layout (rows 8(i/4) + 4half + i%4)
-      if (half == 0) alpha_x[wave][col] = alpha;
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float a = alpha_x[wave][8 * (i >> 2) + 4 * half + (i & 3)];
-#pragma unroll
-        for (int nt = 0; nt < 4; ++nt) O[nt][i] *= a;
-      }
-      // O += P V: k-step kk uses this lane's tokens i in [8kk, 8kk+8)
+      l_run += psum;
+      // O += P V: k-step kk holds this lane's tokens i in [8kk, 8kk + 8), i.e.
+      // chunk tokens 16kk + 4half + {0..3} and 16kk + 8 + 4half + {0..3}
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
         const u32x4 Pa = u32x4{pk[4 * kk], pk[4 * kk + 1], pk[4 * kk + 2], pk[4 * kk + 3]};
+        const uint16_t* vrow = &vt[buf][(32 * ch + 16 * kk) * kKPitch + tr_off];
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt) {
-          const int d = 32 * nt + col;
-          uint32_t w[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            // k positions 8half + 2e, 2e+1 of this k-step <-> tokens (i = 8kk + 2e, 2e+1) of lane-half `half`
-            const int i0 = 8 * kk + 2 * e, i1 = i0 + 1;
-            const int r0 = 32 * ch + 8 * (i0 >> 2) + 4 * half + (i0 & 3);
-            const int r1 = 32 * ch + 8 * (i1 >> 2) + 4 * half + (i1 & 3);
-            w[e] = (uint32_t)vt[buf][r0 * kKPitch + d] | ((uint32_t)vt[buf][r1 * kKPitch + d] << 16);
-          }
-          O[nt] = mfma32x32x16(Pa, u32x4{w[0], w[1], w[2], w[3]}, O[nt]);
+          const uint2 lo = ld_tr16(vrow + 32 * nt);
+          const uint2 hi = ld_tr16(vrow + 8 * kKPitch + 32 * nt);
+          O[nt] = mfma32x32x16(Pa, u32x4{lo.x, lo.y, hi.x, hi.y}, O[nt]);
         }
       }
-      __builtin_amdgcn_wave_barrier();
     }
   }
   // finish: row sums over both halves, then O / l in bf16, lse in natural log
   float l_row = l_run + __shfl_xor(l_run, 32);
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+  __builtin_amdgcn_wave_barrier();
   if (half == 0) alpha_x[wave][col] = 1.0f / l_row;
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();

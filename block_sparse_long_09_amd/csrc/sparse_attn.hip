@@ -183,7 +183,7 @@ __global__ __launch_bounds__(256) void attn_gather_kernel(
     float p[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      p[e] = exp2f(x[e] - m_use);
+      p[e] = fast_exp2(x[e] - m_use);
       psum += p[e];
     }
     l_run = l_run * alpha + psum;
