@@ -129,6 +129,10 @@ def main():
     ap.add_argument("--cpu-sample", type=int, default=256, help="queries in the oracle's timed sample")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="also run one plain device copy of this size (counter calibration runs)")
+    ap.add_argument("--block-size", type=int, default=0,
+                    help="micro-block size r of a variant run (default: the workload's, 4)")
+    ap.add_argument("--budget", type=int, default=0,
+                    help="token budget k*r of a variant run (default: the workload's, 2048)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU; --gpus {args.gpus} is not supported "
@@ -150,6 +154,20 @@ def main():
         Wp, Wd = CONFIGS["c3"], None
     else:
         Wp, Wd = None, CONFIGS["c4"]
+    if args.block_size or args.budget:
+        import dataclasses
+        base = Wp or Wd
+        r = args.block_size or base.r
+        budget = args.budget or base.k * base.r
+        if r not in (1, 2, 4, 8, 16, 32) or budget % r or not 1 <= budget // r <= 1024:
+            print(f"bench.py: need r in {{1, 2, 4, 8, 16, 32}} and budget a multiple of r with "
+                  f"1 <= budget / r <= 1024 (r = {r}, budget = {budget})",
+                  file=sys.stderr)
+            sys.exit(2)
+
+        def variant(W):
+            return dataclasses.replace(W, name=f"{W.name}_r{r}_budget{budget}", r=r, k=budget // r) if W else None
+        Wp, Wd = variant(Wp), variant(Wd)
 
     t_setup = time.time()
     # ------------------------------------------------------------- inputs --
