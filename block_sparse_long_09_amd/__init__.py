@@ -55,6 +55,11 @@ _sig("qsa_sparse_attn_decode", ctypes.c_int,
 _sig("qsa_dense_attn_workspace_size", _sz, [_PA, _i32, _i32, _i64])
 _sig("qsa_dense_attn_prefill", ctypes.c_int, [_PA, _vp, _vp, _vp, _i64, _i32, _i64, _vp, _vp, _vp, _sz, _vp])
 _sig("qsa_dense_attn_decode", ctypes.c_int, [_PA, _vp, _vp, _vp, _i64, _vp, _i32, _vp, _vp, _vp, _sz, _vp])
+_sig("qsa_index_topk_varlen_workspace_size", _sz, [_PI, _i32, _i32, _i64])
+_sig("qsa_index_topk_varlen", ctypes.c_int,
+     [_PI, _vp, _vp, _i64, _vp, _vp, _i32, _i32, _i64, _vp, _vp, _vp, _sz, _vp])
+_sig("qsa_sparse_attn_prefill_paged", ctypes.c_int,
+     [_PA, _i32, _i32, _vp, _vp, _vp, _i32, _i64, _vp, _i32, _vp, _vp, _i32, _i32, _vp, _vp, _vp, _vp, _vp])
 _sig("qsa_status_string", ctypes.c_char_p, [ctypes.c_int])
 _sig("qsa_last_error_message", ctypes.c_char_p, [])
 _sig("qsa_abi_version", ctypes.c_int, [])
@@ -65,6 +70,7 @@ EXPORTS = (
     "qsa_sparse_attn_workspace_size", "qsa_sparse_attn_prefill", "qsa_sparse_attn_decode",
     "qsa_status_string", "qsa_last_error_message", "qsa_abi_version",
     "qsa_dense_attn_workspace_size", "qsa_dense_attn_prefill", "qsa_dense_attn_decode",
+    "qsa_index_topk_varlen_workspace_size", "qsa_index_topk_varlen", "qsa_sparse_attn_prefill_paged",
 )
 
 
@@ -151,6 +157,40 @@ def qsa_index_topk(desc, idx_q, cmp_k, q_pos0, max_q_end, sel_blocks, sel_count,
     _check(_lib.qsa_index_topk(ctypes.byref(desc), _bf16(idx_q, "idx_q"), _bf16(cmp_k, "cmp_k"), cmp_k.stride(0),
                                _i32t(q_pos0, "q_pos0"), max_q_end, B, n_q, _i32t(sel_blocks, "sel_blocks"),
                                _i32t(sel_count, "sel_count"), ws, nbytes, _stream(stream)))
+
+
+def qsa_index_topk_varlen_workspace_size(desc, batch, max_q, max_q_end):
+    return _lib.qsa_index_topk_varlen_workspace_size(ctypes.byref(desc), batch, max_q, max_q_end)
+
+
+def qsa_index_topk_varlen(desc, idx_q, cmp_k, cu_q, q_pos0, max_q, max_q_end, sel_blocks, sel_count, workspace,
+                          stream=None):
+    """Packed rows: idx_q [total_q, H_i, 64]; cmp_k [B, N, 64]; cu_q int32 [B + 1] and q_pos0
+    int32 [B] (device); sel_blocks int32 [total_q, k]; sel_count int32 [total_q]."""
+    if cmp_k.dim() == 2:
+        cmp_k = cmp_k[None]
+    B = q_pos0.shape[0]
+    ws = _ptr(workspace) if workspace is not None and workspace.numel() else None
+    nbytes = workspace.numel() * workspace.element_size() if ws else 0
+    _check(_lib.qsa_index_topk_varlen(ctypes.byref(desc), _bf16(idx_q, "idx_q"), _bf16(cmp_k, "cmp_k"),
+                                      cmp_k.stride(0), _i32t(cu_q, "cu_q"), _i32t(q_pos0, "q_pos0"), B, max_q,
+                                      max_q_end, _i32t(sel_blocks, "sel_blocks"), _i32t(sel_count, "sel_count"),
+                                      ws, nbytes, _stream(stream)))
+
+
+def qsa_sparse_attn_prefill_paged(desc, block_size, q, k_pages, v_pages, page_table, cu_q, q_pos0, sel_blocks,
+                                  sel_count, out, lse=None, stream=None):
+    """Packed rows over a paged pool: q, out [total_q, Hq, D]; k_pages, v_pages
+    [n_pages, page_size, Hkv, D]; page_table int32 [B, max_pages]; cu_q int32 [B + 1];
+    q_pos0 int32 [B]; sel_blocks [total_q, top_k]; lse [total_q, Hq] or None."""
+    n_pages, page_size = k_pages.shape[0], k_pages.shape[1]
+    B, max_pages = page_table.shape
+    _check(_lib.qsa_sparse_attn_prefill_paged(
+        ctypes.byref(desc), block_size, sel_blocks.shape[-1], _bf16(q, "q"), _bf16(k_pages, "k_pages"),
+        _bf16(v_pages, "v_pages"), page_size, n_pages, _i32t(page_table, "page_table"), max_pages,
+        _i32t(cu_q, "cu_q"), _i32t(q_pos0, "q_pos0"), B, q.shape[0], _i32t(sel_blocks, "sel_blocks"),
+        _i32t(sel_count, "sel_count"), _bf16(out, "out"), _ptr(lse) if lse is not None else None,
+        _stream(stream)))
 
 
 def qsa_sparse_attn_workspace_size(desc, batch, n_q, top_k_blocks, block_size):

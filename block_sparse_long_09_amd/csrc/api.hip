@@ -308,4 +308,87 @@ qsa_status_t qsa_dense_attn_decode(const qsa_attn_desc_t* desc, const uint16_t* 
                     "dense_attn_decode launch");
 }
 
+size_t qsa_index_topk_varlen_workspace_size(const qsa_index_desc_t* desc, int32_t batch,
+                                            int32_t max_q, int64_t max_q_end) {
+  if (check_index_desc(desc) != QSA_OK || batch < 0 || max_q < 0 || max_q_end < max_q ||
+      max_q_end > kMaxPos)
+    return 0;
+  if (batch == 0 || max_q == 0) return 0;
+  return qsa::plan_index(desc->n_idx_heads, desc->top_k_blocks, batch, max_q, max_q_end,
+                         desc->block_size, false)
+      .workspace;
+}
+
+qsa_status_t qsa_index_topk_varlen(const qsa_index_desc_t* desc, const uint16_t* idx_q,
+                                   const uint16_t* cmp_k, int64_t cmp_k_batch_stride,
+                                   const int32_t* cu_q, const int32_t* q_pos0, int32_t batch,
+                                   int32_t max_q, int64_t max_q_end, int32_t* sel_blocks,
+                                   int32_t* sel_count, void* workspace, size_t workspace_bytes,
+                                   void* stream) {
+  qsa_status_t s = check_index_desc(desc);
+  if (s != QSA_OK) return s;
+  if (batch < 0 || max_q < 0) return fail(QSA_ERR_INVALID_ARGUMENT, "negative batch or max_q");
+  if (batch > 65535) return fail(QSA_ERR_UNSUPPORTED, "batch %d > 65535", batch);
+  if (max_q_end < max_q || max_q_end > kMaxPos)
+    return fail(QSA_ERR_INVALID_ARGUMENT, "max_q_end %lld must be in [max_q, 2^31)", (long long)max_q_end);
+  if (batch == 0 || max_q == 0) return ok();
+  if (!idx_q || !cmp_k || !cu_q || !q_pos0 || !sel_blocks || !sel_count)
+    return fail(QSA_ERR_INVALID_ARGUMENT, "NULL pointer argument");
+  if (!aligned(idx_q, 16) || !aligned(cmp_k, 16))
+    return fail(QSA_ERR_MISALIGNED, "idx_q/cmp_k must be 16-byte aligned");
+  if (!aligned(cu_q, 4) || !aligned(q_pos0, 4) || !aligned(sel_blocks, 4) || !aligned(sel_count, 4))
+    return fail(QSA_ERR_MISALIGNED, "int32 arrays must be 4-byte aligned");
+  const int r = desc->block_size;
+  const int64_t need_blocks = (max_q_end - 1) / r;
+  if (batch > 1) {
+    if (cmp_k_batch_stride < need_blocks * desc->idx_head_dim)
+      return fail(QSA_ERR_INVALID_ARGUMENT, "cmp_k_batch_stride %lld < %lld blocks x 64",
+                  (long long)cmp_k_batch_stride, (long long)need_blocks);
+    if (cmp_k_batch_stride % 8) return fail(QSA_ERR_MISALIGNED, "cmp_k_batch_stride not a multiple of 8");
+  }
+  const qsa::IndexPlan p =
+      qsa::plan_index(desc->n_idx_heads, desc->top_k_blocks, batch, max_q, max_q_end, r, false);
+  if (workspace_bytes < p.workspace || (p.workspace && !workspace))
+    return fail(QSA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", workspace_bytes, p.workspace);
+  if (!aligned(workspace, 16)) return fail(QSA_ERR_MISALIGNED, "workspace must be 16-byte aligned");
+  return hip_status(qsa::launch_index_topk(p, idx_q, cmp_k, cmp_k_batch_stride, q_pos0, batch, max_q,
+                                           r, desc->top_k_blocks, desc->idx_head_weight, sel_blocks,
+                                           sel_count, workspace, (hipStream_t)stream, cu_q),
+                    "index_topk_varlen launch");
+}
+
+qsa_status_t qsa_sparse_attn_prefill_paged(const qsa_attn_desc_t* desc, int32_t block_size,
+                                           int32_t top_k_blocks, const uint16_t* q,
+                                           const uint16_t* k_pages, const uint16_t* v_pages,
+                                           int32_t page_size, int64_t n_pages,
+                                           const int32_t* page_table, int32_t max_pages,
+                                           const int32_t* cu_q, const int32_t* q_pos0, int32_t batch,
+                                           int32_t total_q, const int32_t* sel_blocks,
+                                           const int32_t* sel_count, uint16_t* out, float* lse,
+                                           void* stream) {
+  qsa_status_t s = check_attn_common(desc, block_size, top_k_blocks);
+  if (s != QSA_OK) return s;
+  if (batch < 0 || total_q < 0 || max_pages < 0 || n_pages < 0)
+    return fail(QSA_ERR_INVALID_ARGUMENT, "negative batch, total_q, max_pages or n_pages");
+  if (page_size < block_size || page_size > (1 << 24) || (page_size & (page_size - 1)))
+    return fail(QSA_ERR_INVALID_ARGUMENT, "page_size %d must be a power of two >= block_size %d",
+                page_size, block_size);
+  if (n_pages * (int64_t)page_size > kMaxPos)
+    return fail(QSA_ERR_INVALID_ARGUMENT, "n_pages * page_size must be below 2^31");
+  if (batch == 0 || total_q == 0) return ok();
+  if (!q || !k_pages || !v_pages || !page_table || !cu_q || !q_pos0 || !sel_blocks || !sel_count || !out)
+    return fail(QSA_ERR_INVALID_ARGUMENT, "NULL pointer argument");
+  if (!aligned(q, 16) || !aligned(k_pages, 16) || !aligned(v_pages, 16) || !aligned(out, 16))
+    return fail(QSA_ERR_MISALIGNED, "q/k_pages/v_pages/out must be 16-byte aligned");
+  if (!aligned(page_table, 4) || !aligned(cu_q, 4) || !aligned(q_pos0, 4) || !aligned(sel_blocks, 4) ||
+      !aligned(sel_count, 4) || !aligned(lse, 4))
+    return fail(QSA_ERR_MISALIGNED, "int32/fp32 arrays must be 4-byte aligned");
+  const qsa::AttnPlan p = qsa::plan_attn(total_q, (int64_t)top_k_blocks * block_size, false);
+  const qsa::PagedRows pg{cu_q, q_pos0, batch, page_table, max_pages, __builtin_ctz((unsigned)page_size)};
+  return hip_status(qsa::launch_attn(p, q, k_pages, v_pages, 0, 0, nullptr, desc->n_q_heads,
+                                     desc->n_kv_heads, block_size, top_k_blocks, sel_blocks, sel_count,
+                                     desc->softmax_scale, out, lse, nullptr, (hipStream_t)stream, pg),
+                    "sparse_attn_prefill_paged launch");
+}
+
 }  // extern "C"

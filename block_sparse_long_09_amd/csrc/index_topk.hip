@@ -244,7 +244,7 @@ __global__ __launch_bounds__(256) void index_stream_kernel(
     const uint16_t* __restrict__ idx_q, const uint16_t* __restrict__ cmp_k, int64_t cmp_stride,
     const int32_t* __restrict__ q_pos0, int n_q, int r, int keep, float a_scale, float w_epi,
     int n_qgroups, int splits, int split_len, int cap, uint2* __restrict__ buf,
-    int* __restrict__ buf_cnt) {
+    int* __restrict__ buf_cnt, const int32_t* __restrict__ cu_q) {
   constexpr int QPH = 16 / HI;    // queries per lane-half per A tile
   constexpr int QPT = 32 / HI;    // queries per A tile
   constexpr int QW = AT * QPT;    // queries per wave
@@ -265,6 +265,9 @@ __global__ __launch_bounds__(256) void index_stream_kernel(
   uint2* stage = stage_all + (size_t)wave * cap;
 
   const int64_t pos0 = q_pos0[b];
+  // this sequence's query rows: [row0, row0 + nqb) (packed rows when cu_q is given)
+  const int64_t row0 = cu_q ? (int64_t)cu_q[b] : (int64_t)b * n_q;
+  const int nqb = cu_q ? min(cu_q[b + 1] - cu_q[b], n_q) : n_q;  // n_q = rows per sequence at most
   const int sbeg = split * split_len;
   const int send = sbeg + split_len;
 
@@ -282,13 +285,13 @@ __global__ __launch_bounds__(256) void index_stream_kernel(
   for (int s = 0; s < NS; ++s) {
     const int qi = slot_query(s, half);
     int l = 0;
-    if (qi < n_q) {
+    if (qi < nqb) {
       const int64_t bt = (pos0 + qi) / r;
       l = (int)(bt < (int64_t)send ? bt : (int64_t)send);
       minlim = min(minlim, l);
     }
     lim[s] = l;
-    tau[s] = qi < n_q ? -1.0f : INFINITY;  // an absent query never takes a candidate
+    tau[s] = qi < nqb ? -1.0f : INFINITY;  // an absent query never takes a candidate
     cnt[s] = 0;
     maxlim = max(maxlim, l);
   }
@@ -312,8 +315,8 @@ __global__ __launch_bounds__(256) void index_stream_kernel(
         const int qi = qg * QW + a * QPT + qs;
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
-          if (qi < n_q) {
-            const u32x4 v = ld16(idx_q + (((int64_t)b * n_q + qi) * HI + head) * 64 + 16 * ks + 8 * half);
+          if (qi < nqb) {
+            const u32x4 v = ld16(idx_q + ((row0 + qi) * HI + head) * 64 + 16 * ks + 8 * half);
             A[a][ks] = a_scale == 1.0f ? v : scale_bf16x8(v, a_scale);
           } else {
             A[a][ks] = u32x4{0u, 0u, 0u, 0u};
@@ -427,7 +430,7 @@ __global__ __launch_bounds__(256) void index_stream_kernel(
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
       const int qi = slot_query(s, half);
-      if (qi < n_q) buf_cnt[((int64_t)b * n_q + qi) * splits + split] = cnt[s];
+      if (qi < nqb) buf_cnt[((int64_t)b * n_q + qi) * splits + split] = cnt[s];
     }
   }
 }
@@ -448,7 +451,7 @@ __global__ __launch_bounds__(256, 2) void index_prefill_kernel(
     const uint16_t* __restrict__ idx_q, const uint16_t* __restrict__ cmp_k, int64_t cmp_stride,
     const int32_t* __restrict__ q_pos0, int n_q, int r, int keep, float a_scale, float w_epi,
     int n_qgroups, int splits, int split_len, int cap, uint2* __restrict__ buf,
-    int* __restrict__ buf_cnt) {
+    int* __restrict__ buf_cnt, const int32_t* __restrict__ cu_q) {
   constexpr int QPH = 16 / HI;
   constexpr int QPT = 32 / HI;
   constexpr int QW = AT * QPT;
@@ -475,6 +478,9 @@ __global__ __launch_bounds__(256, 2) void index_prefill_kernel(
   lds_u32* kstage_l = (lds_u32*)(kstage_all + wave * cap);
 
   const int64_t pos0 = q_pos0[b];
+  // this sequence's query rows: [row0, row0 + nqb) (packed rows when cu_q is given)
+  const int64_t row0 = cu_q ? (int64_t)cu_q[b] : (int64_t)b * n_q;
+  const int nqb = cu_q ? min(cu_q[b + 1] - cu_q[b], n_q) : n_q;  // n_q = rows per sequence at most
   const int sbeg = split * split_len;
   const int send = sbeg + split_len;
   auto slot_query = [&](int s, int hh) { return qg * QW + (s / QPH) * QPT + hh * QPH + (s % QPH); };
@@ -497,14 +503,14 @@ __global__ __launch_bounds__(256, 2) void index_prefill_kernel(
   for (int s = 0; s < NS; ++s) {
     const int qi = slot_query(s, half);
     int l = 0;
-    if (wave_live && qi < n_q) {
+    if (wave_live && qi < nqb) {
       l = lim_of(qi);
       minlim = min(minlim, l);
     }
-    tau[s] = (wave_live && qi < n_q) ? -1.0f : INFINITY;  // an absent query takes nothing
+    tau[s] = (wave_live && qi < nqb) ? -1.0f : INFINITY;  // an absent query takes nothing
     cnt[s] = 0;
     lim[s] = l;
-    bp[s] = (glb_u64*)buf_of(wave_live && qi < n_q ? qi : 0);
+    bp[s] = (glb_u64*)buf_of(wave_live && qi < nqb ? qi : 0);
     maxlim = max(maxlim, l);
   }
 #pragma unroll
@@ -530,8 +536,8 @@ __global__ __launch_bounds__(256, 2) void index_prefill_kernel(
         const int qi = qg * QW + a * QPT + qs;
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
-          if (wave_live && qi < n_q) {
-            const u32x4 v = ld16(idx_q + (((int64_t)b * n_q + qi) * HI + head) * 64 + 16 * ks + 8 * half);
+          if (wave_live && qi < nqb) {
+            const u32x4 v = ld16(idx_q + ((row0 + qi) * HI + head) * 64 + 16 * ks + 8 * half);
             A[a][ks] = a_scale == 1.0f ? v : scale_bf16x8(v, a_scale);
           } else {
             A[a][ks] = u32x4{0u, 0u, 0u, 0u};
@@ -689,7 +695,7 @@ __global__ __launch_bounds__(256, 2) void index_prefill_kernel(
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
       const int qi = slot_query(s, half);
-      if (qi < n_q) buf_cnt[((int64_t)b * n_q + qi) * splits + split] = cnt[s];
+      if (qi < nqb) buf_cnt[((int64_t)b * n_q + qi) * splits + split] = cnt[s];
     }
   }
 }
@@ -698,7 +704,7 @@ __global__ __launch_bounds__(256, 2) void index_prefill_kernel(
 __global__ __launch_bounds__(256) void index_select_kernel(
     const uint2* __restrict__ buf, const int* __restrict__ buf_cnt, const int32_t* __restrict__ q_pos0,
     int n_q, int r, int k, int splits, int cap, int32_t* __restrict__ sel,
-    int32_t* __restrict__ sel_cnt) {
+    int32_t* __restrict__ sel_cnt, const int32_t* __restrict__ cu_q) {
   __shared__ uint32_t hist[256];
   __shared__ uint32_t bc[2 + 8];
   __shared__ uint32_t scratch[kSelScratch];
@@ -708,12 +714,14 @@ __global__ __launch_bounds__(256) void index_select_kernel(
   const int64_t gq = blockIdx.x;  // b * n_q + qi
   const int b = (int)(gq / n_q);
   const int qi = (int)(gq % n_q);
+  const int64_t row = cu_q ? (int64_t)cu_q[b] + qi : gq;  // output row
+  if (cu_q && qi >= cu_q[b + 1] - cu_q[b]) return;  // qi < n_q (rows per sequence at most)
   const int64_t t = (int64_t)q_pos0[b] + qi;
   const int64_t bt = t / r;
   const int keep = (int)((int64_t)(k - 1) < bt ? (int64_t)(k - 1) : bt);
   const uint2* qb = buf + gq * splits * (int64_t)cap;
   const int* qc = buf_cnt + gq * splits;
-  int32_t* out = sel + gq * k;
+  int32_t* out = sel + row * k;
 
   // segment offsets (at most 8 splits, each at most keep entries)
   if (tid == 0) {
@@ -742,7 +750,7 @@ __global__ __launch_bounds__(256) void index_select_kernel(
   }
   if (tid == 0) {
     out[keep] = (int32_t)bt;
-    sel_cnt[gq] = keep + 1;
+    sel_cnt[row] = keep + 1;
   }
   for (int i = keep + 1 + tid; i < k; i += 256) out[i] = -1;
 }
@@ -999,7 +1007,7 @@ static bool pow2_float(float w) {
   return m == 0.5f;
 }
 
-IndexPlan plan_index(int hi, int k, int batch, int n_q, int64_t max_q_end, int r) {
+IndexPlan plan_index(int hi, int k, int batch, int n_q, int64_t max_q_end, int r, bool allow_decode) {
   IndexPlan p{};
   p.hi = hi;
   const int64_t max_cand = max_q_end > 0 ? (max_q_end - 1) / r : 0;
@@ -1017,7 +1025,8 @@ IndexPlan plan_index(int hi, int k, int batch, int n_q, int64_t max_q_end, int r
   if (lmin > 1024) lmin = 1024;
   const int lcap = (lmin + max(16, lmin / 2) + 7) / 8 * 8;
   const int64_t nsplit = dsplits < 1 ? 1 : dsplits;
-  if (n_q == 1 && nsplit <= kDecodeMaxSplits && (size_t)nsplit * lcap * sizeof(uint2) <= kMergeMaxLds) {
+  if (allow_decode && n_q == 1 && nsplit <= kDecodeMaxSplits &&
+      (size_t)nsplit * lcap * sizeof(uint2) <= kMergeMaxLds) {
     p.decode = true;
     p.splits = (int)nsplit;
     p.list_min = lmin;
@@ -1078,7 +1087,7 @@ IndexPlan plan_index(int hi, int k, int batch, int n_q, int64_t max_q_end, int r
 hipError_t launch_index_topk(const IndexPlan& p, const uint16_t* idx_q, const uint16_t* cmp_k,
                              int64_t cmp_stride, const int32_t* q_pos0, int batch, int n_q, int r,
                              int k, float w, int32_t* sel, int32_t* sel_cnt, void* ws,
-                             hipStream_t stream) {
+                             hipStream_t stream, const int32_t* cu_q) {
   const bool exact_scale = pow2_float(w);
   const float a_scale = exact_scale ? w : 1.0f;
   const float w_epi = exact_scale ? 1.0f : w;
@@ -1115,7 +1124,7 @@ hipError_t launch_index_topk(const IndexPlan& p, const uint16_t* idx_q, const ui
   hipLaunchKernelGGL((exact_scale ? index_prefill_kernel<HI_, AT_, false>                        \
                                   : index_prefill_kernel<HI_, AT_, true>), g1, dim3(256), p.stream_lds, stream, idx_q, cmp_k,  \
                      cmp_stride, q_pos0, n_q, r, k - 1, a_scale, w_epi, p.n_qgroups, p.splits,     \
-                     p.split_len, p.cap, buf, cnt)
+                     p.split_len, p.cap, buf, cnt, cu_q)
     switch (p.hi) {
       case 1: QSA_LAUNCH_PREFILL(1, 1); break;
       case 2: QSA_LAUNCH_PREFILL(2, 1); break;
@@ -1131,7 +1140,7 @@ hipError_t launch_index_topk(const IndexPlan& p, const uint16_t* idx_q, const ui
 #define QSA_LAUNCH_STREAM(HI_)                                                                     \
   hipLaunchKernelGGL((index_stream_kernel<HI_, 1>), g1, dim3(256), p.stream_lds, stream, idx_q,    \
                      cmp_k, cmp_stride, q_pos0, n_q, r, k - 1, a_scale, w_epi, p.n_qgroups,        \
-                     p.splits, p.split_len, p.cap, buf, cnt)
+                     p.splits, p.split_len, p.cap, buf, cnt, cu_q)
     switch (p.hi) {
       case 1: QSA_LAUNCH_STREAM(1); break;
       case 2: QSA_LAUNCH_STREAM(2); break;
@@ -1146,7 +1155,7 @@ hipError_t launch_index_topk(const IndexPlan& p, const uint16_t* idx_q, const ui
   if (e != hipSuccess) return e;
   const int64_t nw = (int64_t)batch * n_q;
   hipLaunchKernelGGL(index_select_kernel, dim3((unsigned)nw), dim3(256), p.select_lds, stream, buf, cnt,
-                     q_pos0, n_q, r, k, p.splits, p.cap, sel, sel_cnt);
+                     q_pos0, n_q, r, k, p.splits, p.cap, sel, sel_cnt, cu_q);
   return hipGetLastError();
 }
 

@@ -30,12 +30,15 @@ struct IndexPlan {
   size_t stream_lds, select_lds;    // dynamic LDS bytes of the two kernels
 };
 
-IndexPlan plan_index(int hi, int k, int batch, int n_q, int64_t max_q_end, int r);
+// allow_decode = false keeps one query per sequence on the prefill kernels
+// (packed variable-length batches)
+IndexPlan plan_index(int hi, int k, int batch, int n_q, int64_t max_q_end, int r,
+                     bool allow_decode = true);
 
 hipError_t launch_index_topk(const IndexPlan& p, const uint16_t* idx_q, const uint16_t* cmp_k,
                              int64_t cmp_stride, const int32_t* q_pos0, int batch, int n_q, int r,
                              int k, float w, int32_t* sel, int32_t* sel_cnt, void* ws,
-                             hipStream_t stream);
+                             hipStream_t stream, const int32_t* cu_q = nullptr);
 
 // How the gather attention cuts its work: one workgroup per (row, split).
 struct AttnPlan {
@@ -47,12 +50,27 @@ struct AttnPlan {
 AttnPlan plan_attn(int batch_rows, int64_t max_tokens, bool split_kv);
 size_t attn_workspace_bytes(const AttnPlan& p, int Hq);
 
+// Packed variable-length rows over a paged K/V pool (all null: not used).
+// Sequence b owns rows [cu_q[b], cu_q[b + 1]) at positions q_pos[b] + i; its
+// token s is row (page_table[b * max_pages + (s >> lps)] << lps) + s % 2^lps
+// of the pool.
+struct PagedRows {
+  const int32_t* cu_q;
+  const int32_t* q_pos;
+  int n_seq;
+  const int32_t* page_table;
+  int max_pages;
+  int lps;
+};
+
 // sel == nullptr: dense (tokens 0..t). kv_len == nullptr: prefill rows at
-// q_pos0 + row sharing one K/V; else decode rows with their own caches.
+// q_pos0 + row sharing one K/V (or packed rows of pg); else decode rows with
+// their own caches.
 hipError_t launch_attn(const AttnPlan& p, const uint16_t* q, const uint16_t* k, const uint16_t* v,
                        int64_t kv_batch_stride, int64_t q_pos0, const int32_t* kv_len, int Hq,
                        int Hkv, int r, int top_k, const int32_t* sel, const int32_t* sel_cnt,
-                       float scale, uint16_t* out, float* lse, void* ws, hipStream_t stream);
+                       float scale, uint16_t* out, float* lse, void* ws, hipStream_t stream,
+                       PagedRows pg = PagedRows{nullptr, nullptr, 0, nullptr, 0, 0});
 
 // Dense causal GQA flash attention (comparator), prefill rows at q_pos0 + i.
 hipError_t launch_dense_prefill(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t q_pos0,

@@ -44,11 +44,12 @@ __global__ __launch_bounds__(256) void attn_gather_kernel(
     const int32_t* __restrict__ kv_len, int Hq, int G, int r, int k,
     const int32_t* __restrict__ sel, const int32_t* __restrict__ sel_cnt, int n_splits,
     int split_tokens, float scale_log2, uint16_t* __restrict__ out, float* __restrict__ lse,
-    float* __restrict__ part_o, float2* __restrict__ part_ml) {
+    float* __restrict__ part_o, float2* __restrict__ part_ml, PagedRows pg) {
   constexpr int WPH = 4 / HKV;  // waves per KV head
   __shared__ uint16_t vtile[4][kChunk * kVPitch];
   __shared__ float xm[4][16], xl[4][16];
   __shared__ int32_t sblk[kSelLds];
+  __shared__ int32_t sphys[kSelLds];  // paged: physical token of each kept block's first token
 
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
@@ -59,7 +60,27 @@ __global__ __launch_bounds__(256) void attn_gather_kernel(
   const int64_t row = blockIdx.x;
   const int split = blockIdx.y;
 
-  const int64_t t = kv_len ? (int64_t)kv_len[row] - 1 : q_pos0 + row;
+  int64_t t;
+  int seq = 0;
+  if (pg.cu_q) {
+    // packed rows: the sequence is the last b with cu_q[b] <= row
+    int lo = 0, hi = pg.n_seq - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (pg.cu_q[mid] <= row) lo = mid;
+      else hi = mid - 1;
+    }
+    seq = lo;
+    t = (int64_t)pg.q_pos[seq] + (row - pg.cu_q[seq]);
+  } else {
+    t = kv_len ? (int64_t)kv_len[row] - 1 : q_pos0 + row;
+  }
+  // paged K/V: token s of the sequence lives at page_table[s >> lps] << lps | s % page
+  const int32_t* ptab = pg.page_table ? pg.page_table + (int64_t)seq * pg.max_pages : nullptr;
+  auto phys = [&](int64_t s) -> int64_t {
+    return ptab ? ((int64_t)ptab[s >> pg.lps] << pg.lps) + (s & ((1 << pg.lps) - 1)) : s;
+  };
+  const int64_t t_phys = phys(t);
   const uint16_t* kb = kc + (kv_len ? row * kv_batch_stride : 0);
   const uint16_t* vb = vc + (kv_len ? row * kv_batch_stride : 0);
   const int64_t n_tok = sel ? (int64_t)sel_cnt[row] * r : t + 1;
@@ -82,24 +103,32 @@ __global__ __launch_bounds__(256) void attn_gather_kernel(
   if (srow) {
     const int jb1 = p_end > p_beg ? (int)((p_end - 1) >> lr) + 1 : jb0;
     const int nb = min(jb1 - jb0, kSelLds);
-    for (int i = threadIdx.x; i < nb; i += 256) sblk[i] = srow[jb0 + i];
+    for (int i = threadIdx.x; i < nb; i += 256) {
+      const int j = srow[jb0 + i];
+      sblk[i] = j;
+      if (ptab) sphys[i] = (int32_t)phys((int64_t)j << lr);  // a block never straddles a page
+    }
   }
   __syncthreads();
 
-  // Token of list position p, and whether it is attended.
+  // Storage row (token index into K/V) of list position p, and whether it is
+  // attended; positions that are not attended point at a row that exists.
   auto token_of = [&](int64_t p, bool& valid) -> int64_t {
     int64_t s;
     if (p >= p_end) {
       valid = false;
-      return t;
+      return t_phys;
     }
     if (srow) {
-      const int j = sblk[(int)(p >> lr) - jb0];
-      s = ((int64_t)j << lr) + (p & (r - 1));
+      const int i = (int)(p >> lr) - jb0;
+      const int m = (int)(p & (r - 1));
+      s = ((int64_t)sblk[i] << lr) + m;
+      valid = s <= t;
+      if (ptab) return (int64_t)sphys[i] + (valid ? m : 0);
     } else {
       s = p;
+      valid = s <= t;
     }
-    valid = s <= t;
     return valid ? s : t;
   };
 
@@ -375,7 +404,8 @@ size_t attn_workspace_bytes(const AttnPlan& p, int Hq) {
 hipError_t launch_attn(const AttnPlan& p, const uint16_t* q, const uint16_t* k, const uint16_t* v,
                        int64_t kv_batch_stride, int64_t q_pos0, const int32_t* kv_len, int Hq,
                        int Hkv, int r, int top_k, const int32_t* sel, const int32_t* sel_cnt,
-                       float scale, uint16_t* out, float* lse, void* ws, hipStream_t stream) {
+                       float scale, uint16_t* out, float* lse, void* ws, hipStream_t stream,
+                       PagedRows pg) {
   const int G = Hq / Hkv;
   if (sel && top_k > kSelLds) return hipErrorInvalidValue;
   const float scale_log2 = scale * 1.4426950408889634f;
@@ -390,7 +420,7 @@ hipError_t launch_attn(const AttnPlan& p, const uint16_t* q, const uint16_t* k, 
 #define QSA_LAUNCH_ATTN(HKV_)                                                                   \
   hipLaunchKernelGGL(attn_gather_kernel<HKV_>, grid, dim3(256), 0, stream, q, k, v,            \
                      kv_batch_stride, q_pos0, kv_len, Hq, G, r, top_k, sel, sel_cnt, p.splits, \
-                     (int)p.split_tokens, scale_log2, out, lse, part_o, part_ml)
+                     (int)p.split_tokens, scale_log2, out, lse, part_o, part_ml, pg)
   switch (Hkv) {
     case 1: QSA_LAUNCH_ATTN(1); break;
     case 2: QSA_LAUNCH_ATTN(2); break;

@@ -5,13 +5,17 @@ Sequence of library calls (every step runs in the HIP kernels of libqsa.so):
                  -> qsa_index_topk -> qsa_sparse_attn_prefill
   decode step:   qsa_index_topk (n_q = 1 per sequence at kv_len - 1)
                  -> qsa_sparse_attn_decode
+  packed batch:  qsa_compress_keys per sequence -> qsa_index_topk_varlen
+                 -> qsa_sparse_attn_prefill_paged (new rows of several
+                 sequences appended to cached prefixes, K/V in pages)
 The objects below only own the caller-side buffers (workspaces, selections,
 outputs) so that repeated calls allocate nothing.
 """
 import torch
 
-from . import (attn_desc, index_desc, qsa_compress_keys, qsa_index_topk, qsa_index_topk_workspace_size,
-               qsa_sparse_attn_decode, qsa_sparse_attn_prefill, qsa_sparse_attn_workspace_size, workspace)
+from . import (attn_desc, index_desc, qsa_compress_keys, qsa_index_topk, qsa_index_topk_varlen,
+               qsa_index_topk_varlen_workspace_size, qsa_index_topk_workspace_size, qsa_sparse_attn_decode,
+               qsa_sparse_attn_prefill, qsa_sparse_attn_prefill_paged, qsa_sparse_attn_workspace_size, workspace)
 
 
 class PrefillPath:
@@ -87,3 +91,50 @@ class DecodePath:
     def __call__(self, q, k_cache, v_cache, idx_q, cmp_k, kv_len, q_pos):
         self.select(idx_q, cmp_k, q_pos)
         return self.attend(q, k_cache, v_cache, kv_len)
+
+
+class PagedBatchPath:
+    """Prefill of a packed batch: sequence b appends n[b] new rows at positions
+    q_pos0[b] .. q_pos0[b] + n[b] - 1 to its cached prefix. K/V live in a paged
+    pool ([n_pages, page_size, Hkv, D]) addressed by a page table
+    ([batch, max_pages]); token and block indexer keys are cached per sequence
+    ([batch, max_len, 64] and [batch, max_len / r, 64]). One row per sequence
+    is a decode step of the same batch."""
+
+    def __init__(self, Hq, Hkv, Hi, batch, max_q, max_len, r=4, k=512, D=128, di=64, device="cuda"):
+        self.r, self.k, self.batch, self.max_q, self.max_len = r, k, batch, max_q, max_len
+        self.idesc = index_desc(r, k, Hi, di)
+        self.adesc = attn_desc(Hq, Hkv, D)
+        self.ws_index = workspace(qsa_index_topk_varlen_workspace_size(self.idesc, batch, max_q, max_len), device)
+        self.total_max = batch * max_q
+        self.sel = torch.empty((self.total_max, k), dtype=torch.int32, device=device)
+        self.cnt = torch.empty((self.total_max,), dtype=torch.int32, device=device)
+        self.out = torch.empty((self.total_max, Hq, D), dtype=torch.bfloat16, device=device)
+        self.lse = torch.empty((self.total_max, Hq), dtype=torch.float32, device=device)
+
+    def compress(self, idx_k_cache, cmp_k, q_pos0_host, n_host):
+        """Block keys of the blocks completed by each sequence's new rows."""
+        for b, (p0, n) in enumerate(zip(q_pos0_host, n_host)):
+            first, last = p0 // self.r, (p0 + n) // self.r
+            if last > first:
+                qsa_compress_keys(idx_k_cache[b], cmp_k[b], self.r, first, last - first)
+
+    def select(self, idx_q, cmp_k, cu_q, q_pos0, total_q, max_q_end=None):
+        qsa_index_topk_varlen(self.idesc, idx_q[:total_q], cmp_k, cu_q, q_pos0, self.max_q,
+                              self.max_len if max_q_end is None else max_q_end,
+                              self.sel[:total_q], self.cnt[:total_q], self.ws_index)
+        return self.sel[:total_q], self.cnt[:total_q]
+
+    def attend(self, q, k_pages, v_pages, page_table, cu_q, q_pos0, total_q, sel=None, cnt=None):
+        sel = self.sel[:total_q] if sel is None else sel
+        cnt = self.cnt[:total_q] if cnt is None else cnt
+        qsa_sparse_attn_prefill_paged(self.adesc, self.r, q[:total_q], k_pages, v_pages, page_table, cu_q,
+                                      q_pos0, sel, cnt, self.out[:total_q], self.lse[:total_q])
+        return self.out[:total_q], self.lse[:total_q]
+
+    def __call__(self, q, k_pages, v_pages, page_table, idx_q, idx_k_cache, cmp_k, cu_q, q_pos0, q_pos0_host,
+                 n_host):
+        total_q = int(sum(n_host))
+        self.compress(idx_k_cache, cmp_k, q_pos0_host, n_host)
+        self.select(idx_q, cmp_k, cu_q, q_pos0, total_q)
+        return self.attend(q, k_pages, v_pages, page_table, cu_q, q_pos0, total_q)

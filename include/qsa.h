@@ -146,6 +146,51 @@ qsa_status_t qsa_sparse_attn_decode(const qsa_attn_desc_t* desc, int32_t block_s
                                     uint16_t* out, float* lse, void* workspace,
                                     size_t workspace_bytes, void* stream);
 
+/* ---- Packed variable-length batches over a paged K/V cache (serving) ----
+ * A batch of `batch` sequences whose new queries are packed row after row:
+ * sequence b owns rows [cu_q[b], cu_q[b + 1]) of idx_q / q / sel / out, its
+ * i-th row sitting at position q_pos0[b] + i (a prefill chunk appended to a
+ * cached prefix; one row per sequence is a decode step). cu_q (DEVICE int32
+ * [batch + 1], cu_q[0] = 0, non-decreasing) and q_pos0 (DEVICE int32 [batch])
+ * are read on the device and are not checked. */
+
+/* Bytes of workspace qsa_index_topk_varlen needs (0 on bad input).
+ * max_q: an upper bound on the rows of one sequence; max_q_end: an upper bound
+ * on q_pos0[b] + rows of b. */
+size_t qsa_index_topk_varlen_workspace_size(const qsa_index_desc_t* desc, int32_t batch, int32_t max_q,
+                                            int64_t max_q_end);
+
+/* qsa_index_topk over packed rows: idx_q [total_q][H_i][d_i], sel_blocks
+ * [total_q][k], sel_count [total_q]; cmp_k as for qsa_index_topk (block keys
+ * of sequence b at cmp_k + b * cmp_k_batch_stride, at least
+ * (q_pos0[b] + rows - 1) / r of them). Same selection rule per row. */
+qsa_status_t qsa_index_topk_varlen(const qsa_index_desc_t* desc, const uint16_t* idx_q,
+                                   const uint16_t* cmp_k, int64_t cmp_k_batch_stride,
+                                   const int32_t* cu_q, const int32_t* q_pos0, int32_t batch,
+                                   int32_t max_q, int64_t max_q_end, int32_t* sel_blocks,
+                                   int32_t* sel_count, void* workspace, size_t workspace_bytes,
+                                   void* stream);
+
+/* qsa_sparse_attn_prefill over packed rows and a paged K/V pool.
+ *   q, out [total_q][Hq][D]; lse [total_q][Hq] (may be NULL).
+ *   k_pages, v_pages [n_pages][page_size][Hkv][D]: the pool.
+ *   page_table DEVICE int32 [batch][max_pages]: token s of sequence b lives at
+ *   slot s % page_size of page page_table[b][s / page_size]; the pages of
+ *   every token a row may attend (0 .. its position) must be listed.
+ *   page_size: a power of two, at least block_size (a block never straddles
+ *   pages); n_pages * page_size < 2^31.
+ *   sel_blocks [total_q][top_k_blocks], sel_count [total_q] as written by
+ *   qsa_index_topk_varlen. No workspace is needed (pass NULL, 0). */
+qsa_status_t qsa_sparse_attn_prefill_paged(const qsa_attn_desc_t* desc, int32_t block_size,
+                                           int32_t top_k_blocks, const uint16_t* q,
+                                           const uint16_t* k_pages, const uint16_t* v_pages,
+                                           int32_t page_size, int64_t n_pages,
+                                           const int32_t* page_table, int32_t max_pages,
+                                           const int32_t* cu_q, const int32_t* q_pos0, int32_t batch,
+                                           int32_t total_q, const int32_t* sel_blocks,
+                                           const int32_t* sel_count, uint16_t* out, float* lse,
+                                           void* stream);
+
 const char* qsa_status_string(qsa_status_t status);
 const char* qsa_last_error_message(void);
 int qsa_abi_version(void);
