@@ -123,7 +123,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", default="c5", choices=["c5", "c3", "c4"])
+    ap.add_argument("--config", default="c5", choices=["c5", "c3", "c4", "c6"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=256, help="queries in the oracle's timed sample")
@@ -148,6 +148,8 @@ def main():
 
     torch.cuda.set_device(0)
     dev = "cuda"
+    if args.config == "c6":
+        return run_paged_batch(args, torch, qsa)
     if args.config == "c5":
         Wp, Wd = CONFIGS["c5a"], CONFIGS["c5b"]
     elif args.config == "c3":
@@ -381,6 +383,118 @@ def main():
         "pages_speedup_context": PAGES_SPEEDUP,
         "cpu_baseline": cpu,
         "sample_parity": sample_parity,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def paged_work(W):
+    """Algorithmic work of one packed step (each sequence's new rows)."""
+    work = {"index_flops": 0, "attn_bytes": 0, "attn_flops": 0, "rows": 0}
+    for p0, n in zip(W.prefix, W.new):
+        t = np.arange(p0, p0 + n, dtype=np.int64)
+        b = t // W.r
+        ntok = np.minimum(W.k - 1, b) * W.r + (t - b * W.r) + 1
+        work["index_flops"] += int(b.sum()) * W.Hi * W.di * 2
+        work["attn_bytes"] += int(ntok.sum()) * W.Hkv * W.D * 2 * 2 + 2 * n * W.Hq * W.D * 2 + n * (W.k + 1) * 4
+        work["attn_flops"] += int(ntok.sum()) * W.Hq * W.D * 4
+        work["rows"] += n
+    return work
+
+
+def run_paged_batch(args, torch, qsa):
+    """Packed variable-length batch over a paged K/V pool (config 6)."""
+    from block_sparse_long_09_amd.pipeline import PagedBatchPath
+    from gen.configs import PAGED
+    from gen.device import idx_keys_to_device, normal_to_device
+    W = PAGED[args.config]
+    dev = "cuda"
+    B, page = W.batch, W.page_size
+    L = W.lengths
+    max_len = (max(L) + page - 1) // page * page
+    max_pages = max_len // page
+    pages_of = [(x + page - 1) // page for x in L]
+    n_pages = sum(pages_of)
+    t_setup = time.time()
+    log(f"generating paged pool {W.name}: {n_pages} pages of {page} tokens")
+    kpool = normal_to_device(W.seed, 2, (n_pages, page, W.Hkv, W.D))
+    vpool = normal_to_device(W.seed, 3, (n_pages, page, W.Hkv, W.D))
+    perm = np.random.default_rng(W.seed).permutation(n_pages).astype(np.int32)
+    table = np.zeros((B, max_pages), np.int32)
+    nxt = 0
+    for b in range(B):
+        table[b, :pages_of[b]] = perm[nxt:nxt + pages_of[b]]
+        nxt += pages_of[b]
+    table_d = torch.from_numpy(table).to(dev)
+    total = sum(W.new)
+    Q = normal_to_device(W.seed, 1, (total, W.Hq, W.D))
+    iq = normal_to_device(W.seed, 4, (total, W.Hi, W.di))
+    ik = idx_keys_to_device(W.seed, B, max_len, W.di, W.needle_window, W.r)
+    cmp = torch.zeros((B, max_len // W.r, W.di), dtype=torch.bfloat16, device=dev)
+    for b in range(B):  # the cached prefixes' block keys
+        qsa.qsa_compress_keys(ik[b], cmp[b], W.r, 0, W.prefix[b] // W.r)
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(W.new)]), dtype=torch.int32, device=dev)
+    p0 = torch.tensor(W.prefix, dtype=torch.int32, device=dev)
+    path = PagedBatchPath(W.Hq, W.Hkv, W.Hi, B, max(W.new), max_len, r=W.r, k=W.k, D=W.D, di=W.di, device=dev)
+    torch.cuda.synchronize()
+    log(f"setup {time.time() - t_setup:.1f}s")
+    names = ["compress", "index_varlen", "attn_paged"]
+    fns = [lambda: path.compress(ik, cmp, W.prefix, W.new),
+           lambda: path.select(iq, cmp, cu, p0, total),
+           lambda: path.attend(Q, kpool, vpool, table_d, cu, p0, total)]
+    timer = PhaseTimer(torch, names)
+    for _ in range(args.warmup):
+        timer.run(fns)
+    torch.cuda.synchronize()
+    recorded = [timer.run(fns) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for evs in recorded:
+        timer.collect(evs)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        for f in fns:
+            f()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / args.steps
+    phase = timer.mean_ms()
+    work = paged_work(W)
+    roof = {
+        "attn_paged": {"bound": "hbm", "achieved": work["attn_bytes"] / (phase["attn_paged"] * 1e-3) / 1e9,
+                       "peak": HBM_PEAK_GBS, "unit": "GB/s", "traffic": None, "bytes_per_launch": work["attn_bytes"],
+                       "avg_launch_ms": phase["attn_paged"],
+                       "mfma_tflops": work["attn_flops"] / (phase["attn_paged"] * 1e-3) / 1e12},
+        "index_varlen": {"bound": "mfma", "achieved": work["index_flops"] / (phase["index_varlen"] * 1e-3) / 1e12,
+                         "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s", "traffic": None,
+                         "flops_per_launch": work["index_flops"], "avg_launch_ms": phase["index_varlen"]},
+    }
+    for v in roof.values():
+        v["frac"] = v["achieved"] / v["peak"]
+    dom = max(roof, key=lambda n: phase[n])
+    step_ms = sum(phase.values())
+    out = {
+        "metric": METRIC,
+        "value": work["rows"] / wall,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": wall * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": W.name, "sequences": B, "cached_prefix": list(W.prefix), "new_rows": list(W.new),
+                   "page_size": page, "budget_tokens": W.k * W.r, "block_size": W.r,
+                   "heads_q_kv_idx": [W.Hq, W.Hkv, W.Hi]},
+        "phase_ms": phase,
+        "phase_sum_ms": step_ms,
+        "roofline": dict(roof[dom], kernel=dom),
+        "rooflines": roof,
+        "dense": None,
+        "pages_speedup_context": PAGES_SPEEDUP,
+        "cpu_baseline": None,
+        "sample_parity": None,
     }
     print(json.dumps(out), flush=True)
 

@@ -1051,9 +1051,12 @@ IndexPlan plan_index(int hi, int k, int batch, int n_q, int64_t max_q_end, int r
   p.n_qgroups = (n_q + p.qw - 1) / p.qw;
   int64_t splits;
   if (p.wide) {
-    // workgroups of 4 query groups; about two workgroups per CU in one round
+    // workgroups of 4 query groups; about two workgroups per CU in one round.
+    // A packed batch (allow_decode false) sizes n_q for its longest sequence
+    // and most other workgroups are empty: size the splits for one sequence.
     const int64_t n_wg = ((int64_t)p.n_qgroups + 3) / 4;
-    splits = (512 + batch * n_wg - 1) / (batch * n_wg);
+    const int64_t busy = allow_decode ? batch * n_wg : n_wg;
+    splits = (512 + busy - 1) / busy;
     const int64_t max_splits = (max_cand + 1023) / 1024;
     if (splits > max_splits) splits = max_splits;
   } else {

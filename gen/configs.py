@@ -59,3 +59,44 @@ CONFIGS = {
     # 5b: decode, 4 sequences at 1M
     "c5b": Workload("c5b_decode_b4_1m", "decode", 1006, 4, 1048576, 1, 1048575, 32, 4, 8, needle_window=4096),
 }
+
+
+@dataclass(frozen=True)
+class PagedBatch:
+    """A packed serving batch: sequence b has a cached prefix of prefix[b]
+    tokens and appends new[b] rows (1 = a decode step); K/V in a shared pool of
+    page_size-token pages in shuffled order."""
+    name: str
+    seed: int
+    prefix: tuple
+    new: tuple
+    Hq: int
+    Hkv: int
+    Hi: int
+    page_size: int = 256
+    D: int = 128
+    di: int = 64
+    r: int = 4
+    k: int = 512
+    needle_window: int = 4096
+
+    @property
+    def batch(self):
+        return len(self.prefix)
+
+    @property
+    def w(self):
+        return 1.0 / self.Hi
+
+    @property
+    def lengths(self):
+        return [p + n for p, n in zip(self.prefix, self.new)]
+
+
+PAGED = {
+    # 6: 8 sequences with cached contexts of 128K .. 1M appending chunks of
+    # 1 .. 4096 rows (two of them decode steps), 256-token pages
+    "c6": PagedBatch("c6_paged_batch_8seq_128k_1m", 1007,
+                     (131072, 262144, 393216, 524288, 655360, 786432, 917504, 1040384),
+                     (2048, 1024, 512, 4096, 256, 1, 1, 2048), 32, 4, 8),
+}
