@@ -110,3 +110,37 @@ def test_workspace_sizes_grow_with_work(qsa):
     c = qsa.qsa_index_topk_workspace_size(d, 4, 4096, 1 << 16)
     assert 0 < a <= b <= c
     assert qsa.qsa_index_topk_workspace_size(d, 1, 4096, 100) == 0  # max_q_end < n_q: invalid
+
+
+def test_varlen_and_paged_reject_bad_arguments(qsa):
+    L = qsa._lib
+    d = qsa.index_desc(4, 512, 8)
+    ws = qsa.qsa_index_topk_varlen_workspace_size(d, 8, 4096, 1 << 20)
+    assert ws > 0
+
+    def iv(**kw):
+        a = dict(iq=FAKE, ck=FAKE, st=1 << 24, cu=FAKE, pos=FAKE, b=8, mq=4096, end=1 << 20, sel=FAKE, cnt=FAKE,
+                 ws=FAKE, wsb=ws)
+        a.update(kw)
+        return L.qsa_index_topk_varlen(ctypes.byref(d), a["iq"], a["ck"], a["st"], a["cu"], a["pos"], a["b"],
+                                       a["mq"], a["end"], a["sel"], a["cnt"], a["ws"], a["wsb"], None)
+    assert iv(cu=None) == 1
+    assert iv(wsb=ws - 1) == 4
+    assert iv(end=100) == 1            # max_q_end < max_q
+    assert iv(st=64) == 1              # per-sequence block keys do not fit the stride
+    assert iv(cu=FAKE + 2) == 3
+    assert iv(mq=0) == 0
+    a = qsa.attn_desc(32, 4)
+
+    def pg(**kw):
+        x = dict(r=4, k=512, page=256, npages=100, tab=FAKE, maxp=16, cu=FAKE, pos=FAKE, b=2, tq=10)
+        x.update(kw)
+        return L.qsa_sparse_attn_prefill_paged(ctypes.byref(a), x["r"], x["k"], FAKE, FAKE, FAKE, x["page"],
+                                               x["npages"], x["tab"], x["maxp"], x["cu"], x["pos"], x["b"],
+                                               x["tq"], FAKE, FAKE, FAKE, None, None)
+    assert pg(page=100) == 1           # not a power of two
+    assert pg(page=2, r=4) == 1        # a block would straddle pages
+    assert pg(npages=1 << 30) == 1     # pool beyond 2^31 tokens
+    assert pg(tab=None) == 1
+    assert pg(k=2048) == 2
+    assert pg(tq=0) == 0
