@@ -41,6 +41,7 @@ def lib():
         L.qsa_ref_attend_tokens.argtypes = [vp, vp, vp, i32, i32, i32, f64, vp, i64, vp, vp]
         L.qsa_ref_sparse_attn.argtypes = [vp, vp, vp, i64, i32, i32, i32, i32, f64, i32, i32, vp, vp, vp, vp]
         L.qsa_ref_dense_attn.argtypes = [vp, vp, vp, i64, i32, i32, i32, i32, f64, vp, vp]
+        L.qsa_ref_distill_kl.argtypes = [vp, vp, vp, vp, i64, i32, i32, i32, i32, f64, i32, i32, f64, i32, vp]
         _lib = L
     return _lib
 
@@ -131,3 +132,19 @@ def dense_attn(Q, K, V, t0, scale=None):
     lse = np.empty((nq, Hq), np.float64)
     lib().qsa_ref_dense_attn(_p(Q), _p(K), _p(V), t0, nq, Hq, Hkv, D, scale, _p(out), _p(lse))
     return out, lse
+
+
+def distill_kl(Q, K, idx_q, blocks, t0, r, w, scale=None):
+    """O7: per-query KL(attention-mass target || indexer softmax) over the candidate
+    blocks, for queries t0 .. t0 + nq - 1. Q [nq, Hq, D]; K [L, Hkv, D];
+    idx_q [nq, Hi, di]; blocks [*, di] -> float64 [nq]."""
+    Q, K, idx_q, blocks = _u16(Q), _u16(K), _u16(idx_q), _u16(blocks)
+    nq, Hq, D = Q.shape
+    Hkv = K.shape[1]
+    Hi, di = idx_q.shape[1], idx_q.shape[2]
+    assert K.shape[0] >= t0 + nq
+    scale = 1.0 / math.sqrt(D) if scale is None else scale
+    out = np.empty(nq, np.float64)
+    lib().qsa_ref_distill_kl(_p(Q), _p(K), _p(idx_q), _p(blocks), t0, nq, Hq, Hkv, D, scale, Hi, di, float(w), r,
+                             _p(out))
+    return out

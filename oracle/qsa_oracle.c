@@ -240,3 +240,71 @@ void qsa_ref_dense_attn(const uint16_t* Q, const uint16_t* K, const uint16_t* V,
     free(tok);
   }
 }
+
+/* ---------------------------------------------------------------- O7 ---- */
+/* Forward of the indexer's dense-distillation loss. [EXPLAINER] describes a
+   first training stage in which only the indexer learns, with a KL divergence
+   that pulls it towards the full-attention model's attention distribution.
+   The pages give no formula; the reading taken here, for query t with own
+   block b_t and candidate blocks j < b_t:
+     target     P_j = M_j / sum_{j' < b_t} M_{j'},
+                M_j = sum_h sum_{s in block j} a_h(s), a_h the dense causal
+                softmax of query head h over the tokens s <= t (as in O6);
+     indexer    Q_j = exp(s_j) / sum_{j' < b_t} exp(s_{j'}), s_j the O2 score
+                (rounded to fp32, used as a logit);
+     loss       KL_t = sum_j P_j (ln P_j - ln Q_j), with 0 ln 0 = 0;
+                KL_t = 0 when b_t = 0 (no candidate).
+   Q: [nq][Hq][D]; K: [L][Hkv][D]; idx_q: [nq][Hi][di]; blocks: [*][di].
+   kl: [nq] (double). */
+void qsa_ref_distill_kl(const uint16_t* Q, const uint16_t* K, const uint16_t* idx_q,
+                        const uint16_t* blocks, int64_t t0, int nq, int Hq, int Hkv, int D,
+                        double scale, int Hi, int di, double w, int r, double* kl) {
+  const int G = Hq / Hkv;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int i = 0; i < nq; ++i) {
+    const int64_t t = t0 + i;
+    const int64_t bt = t / r;
+    if (bt == 0) {
+      kl[i] = 0.0;
+      continue;
+    }
+    double* logit = (double*)malloc(sizeof(double) * (size_t)(t + 1));
+    double* mass = (double*)calloc((size_t)bt, sizeof(double));
+    for (int h = 0; h < Hq; ++h) {
+      const int g = h / G;
+      const uint16_t* q = Q + ((int64_t)i * Hq + h) * D;
+      double mx = -INFINITY;
+      for (int64_t s = 0; s <= t; ++s) {
+        const uint16_t* krow = K + (s * Hkv + g) * D;
+        double dot = 0.0;
+        for (int x = 0; x < D; ++x) dot += widen(q[x]) * widen(krow[x]);
+        logit[s] = scale * dot;
+        if (logit[s] > mx) mx = logit[s];
+      }
+      double z = 0.0;
+      for (int64_t s = 0; s <= t; ++s) z += exp(logit[s] - mx);
+      for (int64_t s = 0; s < bt * r; ++s) mass[s / r] += exp(logit[s] - mx) / z;
+    }
+    double msum = 0.0;
+    for (int64_t j = 0; j < bt; ++j) msum += mass[j];
+    // indexer logits and their log-sum-exp
+    float* sc = (float*)malloc(sizeof(float) * (size_t)bt);
+    double smax = -INFINITY;
+    for (int64_t j = 0; j < bt; ++j) {
+      sc[j] = score_block(idx_q + (int64_t)i * Hi * di, blocks + j * di, Hi, di, w);
+      if (sc[j] > smax) smax = sc[j];
+    }
+    double zs = 0.0;
+    for (int64_t j = 0; j < bt; ++j) zs += exp((double)sc[j] - smax);
+    const double lse_s = smax + log(zs);
+    double acc = 0.0;
+    for (int64_t j = 0; j < bt; ++j) {
+      const double p = mass[j] / msum;
+      if (p > 0.0) acc += p * (log(p) - ((double)sc[j] - lse_s));
+    }
+    kl[i] = acc;
+    free(sc);
+    free(mass);
+    free(logit);
+  }
+}

@@ -305,3 +305,56 @@ def test_diagonal_block_is_causally_masked():
     vv = torch.from_numpy(widen(V[:, 0]))[None, None].expand(1, Hq, L, D)
     ref = torch.nn.functional.scaled_dot_product_attention(qq, kk, vv, attn_mask=torch.from_numpy(mask)[None, None, None])
     assert np.abs(o[0] - ref[0, :, 0].numpy()).max() < 1e-12
+
+
+# ------------------------------------------------------------------ O7 pins --
+def _kl_inputs(seed, L, Hq, Hkv, Hi, r):
+    Q = gen.normal(seed, 1, (L, Hq, 128))
+    K = gen.normal(seed, 2, (L, Hkv, 128))
+    iq = gen.normal(seed, 4, (L, Hi, 64))
+    ik = gen.normal(seed, 5, (L, 64))
+    return Q, K, iq, oracle.compress(ik, r)
+
+
+def _lse(x):
+    m = max(x)
+    return m + math.log(sum(math.exp(v - m) for v in x))
+
+
+def test_distill_kl_zero_queries_closed_form():
+    # Q = 0: every head attends uniformly, every complete candidate block holds
+    # r of the t + 1 tokens, so the target is uniform over the b_t candidates and
+    # KL = lse(s) - mean(s) - ln b_t in terms of the (pinned) O2 scores alone
+    L, Hq, Hkv, Hi, r = 120, 4, 2, 4, 4
+    Q, K, iq, blocks = _kl_inputs(71, L, Hq, Hkv, Hi, r)
+    Q0 = np.zeros_like(Q)
+    t0 = 20
+    kl = oracle.distill_kl(Q0[t0:], K, iq[t0:], blocks, t0, r, 1.0 / Hi)
+    for i, t in enumerate(range(t0, L)):
+        bt = t // r
+        s = [float(v) for v in oracle.scores(iq[t], blocks[:bt], 1.0 / Hi)]
+        want = _lse(s) - sum(s) / bt - math.log(bt)
+        assert kl[i] == pytest.approx(want, abs=1e-12)
+
+
+def test_distill_kl_zero_when_both_uniform_and_trivial_cases():
+    L, Hq, Hkv, Hi, r = 64, 4, 1, 4, 4
+    Q, K, iq, blocks = _kl_inputs(73, L, Hq, Hkv, Hi, r)
+    # zero attention and zero indexer queries: both distributions uniform
+    kl = oracle.distill_kl(np.zeros_like(Q), K, np.zeros_like(iq), blocks, 0, r, 1.0 / Hi)
+    assert np.all(np.abs(kl) < 1e-13)
+    # b_t = 0 (no candidate): 0; b_t = 1 (one candidate): both distributions are [1]
+    kl = oracle.distill_kl(Q[:8], K, iq[:8], blocks, 0, r, 1.0 / Hi)
+    assert np.all(kl[:4] == 0.0)
+    assert np.all(np.abs(kl[4:8]) < 1e-13)
+
+
+def test_distill_kl_nonnegative_and_depends_on_scores():
+    L, Hq, Hkv, Hi, r = 200, 8, 2, 8, 4
+    Q, K, iq, blocks = _kl_inputs(79, L, Hq, Hkv, Hi, r)
+    kl = oracle.distill_kl(Q[8:], K, iq[8:], blocks, 8, r, 1.0 / Hi)
+    assert np.all(kl >= -1e-13) and np.all(np.isfinite(kl))
+    # a larger indexer temperature-free logit scale changes the loss
+    iq2 = gen.f32_to_bf16(gen.bf16_to_f64(iq).astype(np.float32) * 4)
+    kl2 = oracle.distill_kl(Q[8:], K, iq2[8:], blocks, 8, r, 1.0 / Hi)
+    assert not np.allclose(kl, kl2)
