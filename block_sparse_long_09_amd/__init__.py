@@ -60,6 +60,8 @@ _sig("qsa_index_topk_varlen", ctypes.c_int,
      [_PI, _vp, _vp, _i64, _vp, _vp, _i32, _i32, _i64, _vp, _vp, _vp, _sz, _vp])
 _sig("qsa_sparse_attn_prefill_paged", ctypes.c_int,
      [_PA, _i32, _i32, _vp, _vp, _vp, _i32, _i64, _vp, _i32, _vp, _vp, _i32, _i32, _vp, _vp, _vp, _vp, _vp])
+_sig("qsa_distill_kl_workspace_size", _sz, [_PA, _i32])
+_sig("qsa_distill_kl_prefill", ctypes.c_int, [_PA, _PI, _vp, _vp, _vp, _vp, _i64, _i32, _i64, _vp, _vp, _sz, _vp])
 _sig("qsa_status_string", ctypes.c_char_p, [ctypes.c_int])
 _sig("qsa_last_error_message", ctypes.c_char_p, [])
 _sig("qsa_abi_version", ctypes.c_int, [])
@@ -71,6 +73,7 @@ EXPORTS = (
     "qsa_status_string", "qsa_last_error_message", "qsa_abi_version",
     "qsa_dense_attn_workspace_size", "qsa_dense_attn_prefill", "qsa_dense_attn_decode",
     "qsa_index_topk_varlen_workspace_size", "qsa_index_topk_varlen", "qsa_sparse_attn_prefill_paged",
+    "qsa_distill_kl_workspace_size", "qsa_distill_kl_prefill",
 )
 
 
@@ -191,6 +194,22 @@ def qsa_sparse_attn_prefill_paged(desc, block_size, q, k_pages, v_pages, page_ta
         _i32t(cu_q, "cu_q"), _i32t(q_pos0, "q_pos0"), B, q.shape[0], _i32t(sel_blocks, "sel_blocks"),
         _i32t(sel_count, "sel_count"), _bf16(out, "out"), _ptr(lse) if lse is not None else None,
         _stream(stream)))
+
+
+def qsa_distill_kl_workspace_size(adesc, n_q):
+    return _lib.qsa_distill_kl_workspace_size(ctypes.byref(adesc), n_q)
+
+
+def qsa_distill_kl_prefill(adesc, idesc, q, k, idx_q, cmp_k, q_pos0, kl, workspace, stream=None):
+    """q [n_q, Hq, D]; k [kv_len, Hkv, D]; idx_q [n_q, 8, 64]; cmp_k [blocks, 64]; kl float32 [n_q]."""
+    n_q = q.shape[0]
+    ws = _ptr(workspace)
+    nbytes = workspace.numel() * workspace.element_size()
+    if kl.dtype != torch.float32:
+        raise TypeError("kl must be float32")
+    _check(_lib.qsa_distill_kl_prefill(ctypes.byref(adesc), ctypes.byref(idesc), _bf16(q, "q"), _bf16(k, "k"),
+                                       _bf16(idx_q, "idx_q"), _bf16(cmp_k, "cmp_k"), q_pos0, n_q, k.shape[0],
+                                       _ptr(kl), ws, nbytes, _stream(stream)))
 
 
 def qsa_sparse_attn_workspace_size(desc, batch, n_q, top_k_blocks, block_size):

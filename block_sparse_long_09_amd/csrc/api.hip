@@ -391,4 +391,37 @@ qsa_status_t qsa_sparse_attn_prefill_paged(const qsa_attn_desc_t* desc, int32_t 
                     "sparse_attn_prefill_paged launch");
 }
 
+size_t qsa_distill_kl_workspace_size(const qsa_attn_desc_t* adesc, int32_t n_q) {
+  if (check_attn_desc(adesc) != QSA_OK || n_q < 0) return 0;
+  return (size_t)n_q * adesc->n_q_heads * sizeof(float);
+}
+
+qsa_status_t qsa_distill_kl_prefill(const qsa_attn_desc_t* adesc, const qsa_index_desc_t* idesc,
+                                    const uint16_t* q, const uint16_t* k, const uint16_t* idx_q,
+                                    const uint16_t* cmp_k, int64_t q_pos0, int32_t n_q, int64_t kv_len,
+                                    float* kl, void* workspace, size_t workspace_bytes, void* stream) {
+  qsa_status_t s = check_attn_desc(adesc);
+  if (s != QSA_OK) return s;
+  s = check_index_desc(idesc);
+  if (s != QSA_OK) return s;
+  if (adesc->n_q_heads != 8 * adesc->n_kv_heads)
+    return fail(QSA_ERR_UNSUPPORTED, "distillation loss needs 8 query heads per KV head");
+  if (idesc->n_idx_heads != 8) return fail(QSA_ERR_UNSUPPORTED, "distillation loss needs 8 indexer heads");
+  if (q_pos0 < 0 || n_q < 0 || kv_len < q_pos0 + n_q || kv_len > kMaxPos)
+    return fail(QSA_ERR_INVALID_ARGUMENT, "need 0 <= q_pos0, q_pos0 + n_q <= kv_len < 2^31");
+  if (n_q == 0) return ok();
+  if (!q || !k || !idx_q || !cmp_k || !kl) return fail(QSA_ERR_INVALID_ARGUMENT, "NULL pointer argument");
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(idx_q, 16) || !aligned(cmp_k, 16))
+    return fail(QSA_ERR_MISALIGNED, "q/k/idx_q/cmp_k must be 16-byte aligned");
+  if (!aligned(kl, 4)) return fail(QSA_ERR_MISALIGNED, "kl must be 4-byte aligned");
+  const size_t need = (size_t)n_q * adesc->n_q_heads * sizeof(float);
+  if (workspace_bytes < need || !workspace)
+    return fail(QSA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", workspace_bytes, need);
+  if (!aligned(workspace, 16)) return fail(QSA_ERR_MISALIGNED, "workspace must be 16-byte aligned");
+  return hip_status(qsa::launch_distill_kl(q, k, idx_q, cmp_k, q_pos0, n_q, adesc->n_q_heads, adesc->n_kv_heads,
+                                           idesc->block_size, adesc->softmax_scale, idesc->idx_head_weight,
+                                           reinterpret_cast<float*>(workspace), kl, (hipStream_t)stream),
+                    "distill_kl launch");
+}
+
 }  // extern "C"

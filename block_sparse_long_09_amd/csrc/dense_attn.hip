@@ -44,6 +44,9 @@ __device__ __forceinline__ uint2 ld_tr16(const uint16_t* p) {
 }
 }  // namespace
 
+// WITH_O = false computes only the per-row log-sum-exp (no V, no P V): the
+// first pass of the distillation loss.
+template <bool WITH_O>
 __global__ __launch_bounds__(256, 2) void dense_prefill_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     int64_t q_pos0, int n_q, int Hq, int Hkv, int G, float scale_log2, uint16_t* __restrict__ out,
@@ -88,7 +91,7 @@ __global__ __launch_bounds__(256, 2) void dense_prefill_kernel(
       const int row = c >> 4, part = c & 15;
       const int64_t s = min(t0 + row, t_end - 1);
       RK[u] = ld16(kb + s * kv_stride + part * 8);
-      RV[u] = ld16(vb + s * kv_stride + part * 8);
+      if (WITH_O) RV[u] = ld16(vb + s * kv_stride + part * 8);
     }
   };
   auto store_tile = [&](int buf, const u32x4* RK, const u32x4* RV) {
@@ -97,7 +100,7 @@ __global__ __launch_bounds__(256, 2) void dense_prefill_kernel(
       const int c = tid + 256 * u;
       const int row = c >> 4, part = c & 15;
       *reinterpret_cast<u32x4*>(&kt[buf][row * kKPitch + part * 8]) = RK[u];
-      *reinterpret_cast<u32x4*>(&vt[buf][row * kKPitch + part * 8]) = RV[u];
+      if (WITH_O) *reinterpret_cast<u32x4*>(&vt[buf][row * kKPitch + part * 8]) = RV[u];
     }
   };
   // transposed V reads: lane group gr = lane / 16 covers dims +16 (gr % 2) of
@@ -155,18 +158,20 @@ __global__ __launch_bounds__(256, 2) void dense_prefill_kernel(
         const float alpha = up ? exp2f(m_run - m_new) : 1.0f;
         m_run = m_new;
         l_run *= alpha;
-        // alpha of row `col` -> O layout (rows 8(i/4) + 4half + i%4)
-        if (half == 0) alpha_x[wave][col] = alpha;
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
+        if (WITH_O) {
+          // alpha of row `col` -> O layout (rows 8(i/4) + 4half + i%4)
+          if (half == 0) alpha_x[wave][col] = alpha;
+          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+          __builtin_amdgcn_wave_barrier();
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float a = alpha_x[wave][8 * (i >> 2) + 4 * half + (i & 3)];
+          for (int i = 0; i < 16; ++i) {
+            const float a = alpha_x[wave][8 * (i >> 2) + 4 * half + (i & 3)];
 #pragma unroll
-          for (int nt = 0; nt < 4; ++nt) O[nt][i] *= a;
+            for (int nt = 0; nt < 4; ++nt) O[nt][i] *= a;
+          }
+          __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+          __builtin_amdgcn_wave_barrier();
         }
-        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-        __builtin_amdgcn_wave_barrier();
       }
       float psum = 0.0f;
       uint32_t pk[8];
@@ -178,6 +183,7 @@ __global__ __launch_bounds__(256, 2) void dense_prefill_kernel(
         pk[i >> 1] = pack_bf16x2_hw(p0, p1);
       }
       l_run += psum;
+      if (!WITH_O) continue;
       // O += P V: k-step kk holds this lane's tokens i in [8kk, 8kk + 8), i.e.
       // chunk tokens 16kk + 4half + {0..3} and 16kk + 8 + 4half + {0..3}
 #pragma unroll
@@ -195,6 +201,10 @@ __global__ __launch_bounds__(256, 2) void dense_prefill_kernel(
   }
   // finish: row sums over both halves, then O / l in bf16, lse in natural log
   float l_row = l_run + __shfl_xor(l_run, 32);
+  if (!WITH_O) {
+    if (lse && half == 0 && my_valid) lse[(int64_t)my_q * Hq + my_h] = (m_run + log2f(l_row)) * 0.69314718055994531f;
+    return;
+  }
   __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
   __builtin_amdgcn_wave_barrier();
   if (half == 0) alpha_x[wave][col] = 1.0f / l_row;
@@ -222,8 +232,12 @@ hipError_t launch_dense_prefill(const uint16_t* q, const uint16_t* k, const uint
   if (32 % G) return hipErrorInvalidValue;
   const int q_per_wg = kFRows / G;
   const dim3 grid((unsigned)((n_q + q_per_wg - 1) / q_per_wg), (unsigned)Hkv);
-  hipLaunchKernelGGL(dense_prefill_kernel, grid, dim3(256), 0, stream, q, k, v, q_pos0, n_q, Hq, Hkv, G,
-                     scale * 1.4426950408889634f, out, lse);
+  if (out)
+    hipLaunchKernelGGL(dense_prefill_kernel<true>, grid, dim3(256), 0, stream, q, k, v, q_pos0, n_q, Hq, Hkv, G,
+                       scale * 1.4426950408889634f, out, lse);
+  else
+    hipLaunchKernelGGL(dense_prefill_kernel<false>, grid, dim3(256), 0, stream, q, k, v, q_pos0, n_q, Hq, Hkv,
+                       G, scale * 1.4426950408889634f, out, lse);
   return hipGetLastError();
 }
 

@@ -77,4 +77,11 @@ hipError_t launch_dense_prefill(const uint16_t* q, const uint16_t* k, const uint
                                 int n_q, int Hq, int Hkv, float scale, uint16_t* out, float* lse,
                                 hipStream_t stream);
 
+// Forward of the indexer's dense-distillation KL per query (pass 1: the dense
+// kernel's log-sum-exp into lse_ws [n_q][Hq]; pass 2: block masses, scores,
+// loss). Hq = 8 Hkv, 8 indexer heads of dim 64.
+hipError_t launch_distill_kl(const uint16_t* q, const uint16_t* k, const uint16_t* idx_q, const uint16_t* cmp_k,
+                             int64_t q_pos0, int n_q, int Hq, int Hkv, int r, float scale, float w_idx,
+                             float* lse_ws, float* kl, hipStream_t stream);
+
 }  // namespace qsa

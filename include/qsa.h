@@ -191,6 +191,25 @@ qsa_status_t qsa_sparse_attn_prefill_paged(const qsa_attn_desc_t* desc, int32_t 
                                            const int32_t* sel_count, uint16_t* out, float* lse,
                                            void* stream);
 
+/* ---- Training-side forward: the indexer's dense-distillation loss ----
+ * Explainer page, sparse-attention section: in the first training stage only
+ * the indexer learns, pulled towards the full-attention distribution by a KL
+ * divergence. For query t (position q_pos0 + i) with own block b_t:
+ *   P_j = sum over query heads h and tokens s of block j of the dense causal
+ *         softmax a_h(s) over s <= t, renormalised over the candidates j < b_t;
+ *   Q_j = softmax over j < b_t of the indexer score s_j (the qsa_index_topk
+ *         score, used as a logit);
+ *   kl[i] = sum_j P_j (ln P_j - ln Q_j), 0 when b_t = 0.
+ *   q [n_q][Hq][D], k [kv_len][Hkv][D] (q_pos0 + n_q <= kv_len),
+ *   idx_q [n_q][H_i][d_i], cmp_k [blocks][d_i] (at least (q_pos0 + n_q - 1) / r),
+ *   kl [n_q] fp32. Supported: Hq = 8 Hkv, H_i = 8, d_i = 64, D = 128.
+ * Workspace: qsa_distill_kl_workspace_size bytes (the per-row log-sum-exp). */
+size_t qsa_distill_kl_workspace_size(const qsa_attn_desc_t* adesc, int32_t n_q);
+qsa_status_t qsa_distill_kl_prefill(const qsa_attn_desc_t* adesc, const qsa_index_desc_t* idesc,
+                                    const uint16_t* q, const uint16_t* k, const uint16_t* idx_q,
+                                    const uint16_t* cmp_k, int64_t q_pos0, int32_t n_q, int64_t kv_len,
+                                    float* kl, void* workspace, size_t workspace_bytes, void* stream);
+
 const char* qsa_status_string(qsa_status_t status);
 const char* qsa_last_error_message(void);
 int qsa_abi_version(void);
