@@ -129,6 +129,8 @@ def main():
     ap.add_argument("--cpu-sample", type=int, default=256, help="queries in the oracle's timed sample")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="also run one plain device copy of this size (counter calibration runs)")
+    ap.add_argument("--kl", action="store_true",
+                    help="time the indexer's dense-distillation loss forward on the config's prefill instead")
     ap.add_argument("--block-size", type=int, default=0,
                     help="micro-block size r of a variant run (default: the workload's, 4)")
     ap.add_argument("--budget", type=int, default=0,
@@ -150,6 +152,8 @@ def main():
     dev = "cuda"
     if args.config == "c6":
         return run_paged_batch(args, torch, qsa)
+    if args.kl:
+        return run_distill_kl(args, torch, qsa)
     if args.config == "c5":
         Wp, Wd = CONFIGS["c5a"], CONFIGS["c5b"]
     elif args.config == "c3":
@@ -495,6 +499,57 @@ def run_paged_batch(args, torch, qsa):
         "pages_speedup_context": PAGES_SPEEDUP,
         "cpu_baseline": None,
         "sample_parity": None,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def run_distill_kl(args, torch, qsa):
+    """Forward of the indexer's dense-distillation KL over a prefill workload."""
+    from gen.configs import CONFIGS
+    from gen.device import idx_keys_to_device, normal_to_device
+    W = CONFIGS["c2" if args.config == "c5" else args.config]
+    if W.mode != "prefill":
+        print("bench.py: --kl needs a prefill workload (c2, c3 or the default)", file=sys.stderr)
+        sys.exit(2)
+    dev = "cuda"
+    t_setup = time.time()
+    n_q = W.chunk or W.n_q
+    q0 = W.q_pos0 + W.n_q - n_q  # the last chunk: the longest rows
+    K = normal_to_device(W.seed, 2, (W.L, W.Hkv, W.D))
+    Q = normal_to_device(W.seed, 1, (W.n_q, W.Hq, W.D))[W.n_q - n_q:]
+    iq = normal_to_device(W.seed, 4, (W.n_q, W.Hi, W.di))[W.n_q - n_q:]
+    ik = idx_keys_to_device(W.seed, 1, W.L, W.di, W.needle_window, W.r)[0]
+    cmp = torch.zeros((W.n_blk, W.di), dtype=torch.bfloat16, device=dev)
+    qsa.qsa_compress_keys(ik, cmp, W.r, 0, W.n_blk)
+    adesc = qsa.attn_desc(W.Hq, W.Hkv, W.D)
+    idesc = qsa.index_desc(W.r, W.k, W.Hi, W.di)
+    kl = torch.empty(n_q, dtype=torch.float32, device=dev)
+    ws = qsa.workspace(qsa.qsa_distill_kl_workspace_size(adesc, n_q))
+    torch.cuda.synchronize()
+    log(f"setup {time.time() - t_setup:.1f}s")
+    f = lambda: qsa.qsa_distill_kl_prefill(adesc, idesc, Q, K, iq, cmp, q0, kl, ws)
+    for _ in range(args.warmup):
+        f()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        f()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / args.steps
+    t = np.arange(q0, q0 + n_q, dtype=np.int64)
+    # two passes of Q K^T over every (query, token <= t) pair, plus the indexer scores of the candidates
+    flops = 2 * int((t + 1).sum()) * W.Hq * W.D * 2 + int((t // W.r).sum()) * W.Hi * W.di * 2
+    roof = {"bound": "mfma", "achieved": flops / wall / 1e12, "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
+            "traffic": None, "flops_per_launch": flops, "avg_launch_ms": wall * 1e3}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    out = {
+        "metric": METRIC, "value": n_q / wall, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": wall * 1e3, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": W.name + "_distill_kl_forward", "queries": n_q, "first_position": q0,
+                   "context": W.L, "block_size": W.r, "heads_q_kv_idx": [W.Hq, W.Hkv, W.Hi]},
+        "kl_mean": float(kl.mean().item()),
+        "roofline": dict(roof, kernel="distill_kl"), "dense": None, "cpu_baseline": None, "sample_parity": None,
     }
     print(json.dumps(out), flush=True)
 
