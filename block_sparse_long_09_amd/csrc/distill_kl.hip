@@ -117,15 +117,24 @@ __global__ __launch_bounds__(64 * HKV) void distill_kl_kernel(
   __syncthreads();
 
   const uint16_t* kb = k + (int64_t)g * kLD + 8 * half;
+  // the K fragments of the next sub-chunk of 32 tokens are in flight while the
+  // current one is reduced (sub-chunks run on across block groups)
+  u32x4 Kn[8];
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) Kn[ks] = ld16(kb + min((int64_t)col, t_last) * HKV * kLD + 16 * ks);
   for (int64_t jb = 0; jb < bt_last; jb += 32) {
     // masses of blocks [jb, jb + 32): r sub-chunks of 32 tokens
     for (int u = 0; u < r; ++u) {
       const int64_t c0 = jb * r + 32 * u;
       if (c0 > t_last) break;
-      const int64_t tok = min(c0 + col, t_last);
       u32x4 Kb[8];
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) Kb[ks] = ld16(kb + tok * HKV * kLD + 16 * ks);
+      for (int ks = 0; ks < 8; ++ks) Kb[ks] = Kn[ks];
+      if (c0 + 32 <= t_last) {
+        const int64_t tok = min(c0 + 32 + col, t_last);
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) Kn[ks] = ld16(kb + tok * HKV * kLD + 16 * ks);
+      }
 #pragma unroll
       for (int T = 0; T < 2; ++T) {
         f32x16 S = f32x16{};
