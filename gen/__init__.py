@@ -18,6 +18,8 @@ _lib = None
 
 # Stream ids of the tensors of one workload.
 STREAM_Q, STREAM_K, STREAM_V, STREAM_IDX_Q, STREAM_IDX_K = 1, 2, 3, 4, 5
+# Streams of the recurrent-layer (gated delta rule) inputs.
+STREAM_GDN_Q, STREAM_GDN_K, STREAM_GDN_V, STREAM_GDN_A, STREAM_GDN_B, STREAM_GDN_S = 8, 9, 10, 11, 12, 13
 
 
 def build():
@@ -101,3 +103,34 @@ def f32_to_bf16(x):
     u = np.asarray(x, np.float32).view(np.uint32).astype(np.uint64)
     u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
     return u.astype(np.uint16)
+
+
+def _unit_rows(bits):
+    """Rows of bf16 bits scaled to unit L2 norm (in double), rounded back to bf16."""
+    x = bf16_to_f64(bits)
+    x /= np.linalg.norm(x, axis=-1, keepdims=True)
+    return f32_to_bf16(x.astype(np.float32))
+
+
+def gdn_inputs(seed, B, T, Hqk, Hv, dk=128, dv=128, decay_shift=3.0):
+    """Inputs of the gated delta rule for B sequences of T tokens.
+
+    q, k [B, T, Hqk, dk]: normal rows scaled to unit norm (the layer normalises
+    them before the mixing), bf16 bits. v [B, T, Hv, dv]: N(0, 1) bf16 bits.
+    g [B, T, Hv] fp32: log of the decay gate sigmoid(x + decay_shift), x
+    normal (mean decay about 0.95 at the default shift). beta [B, T, Hv] fp32:
+    the write gate sigmoid(y), y normal.
+    """
+    q = _unit_rows(normal(seed, STREAM_GDN_Q, (B, T, Hqk, dk)))
+    k = _unit_rows(normal(seed, STREAM_GDN_K, (B, T, Hqk, dk)))
+    v = normal(seed, STREAM_GDN_V, (B, T, Hv, dv))
+    x = bf16_to_f64(normal(seed, STREAM_GDN_A, (B, T, Hv))) + decay_shift
+    g = (-np.logaddexp(0.0, -x)).astype(np.float32)
+    y = bf16_to_f64(normal(seed, STREAM_GDN_B, (B, T, Hv)))
+    beta = (1.0 / (1.0 + np.exp(-y))).astype(np.float32)
+    return q, k, v, g, beta
+
+
+def gdn_state(seed, B, Hv, dv=128, dk=128, scale=0.25):
+    """An initial recurrent state [B, Hv, dv, dk] fp32: scaled normal values."""
+    return (bf16_to_f64(normal(seed, STREAM_GDN_S, (B, Hv, dv, dk))) * scale).astype(np.float32)

@@ -100,3 +100,30 @@ PAGED = {
                      (131072, 262144, 393216, 524288, 655360, 786432, 917504, 1040384),
                      (2048, 1024, 512, 4096, 256, 1, 1, 2048), 32, 4, 8),
 }
+
+
+@dataclass(frozen=True)
+class GdnWorkload:
+    """A gated-delta-rule layer: B sequences of T tokens (prefill) or one
+    token each on a carried state (decode); Hqk key heads, Hv value heads."""
+    name: str
+    mode: str
+    seed: int
+    batch: int
+    T: int
+    Hqk: int = 16
+    Hv: int = 32
+    dk: int = 128
+    dv: int = 128
+
+    @property
+    def scale(self):
+        return self.dk ** -0.5
+
+
+GDN = {
+    # prefill of one 32K-token sequence through one recurrent layer
+    "g1": GdnWorkload("g1_gdn_prefill_32k", "prefill", 1011, 1, 32768),
+    # one decode step of 64 sequences on carried states
+    "g2": GdnWorkload("g2_gdn_decode_b64", "decode", 1012, 64, 1),
+}

@@ -42,6 +42,7 @@ def lib():
         L.qsa_ref_sparse_attn.argtypes = [vp, vp, vp, i64, i32, i32, i32, i32, f64, i32, i32, vp, vp, vp, vp]
         L.qsa_ref_dense_attn.argtypes = [vp, vp, vp, i64, i32, i32, i32, i32, f64, vp, vp]
         L.qsa_ref_distill_kl.argtypes = [vp, vp, vp, vp, i64, i32, i32, i32, i32, f64, i32, i32, f64, i32, vp]
+        L.qsa_ref_gdn.argtypes = [vp, vp, vp, vp, vp, vp, i64, i32, i32, i32, i32, f64, vp, i32, vp, vp]
         _lib = L
     return _lib
 
@@ -148,3 +149,31 @@ def distill_kl(Q, K, idx_q, blocks, t0, r, w, scale=None):
     lib().qsa_ref_distill_kl(_p(Q), _p(K), _p(idx_q), _p(blocks), t0, nq, Hq, Hkv, D, scale, Hi, di, float(w), r,
                              _p(out))
     return out
+
+
+def gdn(q, k, v, g, beta, scale=None, S0=None, heads=None):
+    """O8: gated delta rule over one sequence, token by token.
+
+    q, k [T, Hqk, dk] and v [T, Hv, dv] bf16 bits; g (log decay), beta [T, Hv]
+    fp32; S0 [Hv, dv, dk] fp32 or None (zero state). Returns (o [T, Hv, dv],
+    S_T [Hv, dv, dk]) in float64; with ``heads`` only those value heads are
+    computed (the other entries are NaN).
+    """
+    q, k, v = _u16(q), _u16(k), _u16(v)
+    T, Hqk, dk = q.shape
+    Hv, dv = v.shape[1], v.shape[2]
+    assert k.shape == q.shape and v.shape[0] == T and Hv % Hqk == 0
+    g = np.ascontiguousarray(g, np.float32)
+    beta = np.ascontiguousarray(beta, np.float32)
+    assert g.shape == (T, Hv) and beta.shape == (T, Hv)
+    scale = 1.0 / math.sqrt(dk) if scale is None else scale
+    heads = np.arange(Hv, dtype=np.int32) if heads is None else np.ascontiguousarray(heads, np.int32)
+    s0 = None
+    if S0 is not None:
+        s0 = np.ascontiguousarray(S0, np.float32)
+        assert s0.shape == (Hv, dv, dk)
+    o = np.full((T, Hv, dv), np.nan)
+    S = np.full((Hv, dv, dk), np.nan)
+    lib().qsa_ref_gdn(_p(q), _p(k), _p(v), _p(g), _p(beta), None if s0 is None else _p(s0), T, Hqk, Hv, dk, dv,
+                      float(scale), _p(heads), len(heads), _p(o), _p(S))
+    return o, S

@@ -33,11 +33,15 @@
  *   O5 attend    exact softmax attention over only those tokens  [NEWS],
  *                [EXPLAINER]; GQA: query head h reads KV head h / (Hq/Hkv).
  *   O6 dense     O5 with every token 0..t: the full attention QSA replaces.
+ *   O7 distill   forward of the indexer's KL loss against the dense
+ *                attention mass per block  [EXPLAINER].
+ *   O8 gdn       the gated delta rule of the recurrent layers between the
+ *                attention layers  [EXPLAINER], [DIGEST].
  *
  * Arithmetic: inputs are bf16 bit patterns widened exactly. O1 follows the
  * fixed fp32 rule (left-to-right fp32 sum, divide by r, round to nearest even
- * bf16) so that the stored block keys are a unique byte pattern. O2, O5 and
- * O6 work in double; O2 rounds each score once to fp32. Every value is
+ * bf16) so that the stored block keys are a unique byte pattern. O2, O5 to
+ * O8 work in double; O2 rounds each score once to fp32. Every value is
  * computed by one thread in a fixed order, so results do not depend on the
  * thread count. Build without -ffast-math and with -ffp-contract=off.
  */
@@ -306,5 +310,57 @@ void qsa_ref_distill_kl(const uint16_t* Q, const uint16_t* K, const uint16_t* id
     free(sc);
     free(mass);
     free(logit);
+  }
+}
+
+/* ---------------------------------------------------------------- O8 ---- */
+/* Gated DeltaNet token mixing, the recurrent layer three of every four layers
+   use. [EXPLAINER] (section on the memory/efficiency trade-off) and [DIGEST]
+   (token-mixing paragraph) describe it: a matrix state holds the compressed
+   prefix; for each token the layer forms the error between the token's value
+   and what the memory already returns for its key, then a decay gate sets
+   how much of the old memory is kept and a write gate how much of the
+   correction is written. The pages give no formula; the reading taken here,
+   per value head h with state S (dv x dk, zero or a given initial state):
+     a_t = exp(g_t)                      decay gate, g_t <= 0 given
+     e_t = v_t - a_t S_{t-1} k_t         error against the decayed memory
+     S_t = a_t S_{t-1} + b_t e_t k_t^T   b_t in [0, 1]: write gate
+     o_t = S_t (scale q_t)
+   q, k are the token's key-head vectors (key head h / (Hv / Hqk)); they
+   arrive already normalised (that happens before the mixing).
+   q, k: [T][Hqk][dk]; v: [T][Hv][dv] bf16; g, beta: [T][Hv] fp32;
+   S0: [Hv][dv][dk] fp32 or NULL; o: [T][Hv][dv], S_out: [Hv][dv][dk] double.
+   Only the value heads listed in heads[0 .. n_heads) are computed. Each row of
+   the state evolves on its own (row i only ever sees v_t[i]), so one thread
+   runs one (head, row) pair over every token, in token order. */
+void qsa_ref_gdn(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* g,
+                 const float* beta, const float* S0, int64_t T, int Hqk, int Hv, int dk, int dv,
+                 double scale, const int32_t* heads, int n_heads, double* o, double* S_out) {
+  const int grp = Hv / Hqk;
+#pragma omp parallel for collapse(2) schedule(dynamic, 4)
+  for (int hi = 0; hi < n_heads; ++hi) {
+    for (int i = 0; i < dv; ++i) {
+      const int h = heads[hi];
+      const int hk = h / grp;
+      double* s = (double*)malloc(sizeof(double) * (size_t)dk);
+      for (int c = 0; c < dk; ++c) s[c] = S0 ? (double)S0[((int64_t)h * dv + i) * dk + c] : 0.0;
+      for (int64_t t = 0; t < T; ++t) {
+        const uint16_t* kt = k + (t * Hqk + hk) * dk;
+        const uint16_t* qt = q + (t * Hqk + hk) * dk;
+        const double a = exp((double)g[t * Hv + h]);
+        const double b = (double)beta[t * Hv + h];
+        double sk = 0.0;
+        for (int c = 0; c < dk; ++c) sk += s[c] * widen(kt[c]);
+        const double e = widen(v[(t * Hv + h) * dv + i]) - a * sk;
+        double sq = 0.0;
+        for (int c = 0; c < dk; ++c) {
+          s[c] = a * s[c] + b * e * widen(kt[c]);
+          sq += s[c] * widen(qt[c]);
+        }
+        o[(t * Hv + h) * dv + i] = scale * sq;
+      }
+      for (int c = 0; c < dk; ++c) S_out[((int64_t)h * dv + i) * dk + c] = s[c];
+      free(s);
+    }
   }
 }

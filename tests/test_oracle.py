@@ -358,3 +358,127 @@ def test_distill_kl_nonnegative_and_depends_on_scores():
     iq2 = gen.f32_to_bf16(gen.bf16_to_f64(iq).astype(np.float32) * 4)
     kl2 = oracle.distill_kl(Q[8:], K, iq2[8:], blocks, 8, r, 1.0 / Hi)
     assert not np.allclose(kl, kl2)
+
+
+# ------------------------------------------------------------------ O8 pins --
+def _gdn_small(seed, T, Hqk, Hv, dk, dv):
+    q, k, v, g, beta = gen.gdn_inputs(seed, 1, T, Hqk, Hv, dk, dv)
+    return q[0], k[0], v[0], g[0], beta[0]
+
+
+def test_gdn_single_token_closed_form():
+    # one token on a zero state: the error is v itself, S = b v k^T and
+    # o = scale * b * (k . q) * v
+    q, k, v, g, beta = _gdn_small(81, 1, 2, 4, 16, 8)
+    o, S = oracle.gdn(q, k, v, g, beta, scale=0.3)
+    for h in range(4):
+        kk, qq, vv, b = widen(k[0, h // 2]), widen(q[0, h // 2]), widen(v[0, h]), float(beta[0, h])
+        assert np.allclose(S[h], b * np.outer(vv, kk), rtol=1e-13, atol=1e-15)
+        assert np.allclose(o[0, h], 0.3 * b * (kk @ qq) * vv, rtol=1e-12, atol=1e-15)
+
+
+def test_gdn_no_write_only_decays():
+    # write gate 0: the state only decays, S_t = exp(g_1 + .. + g_t) S0
+    T, Hqk, Hv, dk, dv = 7, 1, 2, 8, 4
+    q, k, v, g, beta = _gdn_small(82, T, Hqk, Hv, dk, dv)
+    S0 = gen.gdn_state(82, 1, Hv, dv, dk)[0]
+    o, S = oracle.gdn(q, k, v, g, np.zeros_like(beta), scale=0.5, S0=S0)
+    G = np.cumsum(g.astype(np.float64), axis=0)
+    for h in range(Hv):
+        assert np.allclose(S[h], math.exp(G[-1, h]) * S0[h].astype(np.float64), rtol=1e-12)
+        for t in range(T):
+            ref = 0.5 * math.exp(G[t, h]) * (S0[h].astype(np.float64) @ widen(q[t, 0]))
+            assert np.allclose(o[t, h], ref, rtol=1e-11, atol=1e-14)
+
+
+def test_gdn_full_write_of_unit_keys_returns_the_value():
+    # decay 1, write gate 1 and exactly unit keys: every token overwrites what
+    # the memory returns for its key, so reading with q = k gives v back
+    T, dk, dv = 40, 32, 8
+    rng = np.random.default_rng(83)
+    k = np.zeros((T, 1, dk), np.float32)
+    for t in range(T):
+        idx = rng.choice(dk, 16, replace=False)
+        k[t, 0, idx] = rng.choice([-0.25, 0.25], 16)  # 16 * 1/16 = 1 exactly
+    k = bf(k)
+    v = gen.normal(83, 10, (T, 1, dv))
+    o, _ = oracle.gdn(k, k, v, np.zeros((T, 1), np.float32), np.ones((T, 1), np.float32), scale=1.0)
+    assert np.abs(o[:, 0] - widen(v[:, 0])).max() < 1e-12
+
+
+def test_gdn_orthogonal_keys_closed_form():
+    # distinct coordinate keys never interfere: from a zero state
+    # S_T = sum_t b_t (prod_{s > t} a_s) v_t e_{p(t)}^T and
+    # o_t = scale * sum_{s <= t} b_s (prod_{s < u <= t} a_u) q_t[p(s)] v_s
+    T, dk, dv = 12, 16, 6
+    rng = np.random.default_rng(84)
+    perm = rng.permutation(dk)[:T]
+    k = np.zeros((T, 1, dk), np.float32)
+    k[np.arange(T), 0, perm] = 1.0
+    k = bf(k)
+    q = gen.normal(84, 8, (T, 1, dk))
+    v = gen.normal(84, 10, (T, 1, dv))
+    g = (-rng.uniform(0.01, 1.0, (T, 1))).astype(np.float32)
+    beta = rng.uniform(0.0, 1.0, (T, 1)).astype(np.float32)
+    o, S = oracle.gdn(q, k, v, g, beta, scale=0.7)
+    a = np.exp(g[:, 0].astype(np.float64))
+    b = beta[:, 0].astype(np.float64)
+    V, Q = widen(v[:, 0]), widen(q[:, 0])
+    ST = np.zeros((dv, dk))
+    for t in range(T):
+        ST[:, perm[t]] += b[t] * np.prod(a[t + 1:]) * V[t]
+    assert np.allclose(S[0], ST, rtol=1e-12, atol=1e-15)
+    for t in range(T):
+        ref = sum(b[s] * np.prod(a[s + 1:t + 1]) * Q[t, perm[s]] * V[s] for s in range(t + 1))
+        assert np.allclose(o[t, 0], 0.7 * ref, rtol=1e-11, atol=1e-14)
+
+
+def test_gdn_matches_expanded_transition_products():
+    # the recurrence unrolled: with A_t = a_t (I - b_t k_t k_t^T),
+    # S_t = S0 A_1 .. A_t + sum_{s <= t} b_s v_s k_s^T A_{s+1} .. A_t
+    T, Hqk, Hv, dk, dv = 10, 2, 4, 8, 5
+    q, k, v, g, beta = _gdn_small(85, T, Hqk, Hv, dk, dv)
+    S0 = gen.gdn_state(85, 1, Hv, dv, dk)[0]
+    o, S = oracle.gdn(q, k, v, g, beta, scale=0.9, S0=S0)
+    for h in range(Hv):
+        K, Q, V = widen(k[:, h // 2]), widen(q[:, h // 2]), widen(v[:, h])
+        a, b = np.exp(g[:, h].astype(np.float64)), beta[:, h].astype(np.float64)
+        A = [a[t] * (np.eye(dk) - b[t] * np.outer(K[t], K[t])) for t in range(T)]
+        for t in range(T):
+            St = S0[h].astype(np.float64)
+            for u in range(t + 1):
+                St = St @ A[u]
+            for s in range(t + 1):
+                W = b[s] * np.outer(V[s], K[s])
+                for u in range(s + 1, t + 1):
+                    W = W @ A[u]
+                St = St + W
+            assert np.allclose(o[t, h], 0.9 * St @ Q[t], rtol=1e-10, atol=1e-13)
+            if t == T - 1:
+                assert np.allclose(S[h], St, rtol=1e-10, atol=1e-13)
+
+
+def test_gdn_key_head_map_and_state_carry():
+    # value head h reads key head h // (Hv / Hqk): the same as repeating the key
+    # heads; and running [0, T1) then [T1, T) from the carried state is the same
+    # as one run (up to the fp32 rounding of the carried state)
+    T, T1, Hqk, Hv, dk, dv = 30, 13, 2, 6, 16, 8
+    q, k, v, g, beta = _gdn_small(86, T, Hqk, Hv, dk, dv)
+    o, S = oracle.gdn(q, k, v, g, beta)
+    rep = np.repeat(np.arange(Hqk), Hv // Hqk)
+    o2, S2 = oracle.gdn(q[:, rep], k[:, rep], v, g, beta)
+    assert np.array_equal(o, o2) and np.array_equal(S, S2)
+    oa, Sa = oracle.gdn(q[:T1], k[:T1], v[:T1], g[:T1], beta[:T1])
+    ob, Sb = oracle.gdn(q[T1:], k[T1:], v[T1:], g[T1:], beta[T1:], S0=Sa.astype(np.float32))
+    assert np.allclose(oa, o[:T1], rtol=0, atol=0)
+    assert np.allclose(ob, o[T1:], rtol=1e-5, atol=1e-6)
+    assert np.allclose(Sb, S, rtol=1e-5, atol=1e-6)
+
+
+def test_gdn_heads_subset():
+    T, Hqk, Hv, dk, dv = 9, 1, 3, 8, 4
+    q, k, v, g, beta = _gdn_small(87, T, Hqk, Hv, dk, dv)
+    o, S = oracle.gdn(q, k, v, g, beta)
+    o1, S1 = oracle.gdn(q, k, v, g, beta, heads=[2])
+    assert np.array_equal(o1[:, 2], o[:, 2]) and np.isnan(o1[:, :2]).all()
+    assert np.array_equal(S1[2], S[2])
