@@ -34,7 +34,12 @@ class AttnDesc(ctypes.Structure):
     _fields_ = [("n_q_heads", _i32), ("n_kv_heads", _i32), ("head_dim", _i32), ("softmax_scale", _f32)]
 
 
-_PI, _PA = ctypes.POINTER(IndexDesc), ctypes.POINTER(AttnDesc)
+class GdnDesc(ctypes.Structure):
+    _fields_ = [("n_qk_heads", _i32), ("n_v_heads", _i32), ("key_dim", _i32), ("value_dim", _i32),
+                ("scale", _f32)]
+
+
+_PI, _PA, _PG = ctypes.POINTER(IndexDesc), ctypes.POINTER(AttnDesc), ctypes.POINTER(GdnDesc)
 
 
 def _sig(name, res, args):
@@ -62,6 +67,9 @@ _sig("qsa_sparse_attn_prefill_paged", ctypes.c_int,
      [_PA, _i32, _i32, _vp, _vp, _vp, _i32, _i64, _vp, _i32, _vp, _vp, _i32, _i32, _vp, _vp, _vp, _vp, _vp])
 _sig("qsa_distill_kl_workspace_size", _sz, [_PA, _i32])
 _sig("qsa_distill_kl_prefill", ctypes.c_int, [_PA, _PI, _vp, _vp, _vp, _vp, _i64, _i32, _i64, _vp, _vp, _sz, _vp])
+_sig("qsa_gdn_prefill_workspace_size", _sz, [_PG, _i32, _i64])
+_sig("qsa_gdn_prefill", ctypes.c_int, [_PG, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i64, _vp, _vp, _vp, _sz, _vp])
+_sig("qsa_gdn_decode", ctypes.c_int, [_PG, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp])
 _sig("qsa_status_string", ctypes.c_char_p, [ctypes.c_int])
 _sig("qsa_last_error_message", ctypes.c_char_p, [])
 _sig("qsa_abi_version", ctypes.c_int, [])
@@ -74,6 +82,7 @@ EXPORTS = (
     "qsa_dense_attn_workspace_size", "qsa_dense_attn_prefill", "qsa_dense_attn_decode",
     "qsa_index_topk_varlen_workspace_size", "qsa_index_topk_varlen", "qsa_sparse_attn_prefill_paged",
     "qsa_distill_kl_workspace_size", "qsa_distill_kl_prefill",
+    "qsa_gdn_prefill_workspace_size", "qsa_gdn_prefill", "qsa_gdn_decode",
 )
 
 
@@ -277,3 +286,39 @@ def workspace(nbytes, device="cuda"):
 
 def softmax_scale(head_dim=128):
     return 1.0 / math.sqrt(head_dim)
+
+
+def gdn_desc(n_qk_heads, n_v_heads, key_dim=128, value_dim=128, scale=None):
+    s = key_dim ** -0.5 if scale is None else scale
+    return GdnDesc(n_qk_heads, n_v_heads, key_dim, value_dim, s)
+
+
+def _f32t(t, name):
+    if t is None:
+        return None
+    if t.dtype != torch.float32:
+        raise TypeError(f"{name} must be float32")
+    return _ptr(t)
+
+
+def qsa_gdn_prefill_workspace_size(desc, batch, seq_len):
+    return _lib.qsa_gdn_prefill_workspace_size(ctypes.byref(desc), batch, seq_len)
+
+
+def qsa_gdn_prefill(desc, q, k, v, g, beta, out, initial_state=None, final_state=None, workspace=None,
+                    stream=None):
+    """q, k [B, T, Hqk, dk]; v, out [B, T, Hv, dv] bf16; g, beta [B, T, Hv] fp32;
+    states [B, Hv, dv, dk] fp32 (optional)."""
+    B, T = v.shape[0], v.shape[1]
+    ws = _ptr(workspace) if workspace is not None and workspace.numel() else None
+    nbytes = workspace.numel() * workspace.element_size() if ws else 0
+    _check(_lib.qsa_gdn_prefill(ctypes.byref(desc), _bf16(q, "q"), _bf16(k, "k"), _bf16(v, "v"), _f32t(g, "g"),
+                                _f32t(beta, "beta"), _f32t(initial_state, "initial_state"), B, T,
+                                _bf16(out, "out"), _f32t(final_state, "final_state"), ws, nbytes, _stream(stream)))
+
+
+def qsa_gdn_decode(desc, q, k, v, g, beta, state, out, stream=None):
+    """q, k [B, Hqk, dk]; v, out [B, Hv, dv] bf16; g, beta [B, Hv] fp32; state [B, Hv, dv, dk] fp32 (in place)."""
+    _check(_lib.qsa_gdn_decode(ctypes.byref(desc), _bf16(q, "q"), _bf16(k, "k"), _bf16(v, "v"), _f32t(g, "g"),
+                               _f32t(beta, "beta"), _f32t(state, "state"), v.shape[0], _bf16(out, "out"),
+                               _stream(stream)))

@@ -15,7 +15,7 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libqsa.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["api.hip", "compress.hip", "index_topk.hip", "sparse_attn.hip", "dense_attn.hip", "distill_kl.hip"]
+SOURCES = ["api.hip", "compress.hip", "index_topk.hip", "sparse_attn.hip", "dense_attn.hip", "distill_kl.hip", "gdn.hip"]
 
 # Packed fp32 VALU ops are turned off (they are not used by hand either).
 FLAGS = [

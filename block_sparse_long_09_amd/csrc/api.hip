@@ -424,4 +424,67 @@ qsa_status_t qsa_distill_kl_prefill(const qsa_attn_desc_t* adesc, const qsa_inde
                     "distill_kl launch");
 }
 
+static qsa_status_t check_gdn_desc(const qsa_gdn_desc_t* d) {
+  if (!d) return fail(QSA_ERR_INVALID_ARGUMENT, "gdn desc is NULL");
+  if (d->key_dim != 128 || d->value_dim != 128)
+    return fail(QSA_ERR_UNSUPPORTED, "key_dim %d / value_dim %d: only 128 is supported", d->key_dim, d->value_dim);
+  if (d->n_qk_heads < 1 || d->n_v_heads < 1 || d->n_v_heads % d->n_qk_heads)
+    return fail(QSA_ERR_INVALID_ARGUMENT, "n_v_heads %d not a positive multiple of n_qk_heads %d", d->n_v_heads,
+                d->n_qk_heads);
+  if (d->n_v_heads > 65535) return fail(QSA_ERR_UNSUPPORTED, "n_v_heads %d > 65535", d->n_v_heads);
+  if (!isfinite(d->scale)) return fail(QSA_ERR_INVALID_ARGUMENT, "scale not finite");
+  return QSA_OK;
+}
+
+size_t qsa_gdn_prefill_workspace_size(const qsa_gdn_desc_t* desc, int32_t batch, int64_t seq_len) {
+  if (check_gdn_desc(desc) != QSA_OK || batch < 0 || seq_len < 0) return 0;
+  return qsa::gdn_workspace_bytes(batch, seq_len, desc->n_v_heads);
+}
+
+qsa_status_t qsa_gdn_prefill(const qsa_gdn_desc_t* desc, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                             const float* g, const float* beta, const float* initial_state, int32_t batch,
+                             int64_t seq_len, uint16_t* out, float* final_state, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  qsa_status_t s = check_gdn_desc(desc);
+  if (s != QSA_OK) return s;
+  if (batch < 0 || seq_len < 0) return fail(QSA_ERR_INVALID_ARGUMENT, "negative batch or seq_len");
+  if (batch > 65535) return fail(QSA_ERR_UNSUPPORTED, "batch %d > 65535", batch);
+  if (seq_len > ((int64_t)1 << 37)) return fail(QSA_ERR_UNSUPPORTED, "seq_len %lld too large", (long long)seq_len);
+  if (batch == 0) return ok();
+  if (seq_len > 0 && (!q || !k || !v || !g || !beta || !out))
+    return fail(QSA_ERR_INVALID_ARGUMENT, "NULL pointer argument");
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16))
+    return fail(QSA_ERR_MISALIGNED, "q/k/v must be 16-byte aligned");
+  if (!aligned(g, 4) || !aligned(beta, 4) || !aligned(out, 2) || !aligned(initial_state, 4) ||
+      !aligned(final_state, 4))
+    return fail(QSA_ERR_MISALIGNED, "g/beta/states must be 4-byte and out 2-byte aligned");
+  const size_t need = qsa::gdn_workspace_bytes(batch, seq_len, desc->n_v_heads);
+  if (need > 0 && (workspace_bytes < need || !workspace))
+    return fail(QSA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", workspace_bytes, need);
+  if (!aligned(workspace, 16)) return fail(QSA_ERR_MISALIGNED, "workspace must be 16-byte aligned");
+  if (seq_len == 0 && !final_state) return ok();
+  return hip_status(qsa::launch_gdn_prefill(q, k, v, g, beta, initial_state, batch, seq_len, desc->n_qk_heads,
+                                            desc->n_v_heads, desc->scale, out, final_state, workspace,
+                                            (hipStream_t)stream),
+                    "gdn prefill launch");
+}
+
+qsa_status_t qsa_gdn_decode(const qsa_gdn_desc_t* desc, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                            const float* g, const float* beta, float* state, int32_t batch, uint16_t* out,
+                            void* stream) {
+  qsa_status_t s = check_gdn_desc(desc);
+  if (s != QSA_OK) return s;
+  if (batch < 0) return fail(QSA_ERR_INVALID_ARGUMENT, "negative batch");
+  if (batch > 65535) return fail(QSA_ERR_UNSUPPORTED, "batch %d > 65535", batch);
+  if (batch == 0) return ok();
+  if (!q || !k || !v || !g || !beta || !state || !out) return fail(QSA_ERR_INVALID_ARGUMENT, "NULL pointer argument");
+  if (!aligned(q, 8) || !aligned(k, 8) || !aligned(v, 2) || !aligned(out, 2))
+    return fail(QSA_ERR_MISALIGNED, "q/k must be 8-byte and v/out 2-byte aligned");
+  if (!aligned(state, 16)) return fail(QSA_ERR_MISALIGNED, "state must be 16-byte aligned");
+  if (!aligned(g, 4) || !aligned(beta, 4)) return fail(QSA_ERR_MISALIGNED, "g/beta must be 4-byte aligned");
+  return hip_status(qsa::launch_gdn_decode(q, k, v, g, beta, batch, desc->n_qk_heads, desc->n_v_heads, desc->scale,
+                                           state, out, (hipStream_t)stream),
+                    "gdn decode launch");
+}
+
 }  // extern "C"

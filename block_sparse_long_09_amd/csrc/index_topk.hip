@@ -761,8 +761,9 @@ __global__ __launch_bounds__(256) void index_select_kernel(
 // LDS and into the score row (kept for the exact fallback). The workgroup then
 // lists, in block order, the split's entries with key >= Ls, where Ls is the
 // lower edge of the histogram bucket holding the split's list_min-th largest
-// key, refined (8 bits per pass, below the bits common to all keys) until at
-// most list_cap entries remain; only when those are all equal to one key is
+// key, refined (8 bits of the offset from the split's smallest key per pass,
+// the offsets' leading zero bits skipped) until at most list_cap entries
+// remain; only when those are all equal to one key is
 // the list cut, in block order. The list goes to list_cap slots with keys
 // shifted by one (0 marks an empty slot); meta = {entries, largest key left
 // out or -1}.

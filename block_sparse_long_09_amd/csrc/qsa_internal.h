@@ -84,4 +84,13 @@ hipError_t launch_distill_kl(const uint16_t* q, const uint16_t* k, const uint16_
                              int64_t q_pos0, int n_q, int Hq, int Hkv, int r, float scale, float w_idx,
                              float* lse_ws, float* kl, hipStream_t stream);
 
+// Gated delta rule (recurrent layers): chunked prefill and one decode step.
+size_t gdn_workspace_bytes(int batch, int64_t T, int Hv);
+hipError_t launch_gdn_prefill(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* g,
+                              const float* beta, const float* S0, int batch, int64_t T, int Hqk, int Hv,
+                              float scale, uint16_t* out, float* S_out, void* ws, hipStream_t stream);
+hipError_t launch_gdn_decode(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* g,
+                             const float* beta, int batch, int Hqk, int Hv, float scale, float* state,
+                             uint16_t* out, hipStream_t stream);
+
 }  // namespace qsa

@@ -210,6 +210,46 @@ qsa_status_t qsa_distill_kl_prefill(const qsa_attn_desc_t* adesc, const qsa_inde
                                     const uint16_t* cmp_k, int64_t q_pos0, int32_t n_q, int64_t kv_len,
                                     float* kl, void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---- Recurrent layers: the gated delta rule ----
+ * Explainer page, section on the memory/efficiency trade-off, and the digest's
+ * token-mixing paragraph: three of every four layers are Gated DeltaNet
+ * layers, which carry a fixed-size matrix state; per token a decay gate sets
+ * how much of the old state is kept and a write gate how much of the error
+ * between the token's value and what the state returns for its key is
+ * written. Per value head h (key head h / (Hv / Hqk)), state S (dv x dk):
+ *   a_t = exp(g_t),  e_t = v_t - a_t S k_t,  S <- a_t S + beta_t e_t k_t^T,
+ *   o_t = S (scale q_t).
+ * q, k are expected already normalised (that happens before the mixing).
+ * Supported: key_dim = value_dim = 128, n_v_heads a multiple of n_qk_heads.
+ * States are fp32 [B][Hv][dv][dk]. */
+typedef struct {
+  int32_t n_qk_heads; /* Hqk: heads of q and k */
+  int32_t n_v_heads;  /* Hv: heads of v, of the output and of the state */
+  int32_t key_dim;    /* dk (128) */
+  int32_t value_dim;  /* dv (128) */
+  float scale;        /* read-out scale on q (e.g. 1/sqrt(dk)) */
+} qsa_gdn_desc_t;
+
+/* Prefill of B sequences of seq_len tokens: q, k [B][T][Hqk][dk], v
+ * [B][T][Hv][dv] bf16 (16-byte aligned); g (log decay, <= 0) and beta (write
+ * gate, in [0, 1]) [B][T][Hv] fp32; initial_state NULL (zero) or [B][Hv][dv][dk];
+ * out [B][T][Hv][dv] bf16; final_state NULL or [B][Hv][dv][dk] (may be the
+ * same buffer as initial_state). Runs in chunks of 64 tokens (per-chunk
+ * factors in the workspace, then one ordered pass per (sequence, head)).
+ * Workspace: qsa_gdn_prefill_workspace_size bytes, 16-byte aligned. */
+size_t qsa_gdn_prefill_workspace_size(const qsa_gdn_desc_t* desc, int32_t batch, int64_t seq_len);
+qsa_status_t qsa_gdn_prefill(const qsa_gdn_desc_t* desc, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                             const float* g, const float* beta, const float* initial_state, int32_t batch,
+                             int64_t seq_len, uint16_t* out, float* final_state, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
+/* One decode step of B sequences: q, k [B][Hqk][dk], v [B][Hv][dv] bf16;
+ * g, beta [B][Hv] fp32; state [B][Hv][dv][dk] fp32 (16-byte aligned), updated
+ * in place; out [B][Hv][dv] bf16. No workspace. */
+qsa_status_t qsa_gdn_decode(const qsa_gdn_desc_t* desc, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                            const float* g, const float* beta, float* state, int32_t batch, uint16_t* out,
+                            void* stream);
+
 const char* qsa_status_string(qsa_status_t status);
 const char* qsa_last_error_message(void);
 int qsa_abi_version(void);

@@ -144,3 +144,35 @@ def test_varlen_and_paged_reject_bad_arguments(qsa):
     assert pg(tab=None) == 1
     assert pg(k=2048) == 2
     assert pg(tq=0) == 0
+
+
+def test_gdn_rejects_bad_arguments(qsa):
+    L = qsa._lib
+    d = qsa.gdn_desc(16, 32)
+    ws = qsa.qsa_gdn_prefill_workspace_size(d, 2, 1000)
+    assert ws > 0 and qsa.qsa_gdn_prefill_workspace_size(d, 2, 2000) > ws
+
+    def pf(desc=d, **kw):
+        a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, b=FAKE, s0=None, B=2, T=1000, out=FAKE, sf=None, ws=FAKE, wsb=ws)
+        a.update(kw)
+        return L.qsa_gdn_prefill(ctypes.byref(desc), a["q"], a["k"], a["v"], a["g"], a["b"], a["s0"], a["B"], a["T"],
+                                 a["out"], a["sf"], a["ws"], a["wsb"], None)
+    assert pf(wsb=ws - 1) == 4
+    assert pf(v=None) == 1
+    assert pf(q=FAKE + 8) == 3
+    assert pf(s0=FAKE + 2) == 3
+    assert pf(T=-1) == 1
+    assert pf(desc=qsa.gdn_desc(16, 24)) == 1      # value heads not a multiple of key heads
+    assert pf(desc=qsa.gdn_desc(16, 32, 64, 64)) == 2
+    assert pf(B=0) == 0
+    assert pf(T=0, q=None, k=None, v=None, g=None, b=None, out=None, ws=None, wsb=0) == 0
+
+    def dc(**kw):
+        a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, b=FAKE, s=FAKE, B=4, out=FAKE)
+        a.update(kw)
+        return L.qsa_gdn_decode(ctypes.byref(d), a["q"], a["k"], a["v"], a["g"], a["b"], a["s"], a["B"], a["out"],
+                                None)
+    assert dc(s=None) == 1
+    assert dc(s=FAKE + 4) == 3
+    assert dc(B=-1) == 1
+    assert dc(B=0) == 0
