@@ -131,6 +131,9 @@ def main():
                     help="also run one plain device copy of this size (counter calibration runs)")
     ap.add_argument("--kl", action="store_true",
                     help="time the indexer's dense-distillation loss forward on the config's prefill instead")
+    ap.add_argument("--gdn", action="store_true",
+                    help="time the recurrent layers' gated delta rule instead: 32K-token prefill of one layer "
+                         "and one decode step of 64 sequences")
     ap.add_argument("--block-size", type=int, default=0,
                     help="micro-block size r of a variant run (default: the workload's, 4)")
     ap.add_argument("--budget", type=int, default=0,
@@ -154,6 +157,8 @@ def main():
         return run_paged_batch(args, torch, qsa)
     if args.kl:
         return run_distill_kl(args, torch, qsa)
+    if args.gdn:
+        return run_gdn(args, torch, qsa)
     if args.config == "c5":
         Wp, Wd = CONFIGS["c5a"], CONFIGS["c5b"]
     elif args.config == "c3":
@@ -552,6 +557,101 @@ def run_distill_kl(args, torch, qsa):
         "roofline": dict(roof, kernel="distill_kl"), "dense": None, "cpu_baseline": None, "sample_parity": None,
     }
     print(json.dumps(out), flush=True)
+
+
+def gdn_work(W):
+    """Algorithmic HBM bytes of one prefill call (inputs read once, outputs
+    written once) and of one decode step (the fp32 state read and written)."""
+    tok = W.batch * W.T
+    prefill = tok * (2 * W.Hqk * W.dk * 2 + W.Hv * W.dv * 2 * 2 + 2 * W.Hv * 4)
+    return {"prefill_bytes": prefill}
+
+
+def run_gdn(args, torch, qsa):
+    import gen
+    from gen.configs import GDN
+    t_setup = time.time()
+    Wp, Wd = GDN["g1"], GDN["g2"]
+    dev = "cuda"
+
+    def up(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    hq, hk, hv, hg, hb = gen.gdn_inputs(Wp.seed, Wp.batch, Wp.T, Wp.Hqk, Wp.Hv, Wp.dk, Wp.dv)
+    q, k, v, g, beta = (up(a) for a in (hq, hk, hv, hg, hb))
+    desc = qsa.gdn_desc(Wp.Hqk, Wp.Hv, Wp.dk, Wp.dv)
+    out = torch.empty((Wp.batch, Wp.T, Wp.Hv, Wp.dv), dtype=torch.bfloat16, device=dev)
+    Sf = torch.empty((Wp.batch, Wp.Hv, Wp.dv, Wp.dk), dtype=torch.float32, device=dev)
+    ws = qsa.workspace(qsa.qsa_gdn_prefill_workspace_size(desc, Wp.batch, Wp.T))
+    # decode: 64 sequences, one token each, on carried states
+    dq, dk_, dv_, dg, db = gen.gdn_inputs(Wd.seed, Wd.batch, 1, Wd.Hqk, Wd.Hv, Wd.dk, Wd.dv)
+    Dq, Dk, Dv, Dg, Db = (up(a[:, 0]) for a in (dq, dk_, dv_, dg, db))
+    state = up(gen.gdn_state(Wd.seed, Wd.batch, Wd.Hv, Wd.dv, Wd.dk))
+    dout = torch.empty((Wd.batch, Wd.Hv, Wd.dv), dtype=torch.bfloat16, device=dev)
+    torch.cuda.synchronize()
+    log(f"setup {time.time() - t_setup:.1f}s")
+    fp = lambda: qsa.qsa_gdn_prefill(desc, q, k, v, g, beta, out, final_state=Sf, workspace=ws)
+    fd = lambda: qsa.qsa_gdn_decode(desc, Dq, Dk, Dv, Dg, Db, state, dout)
+    for _ in range(args.warmup):
+        fp()
+        fd()
+    torch.cuda.synchronize()
+    timer = PhaseTimer(torch, ["prefill", "decode"])
+    evs = []
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        evs.append(timer.run([fp, fd]))
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / args.steps
+    for e in evs:
+        timer.collect(e)
+    ms = timer.mean_ms()
+    work = gdn_work(Wp)
+    dec_bytes = Wd.batch * Wd.Hv * (2 * Wd.dv * Wd.dk * 4 + 2 * Wd.dv * 2) + Wd.batch * Wd.Hqk * Wd.dk * 2 * 2
+    roof_p = {"bound": "hbm", "achieved": work["prefill_bytes"] / (ms["prefill"] * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
+              "unit": "GB/s", "traffic": None, "bytes_per_launch": work["prefill_bytes"],
+              "avg_launch_ms": ms["prefill"]}
+    roof_p["frac"] = roof_p["achieved"] / roof_p["peak"]
+    roof_d = {"bound": "hbm", "achieved": dec_bytes / (ms["decode"] * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
+              "unit": "GB/s", "traffic": None, "bytes_per_launch": dec_bytes, "avg_launch_ms": ms["decode"]}
+    roof_d["frac"] = roof_d["achieved"] / roof_d["peak"]
+    cpu = None
+    sample = None
+    if not args.no_cpu_baseline:
+        import oracle
+        heads = [0, Wp.Hv - 1]
+        log(f"cpu baseline: the oracle over value heads {heads}, all {Wp.T} tokens")
+        tc = time.perf_counter()
+        o_ref, s_ref = oracle.gdn(hq[0], hk[0], hv[0], hg[0], hb[0], heads=heads)
+        el = time.perf_counter() - tc
+        cpu = {"value": Wp.T * len(heads) / Wp.Hv / el, "unit": "tokens/s", "cores": os.cpu_count(),
+               "kind": "oracle",
+               "sample": f"value heads {heads} of {Wp.Hv} over all {Wp.T} tokens of {Wp.name} "
+                         f"({el:.2f}s), scaled to the whole layer"}
+        go = out.float().cpu().numpy().astype(np.float64)
+        gs = Sf.cpu().numpy().astype(np.float64)
+        rel = []
+        for h in heads:
+            e = np.abs(go[0, :, h] - o_ref[:, h])
+            rel.append((e.max() / np.abs(o_ref[:, h]).max(), e.mean() / np.sqrt((o_ref[:, h] ** 2).mean()),
+                        np.abs(gs[0, h] - s_ref[h]).max() / np.sqrt((s_ref[h] ** 2).mean())))
+        sample = {"heads": heads, "out_max_err_rel_max": max(r[0] for r in rel),
+                  "out_mean_err_rel_rms": max(r[1] for r in rel), "state_max_err_rel_rms": max(r[2] for r in rel)}
+    res = {
+        "metric": "GDN (gated delta rule) prefill tokens/s, one layer; decode us/step; % of HBM roofline",
+        "value": Wp.batch * Wp.T / (ms["prefill"] * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": wall * 1e3, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": Wp.name + " + " + Wd.name, "tokens": Wp.T, "heads_qk_v": [Wp.Hqk, Wp.Hv],
+                   "head_dims": [Wp.dk, Wp.dv], "decode_batch": Wd.batch},
+        "prefill_ms": ms["prefill"], "decode_us_per_step": ms["decode"] * 1e3,
+        "roofline": dict(roof_p, kernel="gdn_prefill (prep + scan)"),
+        "rooflines": {"prefill": roof_p, "decode": roof_d},
+        "cpu_baseline": cpu, "sample_parity": sample,
+    }
+    print(json.dumps(res), flush=True)
 
 
 def cpu_baseline(W, P, n_sample):

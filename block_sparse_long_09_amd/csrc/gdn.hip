@@ -8,20 +8,21 @@
 //
 // Prefill runs the chunked form of that recurrence (chunks of C = 64 tokens).
 // Within a chunk with start state S, G_i the running sum of g over the chunk's
-// tokens 0..i and gam_i = exp(G_i), every token's effective write
-// u_j = b_j (v_j - P_j k_j) (P_j the decayed state just before token j)
-// solves the unit lower-triangular system
-//   (I + L) U = diag(b) V - diag(b gam) K S^T,
-//   L_ij = b_i exp(G_i - G_j) k_i . k_j  (j < i),
-// so with T = (I + L)^-1, W = T diag(b gam) K and U~ = T diag(b) V:
-//   U = U~ - W S^T
-//   O = diag(scale gam) Q S^T + M U,  M_ij = scale exp(G_i - G_j) q_i . k_j (j <= i)
-//   S' = gam_C S + (diag(exp(G_C - G_j)) U)^T K.
+// tokens 0..i and gam_i = exp(G_i), the tokens' effective writes
+// u_j = b_j (v_j - P_j k_j) (P_j the decayed state just before token j) solve
+// the unit lower-triangular system (I + L) U = diag(b) R with
+//   L_ij = b_i exp(G_i - G_j) k_i . k_j  (j < i),   R = V - diag(gam) K S^T.
+// With Tb = (I + L)^-1 diag(b):  U = Tb R, and
+//   O  = diag(scale gam) Q S^T + MT R,     MT = M Tb,
+//        M_ij = scale exp(G_i - G_j) q_i . k_j  (j <= i)
+//   S' = gam_C S + R^T Kt,                 Kt = Tb^T diag(exp(G_C - G_j)) K.
 // Every exponent is a difference G_i - G_j with i >= j (or G itself), so no
-// factor exceeds 1. W, U~, M and the gates depend only on the chunk's own
-// tokens: gdn_prep_kernel computes them for all chunks in parallel; then
+// factor exceeds 1. MT, Kt and the gates depend only on the chunk's own
+// tokens: gdn_prep_kernel computes them for every chunk in parallel. Then
 // gdn_scan_kernel walks the chunks of each (sequence, value head) in order,
-// carrying S in registers, with four waves splitting the 128 value rows.
+// carrying S in registers (four waves split the 128 value rows); per chunk it
+// forms X = K S^T and Q S^T, R = V - gam X, O, and the new state: the chain
+// from one state to the next is two products deep.
 // Decode (one token on a carried state) is gdn_decode_kernel: the recurrence
 // itself, one pass over the fp32 state in HBM.
 #include "qsa_device.h"
@@ -34,21 +35,24 @@ constexpr int kC = 64;        // tokens per chunk
 constexpr int kD = 128;       // key and value head dim
 constexpr int kP = kD + 16;   // LDS pitch (elements) of 128-wide bf16 rows
 constexpr int kMP = kC + 8;   // LDS pitch of 64-wide bf16 rows
-constexpr int kTP = kC + 4;   // LDS pitch of 64-wide fp32 rows
+constexpr int kTP = kC + 4;   // LDS pitch of 64-wide fp32 rows (T)
+constexpr int kLP = kC + 8;   // LDS pitch of 64-wide fp32 rows (L)
 
-// Workspace record of one (sequence, value head, chunk), byte offsets.
-constexpr int64_t kRecW = 0;                     // -W, bf16 [64][128], dk order permuted (perm16)
-constexpr int64_t kRecM = kRecW + kC * kD * 2;   // M, bf16 [64][64], column order permuted (perm16)
-constexpr int64_t kRecG = kRecM + kC * kC * 2;   // gates, fp32 [256]: scale gam_i | exp(G_C - G_i) | gam_C
-constexpr int64_t kRecU = kRecG + 256 * 4;       // U~, fp32 [64][128]
-constexpr int64_t kRecBytes = kRecU + kC * kD * 4;
+// Workspace record of one (sequence, value head, chunk), byte offsets. It is
+// the byte image of the scan's LDS staging of these three arrays (row pitches
+// included), so the scan copies it into LDS with direct global-to-LDS loads.
+constexpr int64_t kRecK = 0;                     // Kt, bf16 [64][kP], dk columns in state order
+constexpr int64_t kRecM = kRecK + kC * kP * 2;   // MT, bf16 [64][kMP], columns in accumulator order
+constexpr int64_t kRecG = kRecM + kC * kMP * 2;  // gates, fp32 [256]: scale gam_i | gam_i | gam_C
+constexpr int64_t kRecBytes = kRecG + 256 * 4;   // 28 KB = 7 x 256 threads x 16 B
+static_assert(kRecBytes == 7 * 256 * 16, "record copied in 7 rounds of 16 B per thread");
 
 // Operand order of the k dimension. An MFMA 32x32x16 k-step takes, in lane
 // half h, the eight k indices {4h .. 4h+3, 8+4h .. 8+4h+3} of its sixteen:
 // that is the order in which an accumulator tile holds its rows, so a tile
-// (the state, U) feeds the next product without a transpose. Matrices read as
-// the other operand of such a product (W, M, Q) are stored with the middle
-// two quads of every 16 swapped, which puts each lane's eight values in one
+// (the state, R) feeds the next product without a transpose. A matrix read as
+// the other operand of such a product (MT) is stored with the middle two
+// quads of every 16 swapped, which puts each lane's eight values in one
 // 16-byte run. The map is its own inverse.
 __device__ __forceinline__ int perm16(int x) {
   const int qd = (x >> 2) & 3;
@@ -57,6 +61,8 @@ __device__ __forceinline__ int perm16(int x) {
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) void glb_void;
 
 // ds_read_b64_tr_b16: within each 16-lane group, lane l receives element l % 4
 // of the 4-element chunk addressed by lane 4j + (l % 16) / 4, in slot j.
@@ -80,20 +86,40 @@ __device__ __forceinline__ int tr_offset(int lane) {
   return ((gr >> 1) * 4 + (sl >> 2)) * kP + 16 * (gr & 1) + 4 * (sl & 3);
 }
 
+// Accumulator order of 32 indices for the 16x16x32 MFMA: operand slot p (lane
+// group p / 8, element p % 8) of a packed pair of 16-row accumulator tiles
+// holds accumulator row acc_of_slot(p); slot_of_acc is the inverse.
+__device__ __forceinline__ int acc_of_slot(int p) {
+  const int g = p >> 3, j = p & 7;
+  return j < 4 ? 4 * g + j : 16 + 4 * g + (j - 4);
+}
+__device__ __forceinline__ int slot_of_acc(int x) {
+  return x < 16 ? 8 * (x >> 2) + (x & 3) : 8 * ((x - 16) >> 2) + 4 + (x & 3);
+}
+
+// Pack 8 fp32 accumulator values (slots 8u .. 8u+7 of a tile) as bf16 pairs.
+__device__ __forceinline__ u32x4 pack8(const f32x16& x, int u) {
+  return u32x4{pack_bf16x2_hw(x[8 * u + 0], x[8 * u + 1]), pack_bf16x2_hw(x[8 * u + 2], x[8 * u + 3]),
+               pack_bf16x2_hw(x[8 * u + 4], x[8 * u + 5]), pack_bf16x2_hw(x[8 * u + 6], x[8 * u + 7])};
+}
+
+// Row of accumulator value r (0..15) in a 32-row tile, for lane half `half`.
+__device__ __forceinline__ int acc_row(int r, int half) { return 8 * (r >> 2) + 4 * half + (r & 3); }
+
 // ---------------------------------------------------------------- prep ----
 // One workgroup (4 waves) per (chunk, value head, sequence).
 __global__ __launch_bounds__(256, 2) void gdn_prep_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    const float* __restrict__ g, const float* __restrict__ beta, int64_t T, int Hqk, int Hv, float scale,
-    int n_chunks, uint8_t* __restrict__ ws) {
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[kC * kP];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[kC * kP];
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const float* __restrict__ g,
+    const float* __restrict__ beta, int64_t T, int Hqk, int Hv, float scale, int n_chunks,
+    uint8_t* __restrict__ ws) {
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[kC * kP];   // K tile, natural order
   __shared__ __attribute__((aligned(16))) uint16_t QTs[kC * kP];  // Q tile, then T (fp32 [64][kTP])
-  __shared__ __attribute__((aligned(16))) float Lm[kC * kTP];
+  __shared__ __attribute__((aligned(16))) float Lm[kC * kLP];     // L (fp32), then Tb^T and Td^T (bf16)
+  __shared__ __attribute__((aligned(16))) uint16_t Mb[kC * kMP];  // M (bf16, columns permuted)
   __shared__ float Xs[3][16][17];
   __shared__ __attribute__((aligned(16))) float Gs[kC];
   __shared__ __attribute__((aligned(16))) float Bs[kC];
-  __shared__ __attribute__((aligned(16))) float Fw[kC];
+  __shared__ __attribute__((aligned(16))) float Ds[kC];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
@@ -104,22 +130,22 @@ __global__ __launch_bounds__(256, 2) void gdn_prep_kernel(
   const int n = (int)min<int64_t>(kC, T - t0);
   uint8_t* rec = ws + (((int64_t)b * Hv + h) * n_chunks + c) * kRecBytes;
   float* Tm = reinterpret_cast<float*>(QTs);
+  uint16_t* TbT = reinterpret_cast<uint16_t*>(Lm);  // [64 j][kMP], i permuted: T_ij b_j
+  uint16_t* TdT = TbT + kC * kMP;                   // same times exp(G_C - G_i)
 
-  // tiles of K, Q (key head hk) and V (value head h); rows past the sequence are zero
+  // tiles of K and Q (key head hk); rows past the sequence are zero
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     const int idx = tid + 256 * u;
     const int r = idx >> 4, part = idx & 15;
-    u32x4 kv = u32x4{0u, 0u, 0u, 0u}, qv = kv, vv = kv;
+    u32x4 kv = u32x4{0u, 0u, 0u, 0u}, qv = kv;
     if (r < n) {
       const int64_t tok = (int64_t)b * T + t0 + r;
       kv = ld16(k + (tok * Hqk + hk) * kD + 8 * part);
       qv = ld16(q + (tok * Hqk + hk) * kD + 8 * part);
-      vv = ld16(v + (tok * Hv + h) * kD + 8 * part);
     }
     *reinterpret_cast<u32x4*>(&Ks[r * kP + 8 * part]) = kv;
     *reinterpret_cast<u32x4*>(&QTs[r * kP + 8 * part]) = qv;
-    *reinterpret_cast<u32x4*>(&Vs[r * kP + 8 * part]) = vv;
   }
   if (wave == 0) {
     // running sum of the log decays over the chunk (padding adds 0)
@@ -131,19 +157,19 @@ __global__ __launch_bounds__(256, 2) void gdn_prep_kernel(
       if (lane >= off) x += y;
     }
     const float gl = __shfl(x, 63);
+    const float gam = expf(x);
     Gs[lane] = x;
     Bs[lane] = bt;
-    Fw[lane] = bt * expf(x);
+    Ds[lane] = expf(gl - x);
     float* gates = reinterpret_cast<float*>(rec + kRecG);
-    gates[lane] = scale * expf(x);
-    gates[64 + lane] = expf(gl - x);
+    gates[lane] = scale * gam;
+    gates[64 + lane] = gam;
     gates[128 + lane] = expf(gl);
     gates[192 + lane] = 0.0f;
   }
   __syncthreads();
 
-  // K K^T -> L (fp32, LDS) and Q K^T -> M (bf16, workspace); tiles of 32 x 32
-  uint16_t* Mg = reinterpret_cast<uint16_t*>(rec + kRecM);
+  // K K^T -> L (fp32) and Q K^T -> M (bf16), tiles of 32 x 32 on or below the diagonal
   if (wave < 3) {
     const int ti = wave == 0 ? 0 : 1, tj = wave == 2 ? 1 : 0;
     f32x16 kk = f32x16{}, qk = f32x16{};
@@ -159,18 +185,14 @@ __global__ __launch_bounds__(256, 2) void gdn_prep_kernel(
     const float gj = Gs[j];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int i = 32 * ti + 8 * (r >> 2) + 4 * half + (r & 3);
-      const float d = expf(Gs[i] - gj);  // only read where j <= i
-      Lm[i * kTP + j] = j < i ? Bs[i] * d * kk[r] : 0.0f;
-      const float mv = j <= i ? scale * d * qk[r] : 0.0f;
-      Mg[i * kC + perm16(j)] = (uint16_t)f32_to_bf16_bits(mv);
+      const int i = 32 * ti + acc_row(r, half);
+      const float d = expf(Gs[i] - gj);  // only used where j <= i
+      Lm[i * kLP + j] = j < i ? Bs[i] * d * kk[r] : 0.0f;
+      Mb[i * kMP + perm16(j)] = (uint16_t)f32_to_bf16_bits(j <= i ? scale * d * qk[r] : 0.0f);
     }
   } else {
-    // the tile above the diagonal (rows 0..31, columns 32..63) is zero
-    for (int e = lane; e < 32 * 32; e += 64) {
-      const int i = e >> 5, j = 32 + (e & 31);
-      Mg[i * kC + perm16(j)] = 0;
-    }
+    // the tile above the diagonal (rows 0..31, columns 32..63) of M is zero
+    for (int e = lane; e < 32 * 32; e += 64) Mb[(e >> 5) * kMP + perm16(32 + (e & 31))] = 0;
   }
   __syncthreads();
 
@@ -181,11 +203,11 @@ __global__ __launch_bounds__(256, 2) void gdn_prep_kernel(
     const int a0 = 16 * wave;
     const int cc = lane & 15, part = lane >> 4;
     for (int i = 0; i < 16; ++i) {
-      float s = 0.0f;
-      for (int m = part; m < i; m += 4) s += Lm[(a0 + i) * kTP + a0 + m] * Tm[(a0 + m) * kTP + a0 + cc];
-      s += __shfl_xor(s, 16);
-      s += __shfl_xor(s, 32);
-      if (part == 0) Tm[(a0 + i) * kTP + a0 + cc] = (i == cc ? 1.0f : 0.0f) - s;
+      float sum = 0.0f;
+      for (int m = part; m < i; m += 4) sum += Lm[(a0 + i) * kLP + a0 + m] * Tm[(a0 + m) * kTP + a0 + cc];
+      sum += __shfl_xor(sum, 16);
+      sum += __shfl_xor(sum, 32);
+      if (part == 0) Tm[(a0 + i) * kTP + a0 + cc] = (i == cc ? 1.0f : 0.0f) - sum;
       wave_lds_sync();
     }
   }
@@ -198,7 +220,7 @@ __global__ __launch_bounds__(256, 2) void gdn_prep_kernel(
       const int bb = e >> 8, i = (e >> 4) & 15, cc = e & 15;
       const int a = bb + d;
       float x = 0.0f;
-      for (int m = 16 * bb; m < 16 * a; ++m) x += Lm[(16 * a + i) * kTP + m] * Tm[m * kTP + 16 * bb + cc];
+      for (int m = 16 * bb; m < 16 * a; ++m) x += Lm[(16 * a + i) * kLP + m] * Tm[m * kTP + 16 * bb + cc];
       Xs[bb][i][cc] = x;
     }
     __syncthreads();
@@ -212,266 +234,286 @@ __global__ __launch_bounds__(256, 2) void gdn_prep_kernel(
     }
     __syncthreads();
   }
-  // the blocks above the diagonal of T are zero
+  // Tb = T diag(b) and its copy scaled by the decay to the chunk end, both
+  // transposed (rows j, columns i permuted) in bf16; T is zero above its
+  // diagonal blocks
   for (int e = tid; e < kC * kC; e += 256) {
     const int i = e >> 6, j = e & 63;
-    if ((j >> 4) > (i >> 4)) Tm[i * kTP + j] = 0.0f;
+    const float t = (j >> 4) > (i >> 4) ? 0.0f : Tm[i * kTP + j] * Bs[j];
+    TbT[j * kMP + perm16(i)] = (uint16_t)f32_to_bf16_bits(t);
+    TdT[j * kMP + perm16(i)] = (uint16_t)f32_to_bf16_bits(t * Ds[i]);
   }
   __syncthreads();
 
-  // W = T diag(b gam) K (stored negated) and U~ = T diag(b) V. The A operand
-  // is a row of T scaled per column and rounded once; the B operand is the
-  // token-major K or V tile read transposed. Wave w covers columns 32w..32w+31.
+  // MT = M Tb (wave w: tile (w / 2, w % 2)) and Kt = Td^T K (wave w: columns 32w .. 32w+31)
   {
+    uint16_t* MTg = reinterpret_cast<uint16_t*>(rec + kRecM);
+    const int ti = wave >> 1, tj = wave & 1;
+    f32x16 acc = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const u32x4 am = *reinterpret_cast<const u32x4*>(&Mb[(32 * ti + col) * kMP + 16 * ks + 8 * half]);
+      const u32x4 bt = *reinterpret_cast<const u32x4*>(&TbT[(32 * tj + col) * kMP + 16 * ks + 8 * half]);
+      acc = mfma32x32x16(am, bt, acc);
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int i = 32 * ti + acc_row(r, half);
+      MTg[i * kMP + 32 * tj + slot_of_acc(col)] = (uint16_t)f32_to_bf16_bits(acc[r]);
+    }
+  }
+  {
+    uint16_t* Ktg = reinterpret_cast<uint16_t*>(rec + kRecK);
     const int tro = tr_offset(lane);
-    uint16_t* Wg = reinterpret_cast<uint16_t*>(rec + kRecW);
-    float* Ug = reinterpret_cast<float*>(rec + kRecU);
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt) {
-      f32x16 Wa = f32x16{}, Ua = f32x16{};
+      f32x16 acc = f32x16{};
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
-        const int m0 = 16 * kk + 4 * half;
-        const float* trow = &Tm[(32 * rt + col) * kTP];
-        const f32x4 lo = *reinterpret_cast<const f32x4*>(trow + m0);
-        const f32x4 hi = *reinterpret_cast<const f32x4*>(trow + m0 + 8);
-        const f32x4 fwl = *reinterpret_cast<const f32x4*>(&Fw[m0]);
-        const f32x4 fwh = *reinterpret_cast<const f32x4*>(&Fw[m0 + 8]);
-        const f32x4 fbl = *reinterpret_cast<const f32x4*>(&Bs[m0]);
-        const f32x4 fbh = *reinterpret_cast<const f32x4*>(&Bs[m0 + 8]);
-        const u32x4 aw = u32x4{pack_bf16x2_hw(lo[0] * fwl[0], lo[1] * fwl[1]), pack_bf16x2_hw(lo[2] * fwl[2], lo[3] * fwl[3]),
-                               pack_bf16x2_hw(hi[0] * fwh[0], hi[1] * fwh[1]), pack_bf16x2_hw(hi[2] * fwh[2], hi[3] * fwh[3])};
-        const u32x4 au = u32x4{pack_bf16x2_hw(lo[0] * fbl[0], lo[1] * fbl[1]), pack_bf16x2_hw(lo[2] * fbl[2], lo[3] * fbl[3]),
-                               pack_bf16x2_hw(hi[0] * fbh[0], hi[1] * fbh[1]), pack_bf16x2_hw(hi[2] * fbh[2], hi[3] * fbh[3])};
-        const uint2 kl = ld_tr16(&Ks[(16 * kk) * kP + tro + 32 * wave]);
-        const uint2 kh = ld_tr16(&Ks[(16 * kk + 8) * kP + tro + 32 * wave]);
-        const uint2 vl = ld_tr16(&Vs[(16 * kk) * kP + tro + 32 * wave]);
-        const uint2 vh = ld_tr16(&Vs[(16 * kk + 8) * kP + tro + 32 * wave]);
-        Wa = mfma32x32x16(aw, u32x4{kl.x, kl.y, kh.x, kh.y}, Wa);
-        Ua = mfma32x32x16(au, u32x4{vl.x, vl.y, vh.x, vh.y}, Ua);
+        const u32x4 at = *reinterpret_cast<const u32x4*>(&TdT[(32 * rt + col) * kMP + 16 * kk + 8 * half]);
+        const uint2 lo = ld_tr16(&Ks[(16 * kk) * kP + tro + 32 * wave]);
+        const uint2 hi = ld_tr16(&Ks[(16 * kk + 8) * kP + tro + 32 * wave]);
+        acc = mfma32x32x16(at, u32x4{lo.x, lo.y, hi.x, hi.y}, acc);
       }
-      const int cdk = 32 * wave + col;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int i = 32 * rt + 8 * (r >> 2) + 4 * half + (r & 3);
-        Wg[i * kD + perm16(cdk)] = (uint16_t)f32_to_bf16_bits(-Wa[r]);
-        Ug[i * kD + cdk] = Ua[r];
+        const int j = 32 * rt + acc_row(r, half);
+        Ktg[j * kP + 32 * wave + acc_of_slot(col)] = (uint16_t)f32_to_bf16_bits(acc[r]);
       }
     }
   }
 }
 
 // ---------------------------------------------------------------- scan ----
-// One workgroup per (value head, sequence); wave w carries value rows
-// 32w .. 32w+31 of the state, held transposed (S^T, dk x dv) in four
-// accumulator tiles: tile mt, value r holds S^T[32mt + 8(r/4) + 4half + r%4][32w + lane%32].
-// Per chunk: K, Q, W and M are staged in LDS (double-buffered, the next
-// chunk's loads in flight during the current one), U~ comes straight from the
-// workspace into the accumulator layout.
+// Two workgroups per (value head, sequence), each owning 64 of the 128 value
+// rows; wave w of part p carries rows d0 .. d0+15, d0 = 64p + 16w, of the
+// state, held transposed (S^T, dk x dv) in eight 16 x 16 accumulator tiles of
+// the 16x16x32 MFMA. Lane l of such a tile holds rows 4(l/16) + r, r = 0..3,
+// of column l % 16; a k-step reads, in lane group g = l/16, the eight k
+// indices 8g .. 8g+7. Packing two row-adjacent tiles into an operand
+// therefore gives lane group g rows {4g .. 4g+3, 16+4g .. 16+4g+3}: the
+// "accumulator order" of each 32 indices (acc_of_slot / slot_of_acc below).
+// State row position q holds dk = slot_of_acc(q), so the packed state meets K
+// and Q in their natural dk order; Kt's columns are stored in state order and
+// MT's columns in accumulator order over the tokens, as prep writes them.
+// Per chunk, everything the chunk reads is copied straight from memory into
+// LDS (global-to-LDS loads: 16 bytes per lane, written at consecutive
+// addresses from the wave's base), double-buffered so the next chunk's copies
+// are in flight during the current one. K and Q rows (256 bytes) keep their
+// sixteen 16-byte pieces at piece ^ (row % 16), V rows (this part's 128 bytes)
+// at piece ^ (row % 8), so a piece of 16 consecutive rows spreads over the
+// banks; the record (Kt, MT, gates) is copied as the image prep wrote.
 struct ScanStage {
-  uint16_t K[kC * kP];
-  uint16_t Q[kC * kP];
-  uint16_t W[kC * kP];
-  uint16_t M[kC * kMP];
+  uint16_t K[kC * kD];
+  uint16_t Q[kC * kD];
+  uint16_t V[kC * 64];
+  uint16_t Kt[kC * kP];  // Kt, MT and gates: the workspace record image
+  uint16_t MT[kC * kMP];
   float gates[256];
 };
 
+__device__ __forceinline__ f32x4 mfma16(const u32x4& a, const u32x4& b, const f32x4& c) {
+  return mfma16x16x32(a, b, c);
+}
+
+// Byte offset of 16-byte piece p of row i in a swizzled tile of 256-byte rows.
+__device__ __forceinline__ int swz16(int i, int p) { return i * 256 + (((p ^ i) & 15) << 4); }
+// Same for 128-byte rows.
+__device__ __forceinline__ int swz8(int i, int p) { return i * 128 + (((p ^ i) & 7) << 4); }
+
+__device__ __forceinline__ u32x4 pack_tiles(const f32x4& a, const f32x4& b) {
+  return u32x4{pack_bf16x2_hw(a[0], a[1]), pack_bf16x2_hw(a[2], a[3]), pack_bf16x2_hw(b[0], b[1]),
+               pack_bf16x2_hw(b[2], b[3])};
+}
+
 __global__ __launch_bounds__(256, 1) void gdn_scan_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const float* __restrict__ S0, int64_t T,
-    int Hqk, int Hv, int n_chunks, const uint8_t* __restrict__ ws, uint16_t* __restrict__ out,
-    float* __restrict__ S_out) {
-  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  ScanStage* st = reinterpret_cast<ScanStage*>(smem);
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const float* __restrict__ S0, int64_t T, int Hqk, int Hv, int n_chunks, const uint8_t* __restrict__ ws,
+    uint16_t* __restrict__ out, float* __restrict__ S_out) {
+  // two stages as two separate arrays: the chunk loop is unrolled by two so
+  // that every access names its stage, and the compiler can tell the next
+  // chunk's global-to-LDS copies from the current chunk's reads (one shared
+  // array would make it wait for the copies before the first read)
+  __shared__ __attribute__((aligned(16))) ScanStage st0;
+  __shared__ __attribute__((aligned(16))) ScanStage st1;
+  __shared__ __attribute__((aligned(16))) uint16_t ostage[4][kC * 16];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
-  const int half = lane >> 5, col = lane & 31;
-  const int h = blockIdx.x, b = blockIdx.y;
+  const int grp = lane >> 4, cl = lane & 15;
+  const int part = blockIdx.x & 1, h = blockIdx.x >> 1, b = blockIdx.y;
   const int hk = h / (Hv / Hqk);
-  const int dv = 32 * wave + col;
+  const int d0 = 64 * part + 16 * wave;  // this wave's value rows
+  const int dv = d0 + cl;                // this lane's
   const uint8_t* recs = ws + ((int64_t)b * Hv + h) * n_chunks * kRecBytes;
   const int64_t state_base = ((int64_t)b * Hv + h) * kD * kD;
 
-  f32x16 S[4];
+  // S^T tile mt, value r: state position 16mt + 4grp + r
+  f32x4 S[8];
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt) {
+  for (int mt = 0; mt < 8; ++mt) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int dk = 32 * mt + 8 * (r >> 2) + 4 * half + (r & 3);
-      S[mt][r] = S0 ? S0[state_base + (int64_t)dv * kD + dk] : 0.0f;
+    for (int r = 0; r < 4; ++r) {
+      const int pos = 16 * mt + 4 * grp + r;
+      S[mt][r] = S0 ? S0[state_base + (int64_t)dv * kD + 32 * (pos >> 5) + slot_of_acc(pos & 31)] : 0.0f;
     }
   }
+  // B operand of the identity: adds V (this wave's 16 columns of a 32-column block) to an accumulator
+  u32x4 ident;
+  {
+    const int off = 16 * (wave & 1);
+    uint32_t w[4];
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      const uint32_t lo = (8 * grp + 2 * x == off + cl) ? 0x3F80u : 0u;
+      const uint32_t hi = (8 * grp + 2 * x + 1 == off + cl) ? 0x3F80u : 0u;
+      w[x] = lo | (hi << 16);
+    }
+    ident = u32x4{w[0], w[1], w[2], w[3]};
+  }
 
-  // staging of one chunk: this thread's share of K, Q (16-byte pieces), W, M,
-  // the gates, and this lane's U~ values
-  u32x4 RK[4], RQ[4], RW[4], RM[2], RG;
-  f32x16 RU[2];
-  auto load_chunk = [&](int c) {
+  // row copies: in copy u, wave w fills K/Q rows 16u + 4w .. +3 (lane L: row
+  // 16u + 4w + L/16, stored piece L % 16) and V rows 32u + 8w .. +7 (lane L:
+  // row 32u + 8w + L/8, stored piece L % 8); the source piece does not depend on u
+  const int kq_r = 4 * wave + (lane >> 4);
+  const int v_r = 8 * wave + (lane >> 3);
+  const uint16_t* kq0 = k + (((int64_t)b * T + kq_r) * Hqk + hk) * kD + 8 * ((lane & 15) ^ kq_r);
+  const uint16_t* qq0 = q + (((int64_t)b * T + kq_r) * Hqk + hk) * kD + 8 * ((lane & 15) ^ kq_r);
+  const uint16_t* vv0 = v + (((int64_t)b * T + v_r) * Hv + h) * kD + 64 * part + 8 * ((lane & 7) ^ (v_r & 7));
+  const int64_t kq_row = (int64_t)Hqk * kD, v_row = (int64_t)Hv * kD;
+  auto load_chunk = [&](int c, ScanStage& dst) __attribute__((always_inline)) {
     const int64_t t0 = (int64_t)c * kC;
     const int n = (int)min<int64_t>(kC, T - t0);
     const uint8_t* rec = recs + (int64_t)c * kRecBytes;
+    uint8_t* img = reinterpret_cast<uint8_t*>(dst.Kt);
+#pragma unroll
+    for (int u = 0; u < 7; ++u)
+      __builtin_amdgcn_global_load_lds((glb_void*)(rec + (int64_t)(256 * u + tid) * 16),
+                                       (lds_void*)(img + 4096 * u + 1024 * wave), 16, 0, 0);
+    // rows past the end of the sequence repeat its last row
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const int idx = tid + 256 * u;
-      const int r = idx >> 4, part = idx & 15;
-      RK[u] = u32x4{0u, 0u, 0u, 0u};
-      if (r < n) RK[u] = ld16(k + (((int64_t)b * T + t0 + r) * Hqk + hk) * kD + 8 * part);
-      RW[u] = ld16(rec + kRecW + (int64_t)idx * 16);
+      const int64_t rr = n == kC ? t0 + 16 * u : t0 + min(16 * u + kq_r, n - 1) - kq_r;
+      const int off = 4096 * u + 1024 * wave;
+      __builtin_amdgcn_global_load_lds((glb_void*)(kq0 + rr * kq_row),
+                                       (lds_void*)(reinterpret_cast<uint8_t*>(dst.K) + off), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((glb_void*)(qq0 + rr * kq_row),
+                                       (lds_void*)(reinterpret_cast<uint8_t*>(dst.Q) + off), 16, 0, 0);
     }
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      // Q: 32-byte pieces, stored with the middle quads swapped
-      const int idx = tid + 256 * u;
-      const int r = idx >> 3, pc = idx & 7;
-      RQ[2 * u] = u32x4{0u, 0u, 0u, 0u};
-      RQ[2 * u + 1] = RQ[2 * u];
-      if (r < n) {
-        const uint16_t* src = q + (((int64_t)b * T + t0 + r) * Hqk + hk) * kD + 16 * pc;
-        RQ[2 * u] = ld16(src);
-        RQ[2 * u + 1] = ld16(src + 8);
-      }
-      RM[u] = ld16(rec + kRecM + (int64_t)idx * 16);
-    }
-    RG = tid < 64 ? ld16(rec + kRecG + tid * 16) : u32x4{0u, 0u, 0u, 0u};
-    const float* ug = reinterpret_cast<const float*>(rec + kRecU);
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int i = 32 * rt + 8 * (r >> 2) + 4 * half + (r & 3);
-        RU[rt][r] = ug[i * kD + dv];
-      }
+      const int64_t rr = n == kC ? t0 + 32 * u : t0 + min(32 * u + v_r, n - 1) - v_r;
+      __builtin_amdgcn_global_load_lds((glb_void*)(vv0 + rr * v_row),
+                                       (lds_void*)(reinterpret_cast<uint8_t*>(dst.V) + 4096 * u + 1024 * wave), 16,
+                                       0, 0);
     }
   };
-  auto store_chunk = [&](ScanStage& s) {
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int idx = tid + 256 * u;
-      const int r = idx >> 4, part = idx & 15;
-      *reinterpret_cast<u32x4*>(&s.K[r * kP + 8 * part]) = RK[u];
-      *reinterpret_cast<u32x4*>(&s.W[r * kP + 8 * part]) = RW[u];
-    }
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int idx = tid + 256 * u;
-      const int r = idx >> 3, pc = idx & 7;
-      const u32x4 a = RQ[2 * u], c2 = RQ[2 * u + 1];
-      *reinterpret_cast<u32x4*>(&s.Q[r * kP + 16 * pc]) = u32x4{a.x, a.y, c2.x, c2.y};
-      *reinterpret_cast<u32x4*>(&s.Q[r * kP + 16 * pc + 8]) = u32x4{a.z, a.w, c2.z, c2.w};
-      const int mr = idx >> 3, mp = idx & 7;
-      *reinterpret_cast<u32x4*>(&s.M[mr * kMP + 8 * mp]) = RM[u];
-    }
-    if (tid < 64) *reinterpret_cast<u32x4*>(&s.gates[4 * tid]) = RG;
-  };
 
-  const int tro = tr_offset(lane);
-  if (n_chunks > 0) {
-    load_chunk(0);
-    store_chunk(st[0]);
-  }
-  f32x16 Ucur[2];
-  for (int c = 0; c < n_chunks; ++c) {
-    const int buf = c & 1;
-    Ucur[0] = RU[0];
-    Ucur[1] = RU[1];
-    __syncthreads();  // buffer `buf` is complete; the other one is no longer read
-    if (c + 1 < n_chunks) load_chunk(c + 1);
-    const ScanStage& s = st[buf];
-
-    // state as the B operand (k = dk, n = dv), bf16
-    u32x4 Sb[8];
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        Sb[2 * mt + u] = u32x4{pack_bf16x2_hw(S[mt][8 * u + 0], S[mt][8 * u + 1]),
-                               pack_bf16x2_hw(S[mt][8 * u + 2], S[mt][8 * u + 3]),
-                               pack_bf16x2_hw(S[mt][8 * u + 4], S[mt][8 * u + 5]),
-                               pack_bf16x2_hw(S[mt][8 * u + 6], S[mt][8 * u + 7])};
-      }
-    }
-    // U = U~ - W S^T and O = diag(scale gam) Q S^T (rows: tokens, columns: dv)
-    f32x16 U[2], O[2];
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt) {
-      U[rt] = Ucur[rt];
-      O[rt] = f32x16{};
-#pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-        const u32x4 aw = *reinterpret_cast<const u32x4*>(&s.W[(32 * rt + col) * kP + 16 * ks + 8 * half]);
-        const u32x4 aq = *reinterpret_cast<const u32x4*>(&s.Q[(32 * rt + col) * kP + 16 * ks + 8 * half]);
-        U[rt] = mfma32x32x16(aw, Sb[ks], U[rt]);
-        O[rt] = mfma32x32x16(aq, Sb[ks], O[rt]);
-      }
-    }
-    // U as the B operand (k = token, n = dv); then its decayed copy for the state
-    u32x4 Ub[4], Uh[4];
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int i = 32 * rt + 8 * (r >> 2) + 4 * half + (r & 3);
-        O[rt][r] *= s.gates[i];
-      }
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        float dec[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int r = 8 * u + j;
-          dec[j] = s.gates[64 + 32 * rt + 8 * (r >> 2) + 4 * half + (r & 3)];
-        }
-        const f32x16& x = U[rt];
-        Ub[2 * rt + u] = u32x4{pack_bf16x2_hw(x[8 * u + 0], x[8 * u + 1]), pack_bf16x2_hw(x[8 * u + 2], x[8 * u + 3]),
-                               pack_bf16x2_hw(x[8 * u + 4], x[8 * u + 5]), pack_bf16x2_hw(x[8 * u + 6], x[8 * u + 7])};
-        Uh[2 * rt + u] = u32x4{pack_bf16x2_hw(x[8 * u + 0] * dec[0], x[8 * u + 1] * dec[1]),
-                               pack_bf16x2_hw(x[8 * u + 2] * dec[2], x[8 * u + 3] * dec[3]),
-                               pack_bf16x2_hw(x[8 * u + 4] * dec[4], x[8 * u + 5] * dec[5]),
-                               pack_bf16x2_hw(x[8 * u + 6] * dec[6], x[8 * u + 7] * dec[7])};
-      }
-    }
-    // O += M U
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt) {
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const u32x4 am = *reinterpret_cast<const u32x4*>(&s.M[(32 * rt + col) * kMP + 16 * kk + 8 * half]);
-        O[rt] = mfma32x32x16(am, Ub[kk], O[rt]);
-      }
-    }
-    // S^T = gam_C S^T + K^T Uh (A = K read transposed: row dk, k = token)
-    const float gC = s.gates[128];
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) S[mt][r] *= gC;
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const uint2 lo = ld_tr16(&s.K[(16 * kk) * kP + tro + 32 * mt]);
-        const uint2 hi = ld_tr16(&s.K[(16 * kk + 8) * kP + tro + 32 * mt]);
-        S[mt] = mfma32x32x16(u32x4{lo.x, lo.y, hi.x, hi.y}, Uh[kk], S[mt]);
-      }
-    }
-    // outputs of the chunk
+  // outputs: the wave's 64 x 16 tile goes through its 2 KB of LDS into rows
+  // of 32 bytes, written as 16-byte pieces
+  uint16_t* osw = ostage[wave];
+  uint16_t* out_base = out + ((int64_t)b * T * Hv + h) * kD + d0;
+  auto store_out = [&](int c, const f32x4* O) __attribute__((always_inline)) {
     const int64_t t0 = (int64_t)c * kC;
     const int n = (int)min<int64_t>(kC, T - t0);
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt) {
+    for (int rt = 0; rt < 4; ++rt) {
+      const uint32_t w0 = pack_bf16x2_hw(O[rt][0], O[rt][1]), w1 = pack_bf16x2_hw(O[rt][2], O[rt][3]);
+      const int row = 16 * rt + 4 * grp;
+      osw[(row + 0) * 16 + cl] = (uint16_t)(w0 & 0xFFFFu);
+      osw[(row + 1) * 16 + cl] = (uint16_t)(w0 >> 16);
+      osw[(row + 2) * 16 + cl] = (uint16_t)(w1 & 0xFFFFu);
+      osw[(row + 3) * 16 + cl] = (uint16_t)(w1 >> 16);
+    }
+    wave_lds_sync();
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int i = 32 * rt + 8 * (r >> 2) + 4 * half + (r & 3);
-        if (i < n) out[(((int64_t)b * T + t0 + i) * Hv + h) * kD + dv] = (uint16_t)f32_to_bf16_bits(O[rt][r]);
+    for (int j = 0; j < 2; ++j) {
+      const int id = lane + 64 * j;
+      const int row = id >> 1, hp = id & 1;
+      const u32x4 val = *reinterpret_cast<const u32x4*>(&osw[row * 16 + 8 * hp]);
+      if (n == kC || row < n) *reinterpret_cast<u32x4*>(out_base + (t0 + row) * v_row + 8 * hp) = val;
+    }
+    wave_lds_sync();
+  };
+
+  // transposed reads of Kt (row dk, k = token): lane group g takes tokens
+  // 4g + j of the k-step's first and second 16, column lane % 16 of the window
+  const int tro = (4 * grp + (cl >> 2)) * kP + 4 * (cl & 3);
+  if (n_chunks > 0) load_chunk(0, st0);
+  auto step = [&](int c, const ScanStage& s, ScanStage& nxt) __attribute__((always_inline)) {
+    __syncthreads();  // stage `s` is complete; `nxt` is no longer read
+    if (c + 1 < n_chunks) load_chunk(c + 1, nxt);
+    const uint8_t* sK = reinterpret_cast<const uint8_t*>(s.K);
+    const uint8_t* sQ = reinterpret_cast<const uint8_t*>(s.Q);
+    const uint8_t* sV = reinterpret_cast<const uint8_t*>(s.V);
+
+    // the state as the B operand (k = dk in natural order, n = dv)
+    u32x4 Sb[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) Sb[ks] = pack_tiles(S[2 * ks], S[2 * ks + 1]);
+    // X = K S^T, O = Q S^T and V, tiles of 16 tokens
+    f32x4 X[4], O[4], R[4];
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+      const int row = 16 * rt + cl;
+      X[rt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      O[rt] = X[rt];
+      R[rt] = mfma16(*reinterpret_cast<const u32x4*>(sV + swz8(row, 4 * (wave >> 1) + grp)), ident, X[rt]);
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        X[rt] = mfma16(*reinterpret_cast<const u32x4*>(sK + swz16(row, 4 * ks + grp)), Sb[ks], X[rt]);
+        O[rt] = mfma16(*reinterpret_cast<const u32x4*>(sQ + swz16(row, 4 * ks + grp)), Sb[ks], O[rt]);
       }
     }
-    if (c + 1 < n_chunks) store_chunk(st[buf ^ 1]);
+    // R = V - diag(gam) X as the B operand (k = token in accumulator order)
+    u32x4 Rb[2];
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+      const f32x4 gm = *reinterpret_cast<const f32x4*>(&s.gates[64 + 16 * rt + 4 * grp]);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) R[rt][r] -= gm[r] * X[rt][r];
+    }
+    Rb[0] = pack_tiles(R[0], R[1]);
+    Rb[1] = pack_tiles(R[2], R[3]);
+    // S^T = gam_C S^T + Kt^T R
+    const float gC = s.gates[128];
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) S[mt][r] *= gC;
+    }
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+      for (int mt = 0; mt < 8; ++mt) {
+        const uint2 lo = ld_tr16(&s.Kt[(32 * kk) * kP + tro + 16 * mt]);
+        const uint2 hi = ld_tr16(&s.Kt[(32 * kk + 16) * kP + tro + 16 * mt]);
+        S[mt] = mfma16(u32x4{lo.x, lo.y, hi.x, hi.y}, Rb[kk], S[mt]);
+      }
+    }
+    // O = diag(scale gam) Q S^T + MT R
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+      const f32x4 sg = *reinterpret_cast<const f32x4*>(&s.gates[16 * rt + 4 * grp]);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) O[rt][r] *= sg[r];
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+        O[rt] = mfma16(*reinterpret_cast<const u32x4*>(&s.MT[(16 * rt + cl) * kMP + 32 * kk + 8 * grp]), Rb[kk], O[rt]);
+    }
+    store_out(c, O);
+  };
+  for (int c = 0; c < n_chunks; c += 2) {
+    step(c, st0, st1);
+    if (c + 1 < n_chunks) step(c + 1, st1, st0);
   }
   if (S_out) {
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
+    for (int mt = 0; mt < 8; ++mt) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int dk = 32 * mt + 8 * (r >> 2) + 4 * half + (r & 3);
-        S_out[state_base + (int64_t)dv * kD + dk] = S[mt][r];
+      for (int r = 0; r < 4; ++r) {
+        const int pos = 16 * mt + 4 * grp + r;
+        S_out[state_base + (int64_t)dv * kD + 32 * (pos >> 5) + slot_of_acc(pos & 31)] = S[mt][r];
       }
     }
   }
@@ -537,10 +579,9 @@ hipError_t launch_gdn_prefill(const uint16_t* q, const uint16_t* k, const uint16
                               float scale, uint16_t* out, float* S_out, void* ws, hipStream_t stream) {
   const int64_t n_chunks = (T + kC - 1) / kC;
   if (n_chunks > 0)
-    hipLaunchKernelGGL(gdn_prep_kernel, dim3((unsigned)n_chunks, Hv, batch), dim3(256), 0, stream, q, k, v, g,
-                       beta, T, Hqk, Hv, scale, (int)n_chunks, reinterpret_cast<uint8_t*>(ws));
-  const size_t lds = 2 * sizeof(ScanStage);  // 129 KB of the 160 KB
-  hipLaunchKernelGGL(gdn_scan_kernel, dim3(Hv, batch), dim3(256), lds, stream, q, k, S0, T, Hqk, Hv,
+    hipLaunchKernelGGL(gdn_prep_kernel, dim3((unsigned)n_chunks, Hv, batch), dim3(256), 0, stream, q, k, g, beta,
+                       T, Hqk, Hv, scale, (int)n_chunks, reinterpret_cast<uint8_t*>(ws));
+  hipLaunchKernelGGL(gdn_scan_kernel, dim3(2 * Hv, batch), dim3(256), 0, stream, q, k, v, S0, T, Hqk, Hv,
                      (int)n_chunks, reinterpret_cast<const uint8_t*>(ws), out, S_out);
   return hipGetLastError();
 }
