@@ -761,9 +761,8 @@ __global__ __launch_bounds__(256) void index_select_kernel(
 // LDS and into the score row (kept for the exact fallback). The workgroup then
 // lists, in block order, the split's entries with key >= Ls, where Ls is the
 // lower edge of the histogram bucket holding the split's list_min-th largest
-// key, refined (8 bits of the offset from the split's smallest key per pass,
-// the offsets' leading zero bits skipped) until at most list_cap entries
-// remain; only when those are all equal to one key is
+// key, searched downwards from the largest key (bins of the distance below
+// it, refined 8 bits per pass) until at most list_cap entries remain; only when those are all equal to one key is
 // the list cut, in block order. The list goes to list_cap slots with keys
 // shifted by one (0 marks an empty slot); meta = {entries, largest key left
 // out or -1}.
@@ -845,60 +844,72 @@ __global__ __launch_bounds__(kScanThreads) void index_decode_scan_kernel(
       }
     }
   }
-  // key range of the split
-  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+  // The list threshold is searched downwards from the split's largest key:
+  // a pass counts the keys whose distance below the maximum falls into a
+  // window of 256 bins of 2^s key steps (keys further down are not counted,
+  // so the few keys near the top are all the pass touches), finds the bin
+  // holding the list_min-th largest, and refines inside it 8 bits at a time
+  // until at most list_cap keys lie at or above its lower edge. A first
+  // window too narrow to hold list_min keys is widened 256-fold.
+  uint32_t kmax = 0u;
   __syncthreads();
-  for (int i = tid; i < n; i += NT) {
-    const uint32_t key = __float_as_uint(sc[i]);
-    kmin = min(kmin, key);
-    kmax = max(kmax, key);
-  }
+  for (int i = tid; i < n; i += NT) kmax = max(kmax, __float_as_uint(sc[i]));
 #pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
-    kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, off));
-    kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, off));
-  }
-  if (lane == 0) {
-    red[0][wave] = kmin;
-    red[1][wave] = kmax;
-  }
+  for (int off = 32; off > 0; off >>= 1) kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, off));
+  if (lane == 0) red[1][wave] = kmax;
   __syncthreads();
 #pragma unroll
-  for (int w = 0; w < NW; ++w) {
-    kmin = min(kmin, red[0][w]);
-    kmax = max(kmax, red[1][w]);
-  }
-  uint32_t base = kmin;
-  int hi = range_bits(kmin, kmax);
+  for (int w = 0; w < NW; ++w) kmax = max(kmax, red[1][w]);
   uint32_t need = (uint32_t)min(list_min, n);
   uint32_t above_all = 0, ge = (uint32_t)n;
-  while (hi > 0 && ge > (uint32_t)list_cap) {
-    const int lo = hi > 8 ? hi - 8 : 0;
+  uint32_t Ls = 0u;
+  uint64_t wlo = 0;  // distance of the window's first bin
+  int s = 14;
+  bool done = n <= list_cap;
+  while (!done) {
     if (tid < 256) hist[tid] = 0;
     __syncthreads();
     for (int i = tid; i < n; i += NT) {
-      const int d = range_digit(__float_as_uint(sc[i]), base, hi, lo);
-      if (d >= 0) atomicAdd(&hist[d], 1u);
+      const uint64_t dist = (uint64_t)(kmax - __float_as_uint(sc[i]));
+      if (dist >= wlo) {
+        const uint64_t d = (dist - wlo) >> s;
+        if (d < 256) atomicAdd(&hist[255 - (int)d], 1u);  // larger keys, larger digits
+      }
     }
     __syncthreads();
     if (tid < kWave) {
-      int dig;
-      uint32_t above;
-      wave_find_digit(hist, need, dig, above);
+      const int top = 255 - 4 * lane;
+      uint32_t tot = hist[top] + hist[top - 1] + hist[top - 2] + hist[top - 3];
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) tot += __shfl_xor(tot, off);
+      int dig = 0;
+      uint32_t above = 0;
+      if (tot >= need) wave_find_digit(hist, need, dig, above);
       if (tid == 0) {
         bc[0] = (uint32_t)dig;
         bc[1] = above;
         bc[2] = hist[dig];
+        bc[3] = tot;
       }
     }
     __syncthreads();
-    base += bc[0] << lo;
+    if (bc[3] < need) {  // only the first window can be short
+      s += 8;
+      continue;
+    }
+    const uint64_t db = 255u - bc[0];
     need -= bc[1];
     above_all += bc[1];
     ge = above_all + bc[2];
-    hi = lo;
+    const uint64_t dist_hi = wlo + ((db + 1) << s) - 1;  // the bucket's lowest key
+    Ls = dist_hi >= kmax ? 0u : kmax - (uint32_t)dist_hi;
+    if (ge <= (uint32_t)list_cap || s == 0) {
+      done = true;
+    } else {
+      wlo += db << s;
+      s = s >= 8 ? s - 8 : 0;
+    }
   }
-  const uint32_t Ls = base;
   // all entries >= Ls, or (many equal keys) the first slots' worth of them
   const int take = ge <= (uint32_t)list_cap ? 0x7FFFFFFF : list_cap - (int)above_all;
   const int kept = block_stable_keep<NT>(
@@ -942,7 +953,7 @@ __global__ __launch_bounds__(kMergeThreads) void index_decode_select_kernel(
   __shared__ uint32_t hist[256];
   __shared__ uint32_t bc[2 + 2 * (NT / kWave)];
   __shared__ uint32_t scratch[kSelScratch];
-  __shared__ int s_max, s_total;
+  __shared__ int red_max[NT / kWave], red_tot[NT / kWave];
   extern __shared__ uint2 stage[];
   const int tid = threadIdx.x;
   const int b = blockIdx.x;
@@ -952,22 +963,32 @@ __global__ __launch_bounds__(kMergeThreads) void index_decode_select_kernel(
   const int used = (int)min((int64_t)splits, (bt + kDecodeSplit - 1) / kDecodeSplit);
   const uint2* lb = local + (int64_t)b * splits * list_cap;
   const int2* mb = meta + (int64_t)b * splits;
-  if (tid == 0) {
-    s_max = -1;
-    s_total = 0;
+  // the splits' (count, largest omitted key), reduced per wave then over waves
+  int mx = -1, tot = 0;
+  for (int s2 = tid; s2 < used; s2 += NT) {
+    const int2 m = mb[s2];
+    mx = max(mx, m.y);
+    tot += m.x;
   }
   const int slots = used * list_cap;
 #pragma unroll 8
   for (int i = tid; i < slots; i += NT) stage[i] = lb[i];
-  __syncthreads();
-  for (int s2 = tid; s2 < used; s2 += NT) {
-    const int2 m = mb[s2];
-    atomicMax(&s_max, m.y);
-    atomicAdd(&s_total, m.x);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    mx = max(mx, __shfl_xor(mx, off));
+    tot += __shfl_xor(tot, off);
+  }
+  if ((tid & (kWave - 1)) == 0) {
+    red_max[tid / kWave] = mx;
+    red_tot[tid / kWave] = tot;
   }
   __syncthreads();
-  const int max_omitted = s_max;
-  const int total = s_total;
+  int max_omitted = -1, total = 0;
+#pragma unroll
+  for (int w = 0; w < NT / kWave; ++w) {
+    max_omitted = max(max_omitted, red_max[w]);
+    total += red_tot[w];
+  }
   if (keep > 0) {
     uint32_t tk = 1u;  // shifted: every listed entry
     int need = 0x7FFFFFFF;
