@@ -116,7 +116,7 @@ __global__ __launch_bounds__(256, 2) void gdn_prep_kernel(
   __shared__ __attribute__((aligned(16))) uint16_t QTs[kC * kP];  // Q tile, then T (fp32 [64][kTP])
   __shared__ __attribute__((aligned(16))) float Lm[kC * kLP];     // L (fp32), then Tb^T and Td^T (bf16)
   __shared__ __attribute__((aligned(16))) uint16_t Mb[kC * kMP];  // M (bf16, columns permuted)
-  __shared__ float Xs[3][16][17];
+  __shared__ __attribute__((aligned(16))) float Xs[3][16][16];
   __shared__ __attribute__((aligned(16))) float Gs[kC];
   __shared__ __attribute__((aligned(16))) float Bs[kC];
   __shared__ __attribute__((aligned(16))) float Ds[kC];
@@ -196,43 +196,55 @@ __global__ __launch_bounds__(256, 2) void gdn_prep_kernel(
   }
   __syncthreads();
 
-  // T = (I + L)^-1 in 16 x 16 blocks. Diagonal blocks first, one per wave, by
-  // forward substitution (rows in order, the sum over earlier rows split over
-  // the four 16-lane groups).
-  {
-    const int a0 = 16 * wave;
-    const int cc = lane & 15, part = lane >> 4;
+  // T = (I + L)^-1 in 16 x 16 blocks. The four diagonal blocks by forward
+  // substitution in one wave: lane (a, c) = (lane / 16, lane % 16) keeps
+  // column c of block a in registers, so each row needs only its row of L
+  // (the same for the 16 lanes of a block, read once per row) and no lane
+  // exchange; the entries above the diagonal come out as zeros.
+  if (wave == 0) {
+    const int a0 = 16 * (lane >> 4), cc = lane & 15;
+    float t[16];
+#pragma unroll
     for (int i = 0; i < 16; ++i) {
+      const float* lrow = &Lm[(a0 + i) * kLP + a0];
       float sum = 0.0f;
-      for (int m = part; m < i; m += 4) sum += Lm[(a0 + i) * kLP + a0 + m] * Tm[(a0 + m) * kTP + a0 + cc];
-      sum += __shfl_xor(sum, 16);
-      sum += __shfl_xor(sum, 32);
-      if (part == 0) Tm[(a0 + i) * kTP + a0 + cc] = (i == cc ? 1.0f : 0.0f) - sum;
-      wave_lds_sync();
+#pragma unroll
+      for (int m = 0; m < i; ++m) sum += lrow[m] * t[m];
+      t[i] = (i == cc ? 1.0f : 0.0f) - sum;
     }
+#pragma unroll
+    for (int m = 0; m < 16; ++m) Tm[(a0 + m) * kTP + a0 + cc] = t[m];
   }
   __syncthreads();
   // blocks below the diagonal, by distance d from it:
-  // T_ab = -T_aa X, X = sum_{m in blocks b .. a-1} L_am T_mb  (a = b + d)
-  for (int d = 1; d < 4; ++d) {
-    const int nb = 4 - d;
-    for (int e = tid; e < nb * 256; e += 256) {
-      const int bb = e >> 8, i = (e >> 4) & 15, cc = e & 15;
+  // T_ab = -T_aa X, X = sum_{m in blocks b .. a-1} L_am T_mb  (a = b + d).
+  // Wave w takes block b = w (while b < 4 - d); lane: row i = lane / 4 and
+  // columns 4(lane % 4) .. +3 of the block.
+  {
+    const int bb = wave, i = lane >> 2, c4 = 4 * (lane & 3);
+    for (int d = 1; d < 4; ++d) {
       const int a = bb + d;
-      float x = 0.0f;
-      for (int m = 16 * bb; m < 16 * a; ++m) x += Lm[(16 * a + i) * kLP + m] * Tm[m * kTP + 16 * bb + cc];
-      Xs[bb][i][cc] = x;
-    }
-    __syncthreads();
-    for (int e = tid; e < nb * 256; e += 256) {
-      const int bb = e >> 8, i = (e >> 4) & 15, cc = e & 15;
-      const int a = bb + d;
-      float x = 0.0f;
+      const bool act = a < 4;
+      if (act) {
+        f32x4 x = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        const float* lrow = &Lm[(16 * a + i) * kLP];
+        for (int m = 16 * bb; m < 16 * a; ++m) {
+          const float l = lrow[m];
+          const f32x4 tv = *reinterpret_cast<const f32x4*>(&Tm[m * kTP + 16 * bb + c4]);
+          x += l * tv;
+        }
+        *reinterpret_cast<f32x4*>(&Xs[bb][i][c4]) = x;
+      }
+      __syncthreads();
+      if (act) {
+        f32x4 y = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        const float* trow = &Tm[(16 * a + i) * kTP + 16 * a];
 #pragma unroll
-      for (int m = 0; m < 16; ++m) x += Tm[(16 * a + i) * kTP + 16 * a + m] * Xs[bb][m][cc];
-      Tm[(16 * a + i) * kTP + 16 * bb + cc] = -x;
+        for (int m = 0; m < 16; ++m) y += trow[m] * *reinterpret_cast<const f32x4*>(&Xs[bb][m][c4]);
+        *reinterpret_cast<f32x4*>(&Tm[(16 * a + i) * kTP + 16 * bb + c4]) = -y;
+      }
+      __syncthreads();
     }
-    __syncthreads();
   }
   // Tb = T diag(b) and its copy scaled by the decay to the chunk end, both
   // transposed (rows j, columns i permuted) in bf16; T is zero above its
