@@ -25,6 +25,9 @@
 // from one state to the next is two products deep.
 // Decode (one token on a carried state) is gdn_decode_kernel: the recurrence
 // itself, one pass over the fp32 state in HBM.
+#include <atomic>
+#include <cstddef>
+
 #include "qsa_device.h"
 #include "qsa_internal.h"
 
@@ -60,6 +63,7 @@ __device__ __forceinline__ int perm16(int x) {
 }
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(1))) void glb_void;
@@ -120,6 +124,7 @@ __global__ __launch_bounds__(256, 2) void gdn_prep_kernel(
   __shared__ __attribute__((aligned(16))) float Gs[kC];
   __shared__ __attribute__((aligned(16))) float Bs[kC];
   __shared__ __attribute__((aligned(16))) float Ds[kC];
+  __shared__ __attribute__((aligned(16))) float Rg[256];  // the record's gates
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
@@ -133,6 +138,13 @@ __global__ __launch_bounds__(256, 2) void gdn_prep_kernel(
   uint16_t* TbT = reinterpret_cast<uint16_t*>(Lm);  // [64 j][kMP], i permuted: T_ij b_j
   uint16_t* TdT = TbT + kC * kMP;                   // same times exp(G_C - G_i)
 
+  // this head's log decays and write gates (issued first: their latency
+  // overlaps the tile loads)
+  float gx = 0.0f, bt = 0.0f;
+  if (wave == 0 && lane < n) {
+    gx = g[((int64_t)b * T + t0 + lane) * Hv + h];
+    bt = beta[((int64_t)b * T + t0 + lane) * Hv + h];
+  }
   // tiles of K and Q (key head hk); rows past the sequence are zero
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
@@ -149,8 +161,7 @@ __global__ __launch_bounds__(256, 2) void gdn_prep_kernel(
   }
   if (wave == 0) {
     // running sum of the log decays over the chunk (padding adds 0)
-    float x = lane < n ? g[((int64_t)b * T + t0 + lane) * Hv + h] : 0.0f;
-    const float bt = lane < n ? beta[((int64_t)b * T + t0 + lane) * Hv + h] : 0.0f;
+    float x = gx;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
       const float y = __shfl_up(x, off);
@@ -161,11 +172,10 @@ __global__ __launch_bounds__(256, 2) void gdn_prep_kernel(
     Gs[lane] = x;
     Bs[lane] = bt;
     Ds[lane] = expf(gl - x);
-    float* gates = reinterpret_cast<float*>(rec + kRecG);
-    gates[lane] = scale * gam;
-    gates[64 + lane] = gam;
-    gates[128 + lane] = expf(gl);
-    gates[192 + lane] = 0.0f;
+    Rg[lane] = scale * gam;
+    Rg[64 + lane] = gam;
+    Rg[128 + lane] = expf(gl);
+    Rg[192 + lane] = 0.0f;
   }
   __syncthreads();
 
@@ -257,25 +267,22 @@ __global__ __launch_bounds__(256, 2) void gdn_prep_kernel(
   }
   __syncthreads();
 
-  // MT = M Tb (wave w: tile (w / 2, w % 2)) and Kt = Td^T K (wave w: columns 32w .. 32w+31)
+  // MT = M Tb (wave w: tile (w / 2, w % 2)) and Kt = Td^T K (wave w: columns
+  // 32w .. 32w+31). The record is assembled in LDS in its workspace layout
+  // (Kt over the dead T, MT over M once every wave has read M) and written
+  // out with coalesced 16-byte stores.
+  f32x16 mt = f32x16{};
   {
-    uint16_t* MTg = reinterpret_cast<uint16_t*>(rec + kRecM);
     const int ti = wave >> 1, tj = wave & 1;
-    f32x16 acc = f32x16{};
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       const u32x4 am = *reinterpret_cast<const u32x4*>(&Mb[(32 * ti + col) * kMP + 16 * ks + 8 * half]);
-      const u32x4 bt = *reinterpret_cast<const u32x4*>(&TbT[(32 * tj + col) * kMP + 16 * ks + 8 * half]);
-      acc = mfma32x32x16(am, bt, acc);
-    }
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int i = 32 * ti + acc_row(r, half);
-      MTg[i * kMP + 32 * tj + slot_of_acc(col)] = (uint16_t)f32_to_bf16_bits(acc[r]);
+      const u32x4 bt2 = *reinterpret_cast<const u32x4*>(&TbT[(32 * tj + col) * kMP + 16 * ks + 8 * half]);
+      mt = mfma32x32x16(am, bt2, mt);
     }
   }
   {
-    uint16_t* Ktg = reinterpret_cast<uint16_t*>(rec + kRecK);
+    uint16_t* Ktl = QTs;
     const int tro = tr_offset(lane);
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt) {
@@ -290,38 +297,73 @@ __global__ __launch_bounds__(256, 2) void gdn_prep_kernel(
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int j = 32 * rt + acc_row(r, half);
-        Ktg[j * kP + 32 * wave + acc_of_slot(col)] = (uint16_t)f32_to_bf16_bits(acc[r]);
+        Ktl[j * kP + 32 * wave + acc_of_slot(col)] = (uint16_t)f32_to_bf16_bits(acc[r]);
       }
     }
+  }
+  __syncthreads();
+  {
+    const int ti = wave >> 1, tj = wave & 1;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int i = 32 * ti + acc_row(r, half);
+      Mb[i * kMP + 32 * tj + slot_of_acc(col)] = (uint16_t)f32_to_bf16_bits(mt[r]);
+    }
+  }
+  __syncthreads();
+  static_assert(sizeof(QTs) == kRecM - kRecK && sizeof(Mb) == kRecG - kRecM && sizeof(Rg) == kRecBytes - kRecG,
+                "LDS staging matches the record layout");
+#pragma unroll
+  for (int u = 0; u < 7; ++u) {
+    const int ob = 16 * (tid + 256 * u);
+    const uint8_t* src = ob < kRecM   ? reinterpret_cast<const uint8_t*>(QTs) + ob
+                         : ob < kRecG ? reinterpret_cast<const uint8_t*>(Mb) + (ob - kRecM)
+                                      : reinterpret_cast<const uint8_t*>(Rg) + (ob - kRecG);
+    *reinterpret_cast<u32x4*>(rec + ob) = *reinterpret_cast<const u32x4*>(src);
   }
 }
 
 // ---------------------------------------------------------------- scan ----
-// Two workgroups per (value head, sequence), each owning 64 of the 128 value
-// rows; wave w of part p carries rows d0 .. d0+15, d0 = 64p + 16w, of the
-// state, held transposed (S^T, dk x dv) in eight 16 x 16 accumulator tiles of
-// the 16x16x32 MFMA. Lane l of such a tile holds rows 4(l/16) + r, r = 0..3,
-// of column l % 16; a k-step reads, in lane group g = l/16, the eight k
-// indices 8g .. 8g+7. Packing two row-adjacent tiles into an operand
-// therefore gives lane group g rows {4g .. 4g+3, 16+4g .. 16+4g+3}: the
-// "accumulator order" of each 32 indices (acc_of_slot / slot_of_acc below).
-// State row position q holds dk = slot_of_acc(q), so the packed state meets K
-// and Q in their natural dk order; Kt's columns are stored in state order and
-// MT's columns in accumulator order over the tokens, as prep writes them.
+// Row d of the state only ever meets column d of V and of the outputs, so the
+// 128 value rows of a (sequence, value head) are independent recurrences: they
+// are split over 8 / W workgroups of W waves, and wave w of part p carries
+// rows d0 .. d0+15, d0 = 16 (W p + w). W is chosen per launch so that the grid
+// still covers the chip (one wave per workgroup when sequences x heads are
+// few: each CU then walks one set of rows with its LDS to itself; four when
+// they are many: a chunk's copies then serve four waves). The parts of a head
+// (and neighbouring heads, which share a key head) are given consecutive
+// workgroup slots of one XCD, so the chunk data they all copy is fetched once
+// into that XCD's L2.
+// A wave holds its rows transposed (S^T, dk x 16) in eight 16 x 16
+// accumulator tiles of the 16x16x32 MFMA. Lane l of such a tile holds rows
+// 4(l/16) + r, r = 0..3, of column l % 16; a k-step reads, in lane group
+// g = l/16, the eight k indices 8g .. 8g+7. Packing two row-adjacent tiles
+// into an operand therefore gives lane group g rows {4g .. 4g+3, 16+4g ..
+// 16+4g+3}: the "accumulator order" of each 32 indices (acc_of_slot /
+// slot_of_acc above). State row position q holds dk = slot_of_acc(q), so the
+// packed state meets K and Q in their natural dk order; Kt's columns are
+// stored in state order and MT's columns in accumulator order over the
+// tokens, as prep writes them.
 // Per chunk, everything the chunk reads is copied straight from memory into
 // LDS (global-to-LDS loads: 16 bytes per lane, written at consecutive
 // addresses from the wave's base), double-buffered so the next chunk's copies
 // are in flight during the current one. K and Q rows (256 bytes) keep their
-// sixteen 16-byte pieces at piece ^ (row % 16), V rows (this part's 128 bytes)
-// at piece ^ (row % 8), so a piece of 16 consecutive rows spreads over the
-// banks; the record (Kt, MT, gates) is copied as the image prep wrote.
+// sixteen 16-byte pieces at piece ^ (row % 16), V rows (the staged columns)
+// at piece ^ (row % pieces per row), so a piece of 16 consecutive rows
+// spreads over the banks; the record (Kt, MT, gates) is copied as the image
+// prep wrote.
+template <int W>
 struct ScanStage {
+  // V columns staged: the part's own, and at least the 32-column block that
+  // holds them (one k-step of the MFMA that adds V)
+  static constexpr int kVC = W == 4 ? 64 : 32;
   uint16_t K[kC * kD];
   uint16_t Q[kC * kD];
-  uint16_t V[kC * 64];
+  uint16_t V[kC * kVC];
   uint16_t Kt[kC * kP];  // Kt, MT and gates: the workspace record image
   uint16_t MT[kC * kMP];
   float gates[256];
+  uint32_t sink[64];  // written by the L2 prefetches, never read
 };
 
 __device__ __forceinline__ f32x4 mfma16(const u32x4& a, const u32x4& b, const f32x4& c) {
@@ -330,34 +372,149 @@ __device__ __forceinline__ f32x4 mfma16(const u32x4& a, const u32x4& b, const f3
 
 // Byte offset of 16-byte piece p of row i in a swizzled tile of 256-byte rows.
 __device__ __forceinline__ int swz16(int i, int p) { return i * 256 + (((p ^ i) & 15) << 4); }
-// Same for 128-byte rows.
-__device__ __forceinline__ int swz8(int i, int p) { return i * 128 + (((p ^ i) & 7) << 4); }
+
+// s_waitcnt immediate that waits until at most n (< 64) vector memory
+// operations are outstanding and does not wait on the other counters.
+// Word 3 of a raw buffer resource (32-bit data format, no swizzle).
+constexpr int kBufferFlags = 0x00020000;
+
+constexpr int vmcnt_wait(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
 
 __device__ __forceinline__ u32x4 pack_tiles(const f32x4& a, const f32x4& b) {
   return u32x4{pack_bf16x2_hw(a[0], a[1]), pack_bf16x2_hw(a[2], a[3]), pack_bf16x2_hw(b[0], b[1]),
                pack_bf16x2_hw(b[2], b[3])};
 }
 
-__global__ __launch_bounds__(256, 1) void gdn_scan_kernel(
+template <int W, int NC>
+__global__ __launch_bounds__(64 * (W + NC), 1) void gdn_scan_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const float* __restrict__ S0, int64_t T, int Hqk, int Hv, int n_chunks, const uint8_t* __restrict__ ws,
     uint16_t* __restrict__ out, float* __restrict__ S_out) {
-  // two stages as two separate arrays: the chunk loop is unrolled by two so
-  // that every access names its stage, and the compiler can tell the next
-  // chunk's global-to-LDS copies from the current chunk's reads (one shared
-  // array would make it wait for the copies before the first read)
-  __shared__ __attribute__((aligned(16))) ScanStage st0;
-  __shared__ __attribute__((aligned(16))) ScanStage st1;
-  __shared__ __attribute__((aligned(16))) uint16_t ostage[4][kC * 16];
+  using Stage = ScanStage<W>;
+  constexpr int kVC = Stage::kVC, kVB = 2 * kVC, kVP = kVB / 16;  // V row bytes, 16-byte pieces per row
+  constexpr int kParts = 8 / W;
+  static_assert(offsetof(Stage, MT) - offsetof(Stage, Kt) == kRecM - kRecK &&
+                    offsetof(Stage, gates) - offsetof(Stage, Kt) == kRecG - kRecK,
+                "stage holds the record image");
+  __shared__ __attribute__((aligned(16))) Stage st0;
+  __shared__ __attribute__((aligned(16))) Stage st1;
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
-  const int grp = lane >> 4, cl = lane & 15;
-  const int part = blockIdx.x & 1, h = blockIdx.x >> 1, b = blockIdx.y;
+  // the wave index as a scalar: the copy wave and the compute waves take
+  // different paths, each wave as a whole (their barriers pair up one per chunk)
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  // workgroups are dealt to the eight XCDs in turn: slot L / 8 of XCD L % 8
+  // takes work item (L % 8) (n / 8) + L / 8
+  const int n_wg = (int)gridDim.x, L = (int)blockIdx.x;
+  const int item = n_wg % 8 == 0 ? (L % 8) * (n_wg / 8) + L / 8 : L;
+  const int part = item % kParts, h = (item / kParts) % Hv, b = item / (kParts * Hv);
   const int hk = h / (Hv / Hqk);
-  const int d0 = 64 * part + 16 * wave;  // this wave's value rows
-  const int dv = d0 + cl;                // this lane's
+  const int vbase = kVC * ((16 * W * part) / kVC);  // first staged V column
   const uint8_t* recs = ws + ((int64_t)b * Hv + h) * n_chunks * kRecBytes;
+  const int64_t kq_row = (int64_t)Hqk * kD, v_row = (int64_t)Hv * kD;
+
+  if (wave >= W) {
+    // ---- the copy waves. Copy u of copy wave w fills 1 KB at byte 1024 x,
+    // x = NC u + w, of its array: K/Q rows 4x + lane / 16 (stored piece
+    // lane % 16), V rows x (1024 / kVB) + lane / kVP (stored piece lane % kVP),
+    // record bytes 1024 x + 16 lane; rows past the end of the sequence repeat
+    // its last row.
+    const int cw = wave - W;
+    const uint16_t* kb = k + ((int64_t)b * T * Hqk + hk) * kD;
+    const uint16_t* qb = q + ((int64_t)b * T * Hqk + hk) * kD;
+    const uint16_t* vb = v + ((int64_t)b * T * Hv + h) * kD + vbase;
+    auto load_chunk = [&](int c, Stage& dst) __attribute__((always_inline)) {
+      const int64_t t0 = (int64_t)c * kC;
+      const int n = (int)min<int64_t>(kC, T - t0);
+      const uint8_t* rec = recs + (int64_t)c * kRecBytes;
+      uint8_t* img = reinterpret_cast<uint8_t*>(dst.Kt);
+#pragma unroll
+      for (int u = 0; u < 28 / NC; ++u) {
+        const int x = NC * u + cw;
+        __builtin_amdgcn_global_load_lds((glb_void*)(rec + 1024 * x + 16 * lane), (lds_void*)(img + 1024 * x), 16, 0,
+                                         0);
+      }
+#pragma unroll
+      for (int u = 0; u < 16 / NC; ++u) {
+        const int x = NC * u + cw;
+        const int row = 4 * x + (lane >> 4);
+        const int64_t src = (t0 + min(row, n - 1)) * kq_row + 8 * ((lane & 15) ^ (row & 15));
+        __builtin_amdgcn_global_load_lds((glb_void*)(kb + src),
+                                         (lds_void*)(reinterpret_cast<uint8_t*>(dst.K) + 1024 * x), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((glb_void*)(qb + src),
+                                         (lds_void*)(reinterpret_cast<uint8_t*>(dst.Q) + 1024 * x), 16, 0, 0);
+      }
+#pragma unroll
+      for (int u = 0; u < kC * kVB / 1024 / NC; ++u) {
+        const int x = NC * u + cw;
+        const int row = x * (1024 / kVB) + lane / kVP;
+        const int64_t src = (t0 + min(row, n - 1)) * v_row + 8 * ((lane % kVP) ^ (row % kVP));
+        __builtin_amdgcn_global_load_lds((glb_void*)(vb + src),
+                                         (lds_void*)(reinterpret_cast<uint8_t*>(dst.V) + 1024 * x), 16, 0, 0);
+      }
+    };
+    // L2 prefetch two chunks ahead, shared out over the head's workgroups:
+    // the 128-byte lines they will all copy (the record, whole V rows, K and
+    // Q rows) are dealt round the copy waves of the head's parts, and each
+    // wave touches one word of each of its lines (a stage's sink takes them).
+    // The copies then find the chunk in L2 instead of all missing together.
+    constexpr int kRecLines = (int)(kRecBytes / 128);
+    constexpr int kLines = kRecLines + 2 * kC + 4 * kC;
+    constexpr int kSlices = kParts * NC;
+    constexpr int kPf = (kLines + 64 * kSlices - 1) / (64 * kSlices);  // prefetch loads per copy wave
+    const uint16_t* vrow = v + ((int64_t)b * T * Hv + h) * kD;
+    const int slice = part * NC + cw;
+    auto prefetch_chunk = [&](int c, Stage& sink) __attribute__((always_inline)) {
+      const int64_t t0 = (int64_t)c * kC;
+      const int n = (int)min<int64_t>(kC, T - t0);
+      const uint8_t* rec = recs + (int64_t)c * kRecBytes;
+#pragma unroll
+      for (int i = 0; i < kPf; ++i) {
+        int x = slice + kSlices * (lane + 64 * i);
+        if (x >= kLines) x = slice;  // a line this wave touches anyway
+        const void* src;
+        if (x < kRecLines) {
+          src = rec + 128 * x;
+        } else if (x < kRecLines + 2 * kC) {
+          const int y = x - kRecLines;
+          src = vrow + (t0 + min(y >> 1, n - 1)) * v_row + 64 * (y & 1);
+        } else {
+          const int y = x - kRecLines - 2 * kC;
+          const int row = min((y & (2 * kC - 1)) >> 1, n - 1);
+          src = (y < 2 * kC ? kb : qb) + (t0 + row) * kq_row + 64 * (y & 1);
+        }
+        __builtin_amdgcn_global_load_lds((glb_void*)src, (lds_void*)sink.sink, 4, 0, 0);
+      }
+    };
+    // Vector memory operations complete in issue order: once at most the kPf
+    // prefetches issued after this wave's copies of a chunk are outstanding,
+    // the copies are in LDS, and the barrier hands them to the compute waves
+    // (which by then have finished with the stage the next copies overwrite).
+    auto copy_step = [&](int c, Stage& nxt) __attribute__((always_inline)) {
+      __builtin_amdgcn_s_waitcnt(vmcnt_wait(kPf));
+      __builtin_amdgcn_s_barrier();
+      if (c + 1 < n_chunks) {
+        load_chunk(c + 1, nxt);
+        prefetch_chunk(min(c + 2, n_chunks - 1), nxt);
+      }
+    };
+    if (n_chunks > 0) {
+      load_chunk(0, st0);
+      prefetch_chunk(min(1, n_chunks - 1), st0);
+    }
+    for (int c = 0; c < n_chunks; c += 2) {
+      copy_step(c, st1);
+      if (c + 1 < n_chunks) copy_step(c + 1, st0);
+    }
+    __builtin_amdgcn_s_waitcnt(vmcnt_wait(0));  // no copy into LDS outlives the workgroup
+    return;
+  }
+
+  // ---- the compute waves
+  const int grp = lane >> 4, cl = lane & 15;
+  const int d0 = 16 * (W * part + wave);  // this wave's value rows
+  const int dv = d0 + cl;                 // this lane's
   const int64_t state_base = ((int64_t)b * Hv + h) * kD * kD;
 
   // S^T tile mt, value r: state position 16mt + 4grp + r
@@ -373,7 +530,7 @@ __global__ __launch_bounds__(256, 1) void gdn_scan_kernel(
   // B operand of the identity: adds V (this wave's 16 columns of a 32-column block) to an accumulator
   u32x4 ident;
   {
-    const int off = 16 * (wave & 1);
+    const int off = 16 * ((d0 >> 4) & 1);
     uint32_t w[4];
 #pragma unroll
     for (int x = 0; x < 4; ++x) {
@@ -383,78 +540,32 @@ __global__ __launch_bounds__(256, 1) void gdn_scan_kernel(
     }
     ident = u32x4{w[0], w[1], w[2], w[3]};
   }
+  const int vpiece = 4 * ((d0 - vbase) >> 5) + grp;  // the wave's A-operand piece of a V row
 
-  // row copies: in copy u, wave w fills K/Q rows 16u + 4w .. +3 (lane L: row
-  // 16u + 4w + L/16, stored piece L % 16) and V rows 32u + 8w .. +7 (lane L:
-  // row 32u + 8w + L/8, stored piece L % 8); the source piece does not depend on u
-  const int kq_r = 4 * wave + (lane >> 4);
-  const int v_r = 8 * wave + (lane >> 3);
-  const uint16_t* kq0 = k + (((int64_t)b * T + kq_r) * Hqk + hk) * kD + 8 * ((lane & 15) ^ kq_r);
-  const uint16_t* qq0 = q + (((int64_t)b * T + kq_r) * Hqk + hk) * kD + 8 * ((lane & 15) ^ kq_r);
-  const uint16_t* vv0 = v + (((int64_t)b * T + v_r) * Hv + h) * kD + 64 * part + 8 * ((lane & 7) ^ (v_r & 7));
-  const int64_t kq_row = (int64_t)Hqk * kD, v_row = (int64_t)Hv * kD;
-  auto load_chunk = [&](int c, ScanStage& dst) __attribute__((always_inline)) {
-    const int64_t t0 = (int64_t)c * kC;
-    const int n = (int)min<int64_t>(kC, T - t0);
-    const uint8_t* rec = recs + (int64_t)c * kRecBytes;
-    uint8_t* img = reinterpret_cast<uint8_t*>(dst.Kt);
-#pragma unroll
-    for (int u = 0; u < 7; ++u)
-      __builtin_amdgcn_global_load_lds((glb_void*)(rec + (int64_t)(256 * u + tid) * 16),
-                                       (lds_void*)(img + 4096 * u + 1024 * wave), 16, 0, 0);
-    // rows past the end of the sequence repeat its last row
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int64_t rr = n == kC ? t0 + 16 * u : t0 + min(16 * u + kq_r, n - 1) - kq_r;
-      const int off = 4096 * u + 1024 * wave;
-      __builtin_amdgcn_global_load_lds((glb_void*)(kq0 + rr * kq_row),
-                                       (lds_void*)(reinterpret_cast<uint8_t*>(dst.K) + off), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((glb_void*)(qq0 + rr * kq_row),
-                                       (lds_void*)(reinterpret_cast<uint8_t*>(dst.Q) + off), 16, 0, 0);
-    }
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int64_t rr = n == kC ? t0 + 32 * u : t0 + min(32 * u + v_r, n - 1) - v_r;
-      __builtin_amdgcn_global_load_lds((glb_void*)(vv0 + rr * v_row),
-                                       (lds_void*)(reinterpret_cast<uint8_t*>(dst.V) + 4096 * u + 1024 * wave), 16,
-                                       0, 0);
-    }
-  };
-
-  // outputs: the wave's 64 x 16 tile goes through its 2 KB of LDS into rows
-  // of 32 bytes, written as 16-byte pieces
-  uint16_t* osw = ostage[wave];
+  // outputs: the wave computes O^T, so lane l holds value columns
+  // d0 + 4 (l / 16) .. +3 of token l % 16 of each 16-token tile, stored as 8
+  // bytes; buffer stores whose range ends at the chunk's last token drop the
+  // rest
   uint16_t* out_base = out + ((int64_t)b * T * Hv + h) * kD + d0;
+  const int row_bytes = (int)(v_row * 2);
   auto store_out = [&](int c, const f32x4* O) __attribute__((always_inline)) {
     const int64_t t0 = (int64_t)c * kC;
     const int n = (int)min<int64_t>(kC, T - t0);
+    const __amdgpu_buffer_rsrc_t dst =
+        __builtin_amdgcn_make_buffer_rsrc(out_base + t0 * v_row, 0, (n - 1) * row_bytes + 32, kBufferFlags);
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) {
-      const uint32_t w0 = pack_bf16x2_hw(O[rt][0], O[rt][1]), w1 = pack_bf16x2_hw(O[rt][2], O[rt][3]);
-      const int row = 16 * rt + 4 * grp;
-      osw[(row + 0) * 16 + cl] = (uint16_t)(w0 & 0xFFFFu);
-      osw[(row + 1) * 16 + cl] = (uint16_t)(w0 >> 16);
-      osw[(row + 2) * 16 + cl] = (uint16_t)(w1 & 0xFFFFu);
-      osw[(row + 3) * 16 + cl] = (uint16_t)(w1 >> 16);
+      const u32x2 val = u32x2{pack_bf16x2_hw(O[rt][0], O[rt][1]), pack_bf16x2_hw(O[rt][2], O[rt][3])};
+      __builtin_amdgcn_raw_buffer_store_b64(val, dst, (16 * rt + cl) * row_bytes + 8 * grp, 0, 0);
     }
-    wave_lds_sync();
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int id = lane + 64 * j;
-      const int row = id >> 1, hp = id & 1;
-      const u32x4 val = *reinterpret_cast<const u32x4*>(&osw[row * 16 + 8 * hp]);
-      if (n == kC || row < n) *reinterpret_cast<u32x4*>(out_base + (t0 + row) * v_row + 8 * hp) = val;
-    }
-    wave_lds_sync();
   };
 
   // transposed reads of Kt (row dk, k = token): lane group g takes tokens
   // 4g + j of the k-step's first and second 16, column lane % 16 of the window
   const int tro = (4 * grp + (cl >> 2)) * kP + 4 * (cl & 3);
-  if (n_chunks > 0) load_chunk(0, st0);
-  auto step = [&](int c, const ScanStage& s, ScanStage& nxt) __attribute__((always_inline)) {
-    __syncthreads();  // stage `s` is complete; `nxt` is no longer read
-    if (c + 1 < n_chunks) load_chunk(c + 1, nxt);
+  auto step = [&](int c, const Stage& s) __attribute__((always_inline)) {
+    __builtin_amdgcn_s_barrier();  // chunk c is in `s`
+    asm volatile("" ::: "memory");
     const uint8_t* sK = reinterpret_cast<const uint8_t*>(s.K);
     const uint8_t* sQ = reinterpret_cast<const uint8_t*>(s.Q);
     const uint8_t* sV = reinterpret_cast<const uint8_t*>(s.V);
@@ -463,18 +574,20 @@ __global__ __launch_bounds__(256, 1) void gdn_scan_kernel(
     u32x4 Sb[4];
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) Sb[ks] = pack_tiles(S[2 * ks], S[2 * ks + 1]);
-    // X = K S^T, O = Q S^T and V, tiles of 16 tokens
+    // X = K S^T, O^T = S Q^T (the packed state taken as the A operand, the
+    // same Q fragments as the B operand) and V, tiles of 16 tokens
     f32x4 X[4], O[4], R[4];
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) {
       const int row = 16 * rt + cl;
       X[rt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
       O[rt] = X[rt];
-      R[rt] = mfma16(*reinterpret_cast<const u32x4*>(sV + swz8(row, 4 * (wave >> 1) + grp)), ident, X[rt]);
+      R[rt] = mfma16(*reinterpret_cast<const u32x4*>(sV + row * kVB + (((vpiece ^ row) & (kVP - 1)) << 4)), ident,
+                     X[rt]);
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
         X[rt] = mfma16(*reinterpret_cast<const u32x4*>(sK + swz16(row, 4 * ks + grp)), Sb[ks], X[rt]);
-        O[rt] = mfma16(*reinterpret_cast<const u32x4*>(sQ + swz16(row, 4 * ks + grp)), Sb[ks], O[rt]);
+        O[rt] = mfma16(Sb[ks], *reinterpret_cast<const u32x4*>(sQ + swz16(row, 4 * ks + grp)), O[rt]);
       }
     }
     // R = V - diag(gam) X as the B operand (k = token in accumulator order)
@@ -503,21 +616,22 @@ __global__ __launch_bounds__(256, 1) void gdn_scan_kernel(
         S[mt] = mfma16(u32x4{lo.x, lo.y, hi.x, hi.y}, Rb[kk], S[mt]);
       }
     }
-    // O = diag(scale gam) Q S^T + MT R
+    // O^T = S Q^T diag(scale gam) + R^T MT^T (the packed R as the A operand,
+    // the MT fragments as the B operand)
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) {
-      const f32x4 sg = *reinterpret_cast<const f32x4*>(&s.gates[16 * rt + 4 * grp]);
+      const float sg = s.gates[16 * rt + cl];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) O[rt][r] *= sg[r];
+      for (int r = 0; r < 4; ++r) O[rt][r] *= sg;
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk)
-        O[rt] = mfma16(*reinterpret_cast<const u32x4*>(&s.MT[(16 * rt + cl) * kMP + 32 * kk + 8 * grp]), Rb[kk], O[rt]);
+        O[rt] = mfma16(Rb[kk], *reinterpret_cast<const u32x4*>(&s.MT[(16 * rt + cl) * kMP + 32 * kk + 8 * grp]), O[rt]);
     }
     store_out(c, O);
   };
   for (int c = 0; c < n_chunks; c += 2) {
-    step(c, st0, st1);
-    if (c + 1 < n_chunks) step(c + 1, st1, st0);
+    step(c, st0);
+    if (c + 1 < n_chunks) step(c + 1, st1);
   }
   if (S_out) {
 #pragma unroll
@@ -581,6 +695,21 @@ __global__ __launch_bounds__(256) void gdn_decode_kernel(
 
 }  // namespace
 
+// Compute units of the current device (cached per device).
+constexpr int kScanCopyWaves4 = 2;
+
+static int device_cu_count() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cache[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
 size_t gdn_workspace_bytes(int batch, int64_t T, int Hv) {
   const int64_t n_chunks = (T + kC - 1) / kC;
   return (size_t)batch * Hv * n_chunks * kRecBytes;
@@ -593,8 +722,22 @@ hipError_t launch_gdn_prefill(const uint16_t* q, const uint16_t* k, const uint16
   if (n_chunks > 0)
     hipLaunchKernelGGL(gdn_prep_kernel, dim3((unsigned)n_chunks, Hv, batch), dim3(256), 0, stream, q, k, g, beta,
                        T, Hqk, Hv, scale, (int)n_chunks, reinterpret_cast<uint8_t*>(ws));
-  hipLaunchKernelGGL(gdn_scan_kernel, dim3(2 * Hv, batch), dim3(256), 0, stream, q, k, v, S0, T, Hqk, Hv,
-                     (int)n_chunks, reinterpret_cast<const uint8_t*>(ws), out, S_out);
+  // waves per scan workgroup: the most that still gives every CU a workgroup
+  const int64_t rows_sets = (int64_t)batch * Hv;  // (sequence, value head) pairs
+  const int cus = device_cu_count();
+  const int W = rows_sets * 2 >= cus ? 4 : rows_sets * 4 >= cus ? 2 : 1;
+  const unsigned n_wg = (unsigned)(rows_sets * (8 / W));
+  const uint8_t* wsb = reinterpret_cast<const uint8_t*>(ws);
+  // copy waves: as many as keep one compute wave fed, two beside two or four
+  if (W == 4)
+    hipLaunchKernelGGL((gdn_scan_kernel<4, kScanCopyWaves4>), dim3(n_wg), dim3(64 * (4 + kScanCopyWaves4)), 0, stream,
+                       q, k, v, S0, T, Hqk, Hv, (int)n_chunks, wsb, out, S_out);
+  else if (W == 2)
+    hipLaunchKernelGGL((gdn_scan_kernel<2, 2>), dim3(n_wg), dim3(64 * (2 + 2)), 0, stream, q, k, v, S0, T, Hqk, Hv,
+                       (int)n_chunks, wsb, out, S_out);
+  else
+    hipLaunchKernelGGL((gdn_scan_kernel<1, 4>), dim3(n_wg), dim3(64 * (1 + 4)), 0, stream, q, k, v, S0, T, Hqk, Hv,
+                       (int)n_chunks, wsb, out, S_out);
   return hipGetLastError();
 }
 

@@ -95,6 +95,25 @@ def test_gdn_prefill_matches_oracle(qsa, B, T, Hqk, Hv, with_s0, shift):
             check_state(gs[b, h], s_ref[h], f"b{b} h{h}")
 
 
+@pytest.mark.parametrize("B", [2, 4])
+def test_gdn_prefill_many_heads_matches_oracle(qsa, B):
+    # 32 value heads per sequence: with more (sequence, head) pairs the scan
+    # gives each workgroup more value rows (two or four waves on a 256-CU
+    # device), so these take the wider workgroup shapes; ragged tail, carried
+    # states; the oracle runs a spread of heads
+    T, Hqk, Hv = 150, 16, 32
+    print("[case] gdn prefill many heads", B, T, Hqk, Hv, flush=True)
+    q, k, v, g, beta = gen.gdn_inputs(77 + B, B, T, Hqk, Hv)
+    S0 = gen.gdn_state(77 + B, B, Hv)
+    go, gs = run_prefill(qsa, q, k, v, g, beta, S0)
+    heads = [0, 1, 6, 15, 16, 23, 30, 31]
+    for b in range(B):
+        o_ref, s_ref = oracle.gdn(q[b], k[b], v[b], g[b], beta[b], S0=S0[b], heads=heads)
+        for h in heads:
+            check_out(go[b, :, h], o_ref[:, h], f"b{b} h{h}")
+            check_state(gs[b, h], s_ref[h], f"b{b} h{h}")
+
+
 def test_gdn_prefill_empty_sequence_passes_the_state_through(qsa):
     q, k, v, g, beta = gen.gdn_inputs(3, 2, 0, 1, 2)
     S0 = gen.gdn_state(3, 2, 2)
