@@ -107,6 +107,10 @@ __device__ __forceinline__ u32x4 pack8(const f32x16& x, int u) {
                pack_bf16x2_hw(x[8 * u + 4], x[8 * u + 5]), pack_bf16x2_hw(x[8 * u + 6], x[8 * u + 7])};
 }
 
+// exp(x) for x <= 0 on the hardware exp2 (about 1 ulp; the factors it makes
+// are rounded to bf16 or multiply fp32 products).
+__device__ __forceinline__ float exp_hw(float x) { return __builtin_amdgcn_exp2f(x * 1.4426950408889634f); }
+
 // Row of accumulator value r (0..15) in a 32-row tile, for lane half `half`.
 __device__ __forceinline__ int acc_row(int r, int half) { return 8 * (r >> 2) + 4 * half + (r & 3); }
 
@@ -120,7 +124,6 @@ __global__ __launch_bounds__(256, 2) void gdn_prep_kernel(
   __shared__ __attribute__((aligned(16))) uint16_t QTs[kC * kP];  // Q tile, then T (fp32 [64][kTP])
   __shared__ __attribute__((aligned(16))) float Lm[kC * kLP];     // L (fp32), then Tb^T and Td^T (bf16)
   __shared__ __attribute__((aligned(16))) uint16_t Mb[kC * kMP];  // M (bf16, columns permuted)
-  __shared__ __attribute__((aligned(16))) float Xs[3][16][16];
   __shared__ __attribute__((aligned(16))) float Gs[kC];
   __shared__ __attribute__((aligned(16))) float Bs[kC];
   __shared__ __attribute__((aligned(16))) float Ds[kC];
@@ -194,11 +197,18 @@ __global__ __launch_bounds__(256, 2) void gdn_prep_kernel(
     const int j = 32 * tj + col;
     const float gj = Gs[j];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int i = 32 * ti + acc_row(r, half);
-      const float d = expf(Gs[i] - gj);  // only used where j <= i
-      Lm[i * kLP + j] = j < i ? Bs[i] * d * kk[r] : 0.0f;
-      Mb[i * kMP + perm16(j)] = (uint16_t)f32_to_bf16_bits(j <= i ? scale * d * qk[r] : 0.0f);
+    for (int qd = 0; qd < 4; ++qd) {
+      // rows 32 ti + 8 qd + 4 half + 0..3 of the tile
+      const int i0 = 32 * ti + 8 * qd + 4 * half;
+      const f32x4 gi = *reinterpret_cast<const f32x4*>(&Gs[i0]);
+      const f32x4 bi = *reinterpret_cast<const f32x4*>(&Bs[i0]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 4 * qd + e, i = i0 + e;
+        const float d = exp_hw(gi[e] - gj);  // only used where j <= i, so the exponent is <= 0
+        Lm[i * kLP + j] = j < i ? bi[e] * d * kk[r] : 0.0f;
+        Mb[i * kMP + perm16(j)] = (uint16_t)f32_to_bf16_bits(j <= i ? scale * d * qk[r] : 0.0f);
+      }
     }
   } else {
     // the tile above the diagonal (rows 0..31, columns 32..63) of M is zero
@@ -210,60 +220,79 @@ __global__ __launch_bounds__(256, 2) void gdn_prep_kernel(
   // substitution in one wave: lane (a, c) = (lane / 16, lane % 16) keeps
   // column c of block a in registers, so each row needs only its row of L
   // (the same for the 16 lanes of a block, read once per row) and no lane
-  // exchange; the entries above the diagonal come out as zeros.
+  // exchange; the entries above the diagonal come out as zeros. Four partial
+  // sums keep the chain of dependent adds short.
   if (wave == 0) {
     const int a0 = 16 * (lane >> 4), cc = lane & 15;
     float t[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const float* lrow = &Lm[(a0 + i) * kLP + a0];
-      float sum = 0.0f;
+      float part[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-      for (int m = 0; m < i; ++m) sum += lrow[m] * t[m];
-      t[i] = (i == cc ? 1.0f : 0.0f) - sum;
+      for (int m = 0; m < i; ++m) part[m & 3] += lrow[m] * t[m];
+      t[i] = (i == cc ? 1.0f : 0.0f) - ((part[0] + part[1]) + (part[2] + part[3]));
     }
 #pragma unroll
     for (int m = 0; m < 16; ++m) Tm[(a0 + m) * kTP + a0 + cc] = t[m];
   }
   __syncthreads();
-  // blocks below the diagonal, by distance d from it:
-  // T_ab = -T_aa X, X = sum_{m in blocks b .. a-1} L_am T_mb  (a = b + d).
-  // Wave w takes block b = w (while b < 4 - d); lane: row i = lane / 4 and
-  // columns 4(lane % 4) .. +3 of the block.
-  {
-    const int bb = wave, i = lane >> 2, c4 = 4 * (lane & 3);
-    for (int d = 1; d < 4; ++d) {
-      const int a = bb + d;
-      const bool act = a < 4;
-      if (act) {
-        f32x4 x = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-        const float* lrow = &Lm[(16 * a + i) * kLP];
-        for (int m = 16 * bb; m < 16 * a; ++m) {
-          const float l = lrow[m];
-          const f32x4 tv = *reinterpret_cast<const f32x4*>(&Tm[m * kTP + 16 * bb + c4]);
-          x += l * tv;
-        }
-        *reinterpret_cast<f32x4*>(&Xs[bb][i][c4]) = x;
-      }
-      __syncthreads();
-      if (act) {
-        f32x4 y = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-        const float* trow = &Tm[(16 * a + i) * kTP + 16 * a];
+  // The blocks below the diagonal, column block b by wave b (no exchange
+  // between waves: column block b only needs its own blocks and the diagonal
+  // ones): T_ab = -T_aa X, X = sum_{m = b .. a-1} L_am T_mb, for a = b+1 .. 3
+  // in order, on the fp32 MFMA (16x16x4). The wave keeps its blocks T_mb in
+  // accumulator layout (lane l: rows 4 (l/16) + r, column l % 16), which is
+  // also the B operand of a product whose k-step s takes, in lane group g,
+  // the index 4g + s: the A operand is then row l % 16, columns 4g .. 4g+3 of
+  // the left factor, one 16-byte read.
+  const int g4 = lane >> 4, n16 = lane & 15;
+  f32x4 Tc[4];  // Tc[a] = T_{a, wave}
 #pragma unroll
-        for (int m = 0; m < 16; ++m) y += trow[m] * *reinterpret_cast<const f32x4*>(&Xs[bb][m][c4]);
-        *reinterpret_cast<f32x4*>(&Tm[(16 * a + i) * kTP + 16 * bb + c4]) = -y;
-      }
-      __syncthreads();
+  for (int a = 0; a < 4; ++a) {
+    Tc[a] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    if (a == wave) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) Tc[a][r] = Tm[(16 * a + 4 * g4 + r) * kTP + 16 * a + n16];
     }
   }
+  auto mm16 = [&](const f32x4& arow, const f32x4& bacc, f32x4 c) __attribute__((always_inline)) {
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4) c = __builtin_amdgcn_mfma_f32_16x16x4f32(arow[s4], bacc[s4], c, 0, 0, 0);
+    return c;
+  };
+#pragma unroll
+  for (int a = 1; a < 4; ++a) {
+    if (a > wave) {
+      f32x4 x = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int mb = 0; mb < 3; ++mb) {
+        if (mb >= wave && mb < a)
+          x = mm16(*reinterpret_cast<const f32x4*>(&Lm[(16 * a + n16) * kLP + 16 * mb + 4 * g4]), Tc[mb], x);
+      }
+      const f32x4 y =
+          mm16(*reinterpret_cast<const f32x4*>(&Tm[(16 * a + n16) * kTP + 16 * a + 4 * g4]), x, f32x4{0.0f, 0.0f, 0.0f, 0.0f});
+      Tc[a] = -y;
+    }
+  }
+  __syncthreads();  // L is read no more: Tb^T and Td^T take its place
   // Tb = T diag(b) and its copy scaled by the decay to the chunk end, both
-  // transposed (rows j, columns i permuted) in bf16; T is zero above its
-  // diagonal blocks
-  for (int e = tid; e < kC * kC; e += 256) {
-    const int i = e >> 6, j = e & 63;
-    const float t = (j >> 4) > (i >> 4) ? 0.0f : Tm[i * kTP + j] * Bs[j];
-    TbT[j * kMP + perm16(i)] = (uint16_t)f32_to_bf16_bits(t);
-    TdT[j * kMP + perm16(i)] = (uint16_t)f32_to_bf16_bits(t * Ds[i]);
+  // transposed (rows j, columns i permuted) in bf16, from the registers: lane
+  // (g, n) of wave b holds column j = 16b + n, rows 16a + 4g .. +3 of each
+  // block (zero above the diagonal blocks); four rows go out as 8 bytes
+  // (perm16 keeps a quad together).
+  {
+    const int j = 16 * wave + n16;
+    const float bj = Bs[j];
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      const int i0 = 16 * a + 4 * g4;
+      const f32x4 di = *reinterpret_cast<const f32x4*>(&Ds[i0]);
+      const f32x4 t = Tc[a] * bj;
+      *reinterpret_cast<uint2*>(&TbT[j * kMP + perm16(i0)]) =
+          make_uint2(pack_bf16x2_hw(t[0], t[1]), pack_bf16x2_hw(t[2], t[3]));
+      *reinterpret_cast<uint2*>(&TdT[j * kMP + perm16(i0)]) =
+          make_uint2(pack_bf16x2_hw(t[0] * di[0], t[1] * di[1]), pack_bf16x2_hw(t[2] * di[2], t[3] * di[3]));
+    }
   }
   __syncthreads();
 
