@@ -25,6 +25,7 @@
 // from one state to the next is two products deep.
 // Decode (one token on a carried state) is gdn_decode_kernel: the recurrence
 // itself, one pass over the fp32 state in HBM.
+#include <algorithm>
 #include <atomic>
 #include <cstddef>
 
@@ -115,10 +116,12 @@ __device__ __forceinline__ float exp_hw(float x) { return __builtin_amdgcn_exp2f
 __device__ __forceinline__ int acc_row(int r, int half) { return 8 * (r >> 2) + 4 * half + (r & 3); }
 
 // ---------------------------------------------------------------- prep ----
-// One workgroup (4 waves) per (chunk, value head, sequence).
+// Persistent: each workgroup (4 waves) takes (chunk, value head, sequence)
+// items in turn, and loads the next item's K and Q tiles and gates into
+// registers while it works on the current one.
 __global__ __launch_bounds__(256, 2) void gdn_prep_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const float* __restrict__ g,
-    const float* __restrict__ beta, int64_t T, int Hqk, int Hv, float scale, int n_chunks,
+    const float* __restrict__ beta, int64_t T, int Hqk, int Hv, float scale, int n_chunks, int64_t n_items,
     uint8_t* __restrict__ ws) {
   __shared__ __attribute__((aligned(16))) uint16_t Ks[kC * kP];   // K tile, natural order
   __shared__ __attribute__((aligned(16))) uint16_t QTs[kC * kP];  // Q tile, then T (fp32 [64][kTP])
@@ -132,223 +135,249 @@ __global__ __launch_bounds__(256, 2) void gdn_prep_kernel(
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int half = lane >> 5, col = lane & 31;
-  const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-  const int hk = h / (Hv / Hqk);
-  const int64_t t0 = (int64_t)c * kC;
-  const int n = (int)min<int64_t>(kC, T - t0);
-  uint8_t* rec = ws + (((int64_t)b * Hv + h) * n_chunks + c) * kRecBytes;
   float* Tm = reinterpret_cast<float*>(QTs);
   uint16_t* TbT = reinterpret_cast<uint16_t*>(Lm);  // [64 j][kMP], i permuted: T_ij b_j
   uint16_t* TdT = TbT + kC * kMP;                   // same times exp(G_C - G_i)
 
-  // this head's log decays and write gates (issued first: their latency
-  // overlaps the tile loads)
+  // an item's inputs in registers: thread tid holds 16-byte pieces
+  // tid + 256 u (row / 16, piece % 16) of the K and Q tiles (key head h / (Hv /
+  // Hqk); rows past the sequence are zero), and lane l of wave 0 token l's log
+  // decay and write gate (padding 0)
+  u32x4 kv[4], qv[4];
   float gx = 0.0f, bt = 0.0f;
-  if (wave == 0 && lane < n) {
-    gx = g[((int64_t)b * T + t0 + lane) * Hv + h];
-    bt = beta[((int64_t)b * T + t0 + lane) * Hv + h];
-  }
-  // tiles of K and Q (key head hk); rows past the sequence are zero
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int idx = tid + 256 * u;
-    const int r = idx >> 4, part = idx & 15;
-    u32x4 kv = u32x4{0u, 0u, 0u, 0u}, qv = kv;
-    if (r < n) {
-      const int64_t tok = (int64_t)b * T + t0 + r;
-      kv = ld16(k + (tok * Hqk + hk) * kD + 8 * part);
-      qv = ld16(q + (tok * Hqk + hk) * kD + 8 * part);
+  auto fetch = [&](int64_t it) __attribute__((always_inline)) {
+    const int c = (int)(it % n_chunks), h = (int)((it / n_chunks) % Hv);
+    const int64_t b = it / ((int64_t)n_chunks * Hv);
+    const int hk = h / (Hv / Hqk);
+    const int64_t t0 = (int64_t)c * kC;
+    const int n = (int)min<int64_t>(kC, T - t0);
+    gx = 0.0f;
+    bt = 0.0f;
+    if (wave == 0 && lane < n) {
+      gx = g[(b * T + t0 + lane) * Hv + h];
+      bt = beta[(b * T + t0 + lane) * Hv + h];
     }
-    *reinterpret_cast<u32x4*>(&Ks[r * kP + 8 * part]) = kv;
-    *reinterpret_cast<u32x4*>(&QTs[r * kP + 8 * part]) = qv;
-  }
-  if (wave == 0) {
-    // running sum of the log decays over the chunk (padding adds 0)
-    float x = gx;
 #pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const float y = __shfl_up(x, off);
-      if (lane >= off) x += y;
-    }
-    const float gl = __shfl(x, 63);
-    const float gam = expf(x);
-    Gs[lane] = x;
-    Bs[lane] = bt;
-    Ds[lane] = expf(gl - x);
-    Rg[lane] = scale * gam;
-    Rg[64 + lane] = gam;
-    Rg[128 + lane] = expf(gl);
-    Rg[192 + lane] = 0.0f;
-  }
-  __syncthreads();
-
-  // K K^T -> L (fp32) and Q K^T -> M (bf16), tiles of 32 x 32 on or below the diagonal
-  if (wave < 3) {
-    const int ti = wave == 0 ? 0 : 1, tj = wave == 2 ? 1 : 0;
-    f32x16 kk = f32x16{}, qk = f32x16{};
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      const u32x4 bk = *reinterpret_cast<const u32x4*>(&Ks[(32 * tj + col) * kP + 16 * ks + 8 * half]);
-      const u32x4 ak = *reinterpret_cast<const u32x4*>(&Ks[(32 * ti + col) * kP + 16 * ks + 8 * half]);
-      const u32x4 aq = *reinterpret_cast<const u32x4*>(&QTs[(32 * ti + col) * kP + 16 * ks + 8 * half]);
-      kk = mfma32x32x16(ak, bk, kk);
-      qk = mfma32x32x16(aq, bk, qk);
-    }
-    const int j = 32 * tj + col;
-    const float gj = Gs[j];
-#pragma unroll
-    for (int qd = 0; qd < 4; ++qd) {
-      // rows 32 ti + 8 qd + 4 half + 0..3 of the tile
-      const int i0 = 32 * ti + 8 * qd + 4 * half;
-      const f32x4 gi = *reinterpret_cast<const f32x4*>(&Gs[i0]);
-      const f32x4 bi = *reinterpret_cast<const f32x4*>(&Bs[i0]);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = 4 * qd + e, i = i0 + e;
-        const float d = exp_hw(gi[e] - gj);  // only used where j <= i, so the exponent is <= 0
-        Lm[i * kLP + j] = j < i ? bi[e] * d * kk[r] : 0.0f;
-        Mb[i * kMP + perm16(j)] = (uint16_t)f32_to_bf16_bits(j <= i ? scale * d * qk[r] : 0.0f);
+    for (int u = 0; u < 4; ++u) {
+      const int r = (tid + 256 * u) >> 4, part = tid & 15;
+      kv[u] = u32x4{0u, 0u, 0u, 0u};
+      qv[u] = kv[u];
+      if (r < n) {
+        const int64_t tok = b * T + t0 + r;
+        kv[u] = ld16(k + (tok * Hqk + hk) * kD + 8 * part);
+        qv[u] = ld16(q + (tok * Hqk + hk) * kD + 8 * part);
       }
     }
-  } else {
-    // the tile above the diagonal (rows 0..31, columns 32..63) of M is zero
-    for (int e = lane; e < 32 * 32; e += 64) Mb[(e >> 5) * kMP + perm16(32 + (e & 31))] = 0;
-  }
-  __syncthreads();
-
-  // T = (I + L)^-1 in 16 x 16 blocks. The four diagonal blocks by forward
-  // substitution in one wave: lane (a, c) = (lane / 16, lane % 16) keeps
-  // column c of block a in registers, so each row needs only its row of L
-  // (the same for the 16 lanes of a block, read once per row) and no lane
-  // exchange; the entries above the diagonal come out as zeros. Four partial
-  // sums keep the chain of dependent adds short.
-  if (wave == 0) {
-    const int a0 = 16 * (lane >> 4), cc = lane & 15;
-    float t[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const float* lrow = &Lm[(a0 + i) * kLP + a0];
-      float part[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-      for (int m = 0; m < i; ++m) part[m & 3] += lrow[m] * t[m];
-      t[i] = (i == cc ? 1.0f : 0.0f) - ((part[0] + part[1]) + (part[2] + part[3]));
-    }
-#pragma unroll
-    for (int m = 0; m < 16; ++m) Tm[(a0 + m) * kTP + a0 + cc] = t[m];
-  }
-  __syncthreads();
-  // The blocks below the diagonal, column block b by wave b (no exchange
-  // between waves: column block b only needs its own blocks and the diagonal
-  // ones): T_ab = -T_aa X, X = sum_{m = b .. a-1} L_am T_mb, for a = b+1 .. 3
-  // in order, on the fp32 MFMA (16x16x4). The wave keeps its blocks T_mb in
-  // accumulator layout (lane l: rows 4 (l/16) + r, column l % 16), which is
-  // also the B operand of a product whose k-step s takes, in lane group g,
-  // the index 4g + s: the A operand is then row l % 16, columns 4g .. 4g+3 of
-  // the left factor, one 16-byte read.
-  const int g4 = lane >> 4, n16 = lane & 15;
-  f32x4 Tc[4];  // Tc[a] = T_{a, wave}
-#pragma unroll
-  for (int a = 0; a < 4; ++a) {
-    Tc[a] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    if (a == wave) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) Tc[a][r] = Tm[(16 * a + 4 * g4 + r) * kTP + 16 * a + n16];
-    }
-  }
-  auto mm16 = [&](const f32x4& arow, const f32x4& bacc, f32x4 c) __attribute__((always_inline)) {
-#pragma unroll
-    for (int s4 = 0; s4 < 4; ++s4) c = __builtin_amdgcn_mfma_f32_16x16x4f32(arow[s4], bacc[s4], c, 0, 0, 0);
-    return c;
   };
+  // the tiles go to LDS once the previous item is done with every LDS array
+  auto stage = [&]() __attribute__((always_inline)) {
 #pragma unroll
-  for (int a = 1; a < 4; ++a) {
-    if (a > wave) {
-      f32x4 x = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-      for (int mb = 0; mb < 3; ++mb) {
-        if (mb >= wave && mb < a)
-          x = mm16(*reinterpret_cast<const f32x4*>(&Lm[(16 * a + n16) * kLP + 16 * mb + 4 * g4]), Tc[mb], x);
-      }
-      const f32x4 y =
-          mm16(*reinterpret_cast<const f32x4*>(&Tm[(16 * a + n16) * kTP + 16 * a + 4 * g4]), x, f32x4{0.0f, 0.0f, 0.0f, 0.0f});
-      Tc[a] = -y;
+    for (int u = 0; u < 4; ++u) {
+      const int r = (tid + 256 * u) >> 4, part = tid & 15;
+      *reinterpret_cast<u32x4*>(&Ks[r * kP + 8 * part]) = kv[u];
+      *reinterpret_cast<u32x4*>(&QTs[r * kP + 8 * part]) = qv[u];
     }
+  };
+  if ((int64_t)blockIdx.x < n_items) {
+    fetch(blockIdx.x);
+    stage();
   }
-  __syncthreads();  // L is read no more: Tb^T and Td^T take its place
-  // Tb = T diag(b) and its copy scaled by the decay to the chunk end, both
-  // transposed (rows j, columns i permuted) in bf16, from the registers: lane
-  // (g, n) of wave b holds column j = 16b + n, rows 16a + 4g .. +3 of each
-  // block (zero above the diagonal blocks); four rows go out as 8 bytes
-  // (perm16 keeps a quad together).
-  {
-    const int j = 16 * wave + n16;
-    const float bj = Bs[j];
+  for (int64_t item = blockIdx.x; item < n_items; item += gridDim.x) {
+    uint8_t* rec = ws + item * kRecBytes;  // items are numbered as the records
+    const bool more = item + gridDim.x < n_items;
+    if (wave == 0) {
+      // running sum of the log decays over the chunk (padding adds 0)
+      float x = gx;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const float y = __shfl_up(x, off);
+        if (lane >= off) x += y;
+      }
+      const float gl = __shfl(x, 63);
+      const float gam = expf(x);
+      Gs[lane] = x;
+      Bs[lane] = bt;
+      Ds[lane] = expf(gl - x);
+      Rg[lane] = scale * gam;
+      Rg[64 + lane] = gam;
+      Rg[128 + lane] = expf(gl);
+      Rg[192 + lane] = 0.0f;
+    }
+    if (more) fetch(item + gridDim.x);
+    __syncthreads();
+
+    // K K^T -> L (fp32) and Q K^T -> M (bf16), tiles of 32 x 32 on or below the diagonal
+    if (wave < 3) {
+      const int ti = wave == 0 ? 0 : 1, tj = wave == 2 ? 1 : 0;
+      f32x16 kk = f32x16{}, qk = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        const u32x4 bk = *reinterpret_cast<const u32x4*>(&Ks[(32 * tj + col) * kP + 16 * ks + 8 * half]);
+        const u32x4 ak = *reinterpret_cast<const u32x4*>(&Ks[(32 * ti + col) * kP + 16 * ks + 8 * half]);
+        const u32x4 aq = *reinterpret_cast<const u32x4*>(&QTs[(32 * ti + col) * kP + 16 * ks + 8 * half]);
+        kk = mfma32x32x16(ak, bk, kk);
+        qk = mfma32x32x16(aq, bk, qk);
+      }
+      const int j = 32 * tj + col;
+      const float gj = Gs[j];
+#pragma unroll
+      for (int qd = 0; qd < 4; ++qd) {
+        // rows 32 ti + 8 qd + 4 half + 0..3 of the tile
+        const int i0 = 32 * ti + 8 * qd + 4 * half;
+        const f32x4 gi = *reinterpret_cast<const f32x4*>(&Gs[i0]);
+        const f32x4 bi = *reinterpret_cast<const f32x4*>(&Bs[i0]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * qd + e, i = i0 + e;
+          const float d = exp_hw(gi[e] - gj);  // only used where j <= i, so the exponent is <= 0
+          Lm[i * kLP + j] = j < i ? bi[e] * d * kk[r] : 0.0f;
+          Mb[i * kMP + perm16(j)] = (uint16_t)f32_to_bf16_bits(j <= i ? scale * d * qk[r] : 0.0f);
+        }
+      }
+    } else {
+      // the tile above the diagonal (rows 0..31, columns 32..63) of M is zero
+      for (int e = lane; e < 32 * 32; e += 64) Mb[(e >> 5) * kMP + perm16(32 + (e & 31))] = 0;
+    }
+    __syncthreads();
+
+    // T = (I + L)^-1 in 16 x 16 blocks. The four diagonal blocks by forward
+    // substitution in one wave: lane (a, c) = (lane / 16, lane % 16) keeps
+    // column c of block a in registers, so each row needs only its row of L
+    // (the same for the 16 lanes of a block, read once per row) and no lane
+    // exchange; the entries above the diagonal come out as zeros. Four partial
+    // sums keep the chain of dependent adds short.
+    if (wave == 0) {
+      const int a0 = 16 * (lane >> 4), cc = lane & 15;
+      float t[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float* lrow = &Lm[(a0 + i) * kLP + a0];
+        float part[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int m = 0; m < i; ++m) part[m & 3] += lrow[m] * t[m];
+        t[i] = (i == cc ? 1.0f : 0.0f) - ((part[0] + part[1]) + (part[2] + part[3]));
+      }
+#pragma unroll
+      for (int m = 0; m < 16; ++m) Tm[(a0 + m) * kTP + a0 + cc] = t[m];
+    }
+    __syncthreads();
+    // The blocks below the diagonal, column block b by wave b (no exchange
+    // between waves: column block b only needs its own blocks and the diagonal
+    // ones): T_ab = -T_aa X, X = sum_{m = b .. a-1} L_am T_mb, for a = b+1 .. 3
+    // in order, on the fp32 MFMA (16x16x4). The wave keeps its blocks T_mb in
+    // accumulator layout (lane l: rows 4 (l/16) + r, column l % 16), which is
+    // also the B operand of a product whose k-step s takes, in lane group g,
+    // the index 4g + s: the A operand is then row l % 16, columns 4g .. 4g+3 of
+    // the left factor, one 16-byte read.
+    const int g4 = lane >> 4, n16 = lane & 15;
+    f32x4 Tc[4];  // Tc[a] = T_{a, wave}
 #pragma unroll
     for (int a = 0; a < 4; ++a) {
-      const int i0 = 16 * a + 4 * g4;
-      const f32x4 di = *reinterpret_cast<const f32x4*>(&Ds[i0]);
-      const f32x4 t = Tc[a] * bj;
-      *reinterpret_cast<uint2*>(&TbT[j * kMP + perm16(i0)]) =
-          make_uint2(pack_bf16x2_hw(t[0], t[1]), pack_bf16x2_hw(t[2], t[3]));
-      *reinterpret_cast<uint2*>(&TdT[j * kMP + perm16(i0)]) =
-          make_uint2(pack_bf16x2_hw(t[0] * di[0], t[1] * di[1]), pack_bf16x2_hw(t[2] * di[2], t[3] * di[3]));
-    }
-  }
-  __syncthreads();
-
-  // MT = M Tb (wave w: tile (w / 2, w % 2)) and Kt = Td^T K (wave w: columns
-  // 32w .. 32w+31). The record is assembled in LDS in its workspace layout
-  // (Kt over the dead T, MT over M once every wave has read M) and written
-  // out with coalesced 16-byte stores.
-  f32x16 mt = f32x16{};
-  {
-    const int ti = wave >> 1, tj = wave & 1;
+      Tc[a] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      if (a == wave) {
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const u32x4 am = *reinterpret_cast<const u32x4*>(&Mb[(32 * ti + col) * kMP + 16 * ks + 8 * half]);
-      const u32x4 bt2 = *reinterpret_cast<const u32x4*>(&TbT[(32 * tj + col) * kMP + 16 * ks + 8 * half]);
-      mt = mfma32x32x16(am, bt2, mt);
-    }
-  }
-  {
-    uint16_t* Ktl = QTs;
-    const int tro = tr_offset(lane);
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt) {
-      f32x16 acc = f32x16{};
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const u32x4 at = *reinterpret_cast<const u32x4*>(&TdT[(32 * rt + col) * kMP + 16 * kk + 8 * half]);
-        const uint2 lo = ld_tr16(&Ks[(16 * kk) * kP + tro + 32 * wave]);
-        const uint2 hi = ld_tr16(&Ks[(16 * kk + 8) * kP + tro + 32 * wave]);
-        acc = mfma32x32x16(at, u32x4{lo.x, lo.y, hi.x, hi.y}, acc);
+        for (int r = 0; r < 4; ++r) Tc[a][r] = Tm[(16 * a + 4 * g4 + r) * kTP + 16 * a + n16];
       }
+    }
+    auto mm16 = [&](const f32x4& arow, const f32x4& bacc, f32x4 c) __attribute__((always_inline)) {
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4) c = __builtin_amdgcn_mfma_f32_16x16x4f32(arow[s4], bacc[s4], c, 0, 0, 0);
+      return c;
+    };
+#pragma unroll
+    for (int a = 1; a < 4; ++a) {
+      if (a > wave) {
+        f32x4 x = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int mb = 0; mb < 3; ++mb) {
+          if (mb >= wave && mb < a)
+            x = mm16(*reinterpret_cast<const f32x4*>(&Lm[(16 * a + n16) * kLP + 16 * mb + 4 * g4]), Tc[mb], x);
+        }
+        const f32x4 y =
+            mm16(*reinterpret_cast<const f32x4*>(&Tm[(16 * a + n16) * kTP + 16 * a + 4 * g4]), x, f32x4{0.0f, 0.0f, 0.0f, 0.0f});
+        Tc[a] = -y;
+      }
+    }
+    __syncthreads();  // L is read no more: Tb^T and Td^T take its place
+    // Tb = T diag(b) and its copy scaled by the decay to the chunk end, both
+    // transposed (rows j, columns i permuted) in bf16, from the registers: lane
+    // (g, n) of wave b holds column j = 16b + n, rows 16a + 4g .. +3 of each
+    // block (zero above the diagonal blocks); four rows go out as 8 bytes
+    // (perm16 keeps a quad together).
+    {
+      const int j = 16 * wave + n16;
+      const float bj = Bs[j];
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const int i0 = 16 * a + 4 * g4;
+        const f32x4 di = *reinterpret_cast<const f32x4*>(&Ds[i0]);
+        const f32x4 t = Tc[a] * bj;
+        *reinterpret_cast<uint2*>(&TbT[j * kMP + perm16(i0)]) =
+            make_uint2(pack_bf16x2_hw(t[0], t[1]), pack_bf16x2_hw(t[2], t[3]));
+        *reinterpret_cast<uint2*>(&TdT[j * kMP + perm16(i0)]) =
+            make_uint2(pack_bf16x2_hw(t[0] * di[0], t[1] * di[1]), pack_bf16x2_hw(t[2] * di[2], t[3] * di[3]));
+      }
+    }
+    __syncthreads();
+
+    // MT = M Tb (wave w: tile (w / 2, w % 2)) and Kt = Td^T K (wave w: columns
+    // 32w .. 32w+31). The record is assembled in LDS in its workspace layout
+    // (Kt over the dead T, MT over M once every wave has read M) and written
+    // out with coalesced 16-byte stores.
+    f32x16 mt = f32x16{};
+    {
+      const int ti = wave >> 1, tj = wave & 1;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const u32x4 am = *reinterpret_cast<const u32x4*>(&Mb[(32 * ti + col) * kMP + 16 * ks + 8 * half]);
+        const u32x4 bt2 = *reinterpret_cast<const u32x4*>(&TbT[(32 * tj + col) * kMP + 16 * ks + 8 * half]);
+        mt = mfma32x32x16(am, bt2, mt);
+      }
+    }
+    {
+      uint16_t* Ktl = QTs;
+      const int tro = tr_offset(lane);
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt) {
+        f32x16 acc = f32x16{};
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+          const u32x4 at = *reinterpret_cast<const u32x4*>(&TdT[(32 * rt + col) * kMP + 16 * kk + 8 * half]);
+          const uint2 lo = ld_tr16(&Ks[(16 * kk) * kP + tro + 32 * wave]);
+          const uint2 hi = ld_tr16(&Ks[(16 * kk + 8) * kP + tro + 32 * wave]);
+          acc = mfma32x32x16(at, u32x4{lo.x, lo.y, hi.x, hi.y}, acc);
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int j = 32 * rt + acc_row(r, half);
+          Ktl[j * kP + 32 * wave + acc_of_slot(col)] = (uint16_t)f32_to_bf16_bits(acc[r]);
+        }
+      }
+    }
+    __syncthreads();
+    {
+      const int ti = wave >> 1, tj = wave & 1;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int j = 32 * rt + acc_row(r, half);
-        Ktl[j * kP + 32 * wave + acc_of_slot(col)] = (uint16_t)f32_to_bf16_bits(acc[r]);
+        const int i = 32 * ti + acc_row(r, half);
+        Mb[i * kMP + 32 * tj + slot_of_acc(col)] = (uint16_t)f32_to_bf16_bits(mt[r]);
       }
     }
-  }
-  __syncthreads();
-  {
-    const int ti = wave >> 1, tj = wave & 1;
+    __syncthreads();
+    static_assert(sizeof(QTs) == kRecM - kRecK && sizeof(Mb) == kRecG - kRecM && sizeof(Rg) == kRecBytes - kRecG,
+                  "LDS staging matches the record layout");
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int i = 32 * ti + acc_row(r, half);
-      Mb[i * kMP + 32 * tj + slot_of_acc(col)] = (uint16_t)f32_to_bf16_bits(mt[r]);
+    for (int u = 0; u < 7; ++u) {
+      const int ob = 16 * (tid + 256 * u);
+      const uint8_t* src = ob < kRecM   ? reinterpret_cast<const uint8_t*>(QTs) + ob
+                           : ob < kRecG ? reinterpret_cast<const uint8_t*>(Mb) + (ob - kRecM)
+                                        : reinterpret_cast<const uint8_t*>(Rg) + (ob - kRecG);
+      *reinterpret_cast<u32x4*>(rec + ob) = *reinterpret_cast<const u32x4*>(src);
     }
-  }
-  __syncthreads();
-  static_assert(sizeof(QTs) == kRecM - kRecK && sizeof(Mb) == kRecG - kRecM && sizeof(Rg) == kRecBytes - kRecG,
-                "LDS staging matches the record layout");
-#pragma unroll
-  for (int u = 0; u < 7; ++u) {
-    const int ob = 16 * (tid + 256 * u);
-    const uint8_t* src = ob < kRecM   ? reinterpret_cast<const uint8_t*>(QTs) + ob
-                         : ob < kRecG ? reinterpret_cast<const uint8_t*>(Mb) + (ob - kRecM)
-                                      : reinterpret_cast<const uint8_t*>(Rg) + (ob - kRecG);
-    *reinterpret_cast<u32x4*>(rec + ob) = *reinterpret_cast<const u32x4*>(src);
+    if (more) {
+      __syncthreads();  // every LDS array is free for the next item
+      stage();
+    }
   }
 }
 
@@ -748,9 +777,12 @@ hipError_t launch_gdn_prefill(const uint16_t* q, const uint16_t* k, const uint16
                               const float* beta, const float* S0, int batch, int64_t T, int Hqk, int Hv,
                               float scale, uint16_t* out, float* S_out, void* ws, hipStream_t stream) {
   const int64_t n_chunks = (T + kC - 1) / kC;
-  if (n_chunks > 0)
-    hipLaunchKernelGGL(gdn_prep_kernel, dim3((unsigned)n_chunks, Hv, batch), dim3(256), 0, stream, q, k, g, beta,
-                       T, Hqk, Hv, scale, (int)n_chunks, reinterpret_cast<uint8_t*>(ws));
+  if (n_chunks > 0) {
+    const int64_t n_items = (int64_t)batch * Hv * n_chunks;  // (sequence, value head, chunk), chunk fastest
+    const unsigned grid = (unsigned)std::min<int64_t>(n_items, 2 * (int64_t)device_cu_count());
+    hipLaunchKernelGGL(gdn_prep_kernel, dim3(grid), dim3(256), 0, stream, q, k, g, beta, T, Hqk, Hv, scale,
+                       (int)n_chunks, n_items, reinterpret_cast<uint8_t*>(ws));
+  }
   // waves per scan workgroup: the most that still gives every CU a workgroup
   const int64_t rows_sets = (int64_t)batch * Hv;  // (sequence, value head) pairs
   const int cus = device_cu_count();
