@@ -384,12 +384,13 @@ __global__ __launch_bounds__(256, 2) void gdn_prep_kernel(
 // ---------------------------------------------------------------- scan ----
 // Row d of the state only ever meets column d of V and of the outputs, so the
 // 128 value rows of a (sequence, value head) are independent recurrences: they
-// are split over 8 / W workgroups of W waves, and wave w of part p carries
-// rows d0 .. d0+15, d0 = 16 (W p + w). W is chosen per launch so that the grid
-// still covers the chip (one wave per workgroup when sequences x heads are
-// few: each CU then walks one set of rows with its LDS to itself; four when
-// they are many: a chunk's copies then serve four waves). The parts of a head
-// (and neighbouring heads, which share a key head) are given consecutive
+// are split over 8 / W workgroups of W sets of 16 rows, set w of part p being
+// rows d0 .. d0+15, d0 = 16 (W p + w). W (1 or 2) is chosen per launch so
+// that the grid still covers the chip. Each set has two compute waves: the
+// recurrence wave forms X, R and the next state (the chain from one chunk to
+// the next), the output wave forms O from the state and R it publishes in
+// LDS; separate copy waves fill the chunk stages. The parts of a head (and
+// neighbouring heads, which share a key head) are given consecutive
 // workgroup slots of one XCD, so the chunk data they all copy is fetched once
 // into that XCD's L2.
 // A wave holds its rows transposed (S^T, dk x 16) in eight 16 x 16
@@ -414,7 +415,8 @@ template <int W>
 struct ScanStage {
   // V columns staged: the part's own, and at least the 32-column block that
   // holds them (one k-step of the MFMA that adds V)
-  static constexpr int kVC = W == 4 ? 64 : 32;
+  static_assert(W == 1 || W == 2, "one or two row sets per workgroup");
+  static constexpr int kVC = 32;
   uint16_t K[kC * kD];
   uint16_t Q[kC * kD];
   uint16_t V[kC * kVC];
@@ -437,6 +439,9 @@ __device__ __forceinline__ int swz16(int i, int p) { return i * 256 + (((p ^ i) 
 constexpr int kBufferFlags = 0x00020000;
 
 constexpr int vmcnt_wait(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
+// s_waitcnt immediate that waits for every LDS operation of the wave and
+// does not wait on the other counters.
+constexpr int kLgkmWait0 = 15 | (7 << 4) | (0 << 8) | (3 << 14);
 
 __device__ __forceinline__ u32x4 pack_tiles(const f32x4& a, const f32x4& b) {
   return u32x4{pack_bf16x2_hw(a[0], a[1]), pack_bf16x2_hw(a[2], a[3]), pack_bf16x2_hw(b[0], b[1]),
@@ -444,7 +449,7 @@ __device__ __forceinline__ u32x4 pack_tiles(const f32x4& a, const f32x4& b) {
 }
 
 template <int W, int NC>
-__global__ __launch_bounds__(64 * (W + NC), 1) void gdn_scan_kernel(
+__global__ __launch_bounds__(64 * (2 * W + NC), 1) void gdn_scan_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const float* __restrict__ S0, int64_t T, int Hqk, int Hv, int n_chunks, const uint8_t* __restrict__ ws,
     uint16_t* __restrict__ out, float* __restrict__ S_out) {
@@ -456,6 +461,12 @@ __global__ __launch_bounds__(64 * (W + NC), 1) void gdn_scan_kernel(
                 "stage holds the record image");
   __shared__ __attribute__((aligned(16))) Stage st0;
   __shared__ __attribute__((aligned(16))) Stage st1;
+  // handed from a set's recurrence wave to its output wave: the packed state
+  // entering a chunk (two chunks' worth, by parity) and the chunk's packed R,
+  // as the lanes hold them
+  __shared__ __attribute__((aligned(16))) u32x4 sx[W][2][4][64];
+  __shared__ __attribute__((aligned(16))) u32x4 rx[W][2][64];
+  __shared__ int r_ready[W];  // chunks whose R has been handed over, per set
 
   const int tid = threadIdx.x;
   // the wave index as a scalar: the copy wave and the compute waves take
@@ -472,13 +483,13 @@ __global__ __launch_bounds__(64 * (W + NC), 1) void gdn_scan_kernel(
   const uint8_t* recs = ws + ((int64_t)b * Hv + h) * n_chunks * kRecBytes;
   const int64_t kq_row = (int64_t)Hqk * kD, v_row = (int64_t)Hv * kD;
 
-  if (wave >= W) {
+  if (wave >= 2 * W) {
     // ---- the copy waves. Copy u of copy wave w fills 1 KB at byte 1024 x,
     // x = NC u + w, of its array: K/Q rows 4x + lane / 16 (stored piece
     // lane % 16), V rows x (1024 / kVB) + lane / kVP (stored piece lane % kVP),
     // record bytes 1024 x + 16 lane; rows past the end of the sequence repeat
     // its last row.
-    const int cw = wave - W;
+    const int cw = wave - 2 * W;
     const uint16_t* kb = k + ((int64_t)b * T * Hqk + hk) * kD;
     const uint16_t* qb = q + ((int64_t)b * T * Hqk + hk) * kD;
     const uint16_t* vb = v + ((int64_t)b * T * Hv + h) * kD + vbase;
@@ -569,44 +580,170 @@ __global__ __launch_bounds__(64 * (W + NC), 1) void gdn_scan_kernel(
     return;
   }
 
-  // ---- the compute waves
+  // ---- the compute waves: set `set`, recurrence (waves 0 .. W-1) or output
+  // (waves W .. 2W-1); one barrier per chunk, as the copy waves. Within a
+  // chunk the recurrence wave hands R to the output wave through r_ready.
+  const bool recur = wave < W;
+  const int set = recur ? wave : wave - W;
   const int grp = lane >> 4, cl = lane & 15;
-  const int d0 = 16 * (W * part + wave);  // this wave's value rows
-  const int dv = d0 + cl;                 // this lane's
+  const int d0 = 16 * (W * part + set);  // this set's value rows
+  const int dv = d0 + cl;                // this lane's
   const int64_t state_base = ((int64_t)b * Hv + h) * kD * kD;
+  // (the barrier does not wait for this wave's LDS writes by itself: the
+  // handed-over state and R must have landed before the other wave reads them)
+  auto barrier = [&]() __attribute__((always_inline)) {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(kLgkmWait0);
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
 
-  // S^T tile mt, value r: state position 16mt + 4grp + r
-  f32x4 S[8];
+  if (recur) {
+    // S^T tile mt, value r: state position 16mt + 4grp + r
+    f32x4 S[8];
 #pragma unroll
-  for (int mt = 0; mt < 8; ++mt) {
+    for (int mt = 0; mt < 8; ++mt) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int pos = 16 * mt + 4 * grp + r;
-      S[mt][r] = S0 ? S0[state_base + (int64_t)dv * kD + 32 * (pos >> 5) + slot_of_acc(pos & 31)] : 0.0f;
+      for (int r = 0; r < 4; ++r) {
+        const int pos = 16 * mt + 4 * grp + r;
+        S[mt][r] = S0 ? S0[state_base + (int64_t)dv * kD + 32 * (pos >> 5) + slot_of_acc(pos & 31)] : 0.0f;
+      }
     }
-  }
-  // B operand of the identity: adds V (this wave's 16 columns of a 32-column block) to an accumulator
-  u32x4 ident;
-  {
-    const int off = 16 * ((d0 >> 4) & 1);
-    uint32_t w[4];
+    // B operand of the identity: adds V (this set's 16 columns of a 32-column block) to an accumulator
+    u32x4 ident;
+    {
+      const int off = 16 * ((d0 >> 4) & 1);
+      uint32_t w[4];
 #pragma unroll
-    for (int x = 0; x < 4; ++x) {
-      const uint32_t lo = (8 * grp + 2 * x == off + cl) ? 0x3F80u : 0u;
-      const uint32_t hi = (8 * grp + 2 * x + 1 == off + cl) ? 0x3F80u : 0u;
-      w[x] = lo | (hi << 16);
+      for (int x = 0; x < 4; ++x) {
+        const uint32_t lo = (8 * grp + 2 * x == off + cl) ? 0x3F80u : 0u;
+        const uint32_t hi = (8 * grp + 2 * x + 1 == off + cl) ? 0x3F80u : 0u;
+        w[x] = lo | (hi << 16);
+      }
+      ident = u32x4{w[0], w[1], w[2], w[3]};
     }
-    ident = u32x4{w[0], w[1], w[2], w[3]};
+    const int vpiece = grp;  // the set's A-operand piece of a (32-column) V row
+    // the state as the B operand (k = dk in natural order, n = dv), also
+    // handed to the output wave
+    u32x4 Sb[4];
+    auto pack_state = [&](int parity) __attribute__((always_inline)) {
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        Sb[ks] = pack_tiles(S[2 * ks], S[2 * ks + 1]);
+        sx[set][parity][ks][lane] = Sb[ks];
+      }
+    };
+    pack_state(0);
+    r_ready[set] = 0;
+    // transposed reads of Kt (row dk, k = token): lane group g takes tokens
+    // 4g + j of the k-step's first and second 16, column lane % 16 of the window
+    const int tro = (4 * grp + (cl >> 2)) * kP + 4 * (cl & 3);
+    auto step = [&](int c, const Stage& s, int parity) __attribute__((always_inline)) {
+      barrier();  // the chunk is in `s`
+      const uint8_t* sK = reinterpret_cast<const uint8_t*>(s.K);
+      const uint8_t* sV = reinterpret_cast<const uint8_t*>(s.V);
+      // X = K S^T and V, tiles of 16 tokens
+      f32x4 X[4], R[4];
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) {
+        const int row = 16 * rt + cl;
+        X[rt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        R[rt] = mfma16(*reinterpret_cast<const u32x4*>(sV + row * kVB + (((vpiece ^ row) & (kVP - 1)) << 4)), ident,
+                       X[rt]);
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+          X[rt] = mfma16(*reinterpret_cast<const u32x4*>(sK + swz16(row, 4 * ks + grp)), Sb[ks], X[rt]);
+      }
+      // R = V - diag(gam) X as the B operand (k = token in accumulator order)
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) {
+        const f32x4 gm = *reinterpret_cast<const f32x4*>(&s.gates[64 + 16 * rt + 4 * grp]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) R[rt][r] -= gm[r] * X[rt][r];
+      }
+      u32x4 Rb[2];
+      Rb[0] = pack_tiles(R[0], R[1]);
+      Rb[1] = pack_tiles(R[2], R[3]);
+      rx[set][0][lane] = Rb[0];
+      rx[set][1][lane] = Rb[1];
+      // R has landed before the flag says so (LDS operations of a wave are
+      // waited for in order)
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_waitcnt(kLgkmWait0);
+      __hip_atomic_store(&r_ready[set], c + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      // S^T = gam_C S^T + Kt^T R
+      const float gC = s.gates[128];
+#pragma unroll
+      for (int mt = 0; mt < 8; ++mt) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) S[mt][r] *= gC;
+      }
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt) {
+          const uint2 lo = ld_tr16(&s.Kt[(32 * kk) * kP + tro + 16 * mt]);
+          const uint2 hi = ld_tr16(&s.Kt[(32 * kk + 16) * kP + tro + 16 * mt]);
+          S[mt] = mfma16(u32x4{lo.x, lo.y, hi.x, hi.y}, Rb[kk], S[mt]);
+        }
+      }
+      pack_state(parity ^ 1);  // the state entering the next chunk
+    };
+    for (int c = 0; c < n_chunks; c += 2) {
+      step(c, st0, 0);
+      if (c + 1 < n_chunks) step(c + 1, st1, 1);
+    }
+    if (S_out) {
+#pragma unroll
+      for (int mt = 0; mt < 8; ++mt) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int pos = 16 * mt + 4 * grp + r;
+          S_out[state_base + (int64_t)dv * kD + 32 * (pos >> 5) + slot_of_acc(pos & 31)] = S[mt][r];
+        }
+      }
+    }
+    return;
   }
-  const int vpiece = 4 * ((d0 - vbase) >> 5) + grp;  // the wave's A-operand piece of a V row
 
-  // outputs: the wave computes O^T, so lane l holds value columns
-  // d0 + 4 (l / 16) .. +3 of token l % 16 of each 16-token tile, stored as 8
-  // bytes; buffer stores whose range ends at the chunk's last token drop the
-  // rest
+  // the output wave: O^T = S Q^T diag(scale gam) + R^T MT^T (the packed state
+  // and R as the A operands, the Q and MT fragments as the B operands), so
+  // lane l holds value columns d0 + 4 (l / 16) .. +3 of token l % 16 of each
+  // 16-token tile, stored as 8 bytes; buffer stores whose range ends at the
+  // chunk's last token drop the rest
   uint16_t* out_base = out + ((int64_t)b * T * Hv + h) * kD + d0;
   const int row_bytes = (int)(v_row * 2);
-  auto store_out = [&](int c, const f32x4* O) __attribute__((always_inline)) {
+  auto step = [&](int c, const Stage& s, int parity) __attribute__((always_inline)) {
+    barrier();  // the chunk is in `s`, its entering state in sx[set][parity]
+    const uint8_t* sQ = reinterpret_cast<const uint8_t*>(s.Q);
+    u32x4 Sb[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) Sb[ks] = sx[set][parity][ks][lane];
+    f32x4 O[4];
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+      const int row = 16 * rt + cl;
+      O[rt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        O[rt] = mfma16(Sb[ks], *reinterpret_cast<const u32x4*>(sQ + swz16(row, 4 * ks + grp)), O[rt]);
+      const float sg = s.gates[16 * rt + cl];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) O[rt][r] *= sg;
+    }
+    // wait for the chunk's R (the recurrence wave always gets there; the
+    // bound only keeps a fault from turning into a hang)
+    for (int spin = 0; spin < (1 << 24); ++spin) {
+      if (__hip_atomic_load(&r_ready[set], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) > c) break;
+      __builtin_amdgcn_s_sleep(1);
+    }
+    asm volatile("" ::: "memory");
+    const u32x4 Rb0 = rx[set][0][lane], Rb1 = rx[set][1][lane];
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+      O[rt] = mfma16(Rb0, *reinterpret_cast<const u32x4*>(&s.MT[(16 * rt + cl) * kMP + 8 * grp]), O[rt]);
+      O[rt] = mfma16(Rb1, *reinterpret_cast<const u32x4*>(&s.MT[(16 * rt + cl) * kMP + 32 + 8 * grp]), O[rt]);
+    }
     const int64_t t0 = (int64_t)c * kC;
     const int n = (int)min<int64_t>(kC, T - t0);
     const __amdgpu_buffer_rsrc_t dst =
@@ -617,89 +754,9 @@ __global__ __launch_bounds__(64 * (W + NC), 1) void gdn_scan_kernel(
       __builtin_amdgcn_raw_buffer_store_b64(val, dst, (16 * rt + cl) * row_bytes + 8 * grp, 0, 0);
     }
   };
-
-  // transposed reads of Kt (row dk, k = token): lane group g takes tokens
-  // 4g + j of the k-step's first and second 16, column lane % 16 of the window
-  const int tro = (4 * grp + (cl >> 2)) * kP + 4 * (cl & 3);
-  auto step = [&](int c, const Stage& s) __attribute__((always_inline)) {
-    __builtin_amdgcn_s_barrier();  // chunk c is in `s`
-    asm volatile("" ::: "memory");
-    const uint8_t* sK = reinterpret_cast<const uint8_t*>(s.K);
-    const uint8_t* sQ = reinterpret_cast<const uint8_t*>(s.Q);
-    const uint8_t* sV = reinterpret_cast<const uint8_t*>(s.V);
-
-    // the state as the B operand (k = dk in natural order, n = dv)
-    u32x4 Sb[4];
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) Sb[ks] = pack_tiles(S[2 * ks], S[2 * ks + 1]);
-    // X = K S^T, O^T = S Q^T (the packed state taken as the A operand, the
-    // same Q fragments as the B operand) and V, tiles of 16 tokens
-    f32x4 X[4], O[4], R[4];
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt) {
-      const int row = 16 * rt + cl;
-      X[rt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-      O[rt] = X[rt];
-      R[rt] = mfma16(*reinterpret_cast<const u32x4*>(sV + row * kVB + (((vpiece ^ row) & (kVP - 1)) << 4)), ident,
-                     X[rt]);
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        X[rt] = mfma16(*reinterpret_cast<const u32x4*>(sK + swz16(row, 4 * ks + grp)), Sb[ks], X[rt]);
-        O[rt] = mfma16(Sb[ks], *reinterpret_cast<const u32x4*>(sQ + swz16(row, 4 * ks + grp)), O[rt]);
-      }
-    }
-    // R = V - diag(gam) X as the B operand (k = token in accumulator order)
-    u32x4 Rb[2];
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt) {
-      const f32x4 gm = *reinterpret_cast<const f32x4*>(&s.gates[64 + 16 * rt + 4 * grp]);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) R[rt][r] -= gm[r] * X[rt][r];
-    }
-    Rb[0] = pack_tiles(R[0], R[1]);
-    Rb[1] = pack_tiles(R[2], R[3]);
-    // S^T = gam_C S^T + Kt^T R
-    const float gC = s.gates[128];
-#pragma unroll
-    for (int mt = 0; mt < 8; ++mt) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) S[mt][r] *= gC;
-    }
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-#pragma unroll
-      for (int mt = 0; mt < 8; ++mt) {
-        const uint2 lo = ld_tr16(&s.Kt[(32 * kk) * kP + tro + 16 * mt]);
-        const uint2 hi = ld_tr16(&s.Kt[(32 * kk + 16) * kP + tro + 16 * mt]);
-        S[mt] = mfma16(u32x4{lo.x, lo.y, hi.x, hi.y}, Rb[kk], S[mt]);
-      }
-    }
-    // O^T = S Q^T diag(scale gam) + R^T MT^T (the packed R as the A operand,
-    // the MT fragments as the B operand)
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt) {
-      const float sg = s.gates[16 * rt + cl];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) O[rt][r] *= sg;
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk)
-        O[rt] = mfma16(Rb[kk], *reinterpret_cast<const u32x4*>(&s.MT[(16 * rt + cl) * kMP + 32 * kk + 8 * grp]), O[rt]);
-    }
-    store_out(c, O);
-  };
   for (int c = 0; c < n_chunks; c += 2) {
-    step(c, st0);
-    if (c + 1 < n_chunks) step(c + 1, st1);
-  }
-  if (S_out) {
-#pragma unroll
-    for (int mt = 0; mt < 8; ++mt) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int pos = 16 * mt + 4 * grp + r;
-        S_out[state_base + (int64_t)dv * kD + 32 * (pos >> 5) + slot_of_acc(pos & 31)] = S[mt][r];
-      }
-    }
+    step(c, st0, 0);
+    if (c + 1 < n_chunks) step(c + 1, st1, 1);
   }
 }
 
@@ -754,8 +811,6 @@ __global__ __launch_bounds__(256) void gdn_decode_kernel(
 }  // namespace
 
 // Compute units of the current device (cached per device).
-constexpr int kScanCopyWaves4 = 2;
-
 static int device_cu_count() {
   static std::atomic<int> cache[64];
   int dev = 0;
@@ -783,21 +838,17 @@ hipError_t launch_gdn_prefill(const uint16_t* q, const uint16_t* k, const uint16
     hipLaunchKernelGGL(gdn_prep_kernel, dim3(grid), dim3(256), 0, stream, q, k, g, beta, T, Hqk, Hv, scale,
                        (int)n_chunks, n_items, reinterpret_cast<uint8_t*>(ws));
   }
-  // waves per scan workgroup: the most that still gives every CU a workgroup
+  // row sets per scan workgroup: two once that still gives every CU a workgroup
   const int64_t rows_sets = (int64_t)batch * Hv;  // (sequence, value head) pairs
-  const int cus = device_cu_count();
-  const int W = rows_sets * 2 >= cus ? 4 : rows_sets * 4 >= cus ? 2 : 1;
+  const int W = rows_sets * 4 >= device_cu_count() ? 2 : 1;
   const unsigned n_wg = (unsigned)(rows_sets * (8 / W));
   const uint8_t* wsb = reinterpret_cast<const uint8_t*>(ws);
-  // copy waves: as many as keep one compute wave fed, two beside two or four
-  if (W == 4)
-    hipLaunchKernelGGL((gdn_scan_kernel<4, kScanCopyWaves4>), dim3(n_wg), dim3(64 * (4 + kScanCopyWaves4)), 0, stream,
-                       q, k, v, S0, T, Hqk, Hv, (int)n_chunks, wsb, out, S_out);
-  else if (W == 2)
-    hipLaunchKernelGGL((gdn_scan_kernel<2, 2>), dim3(n_wg), dim3(64 * (2 + 2)), 0, stream, q, k, v, S0, T, Hqk, Hv,
+  // copy waves: four beside one row set, two beside two
+  if (W == 2)
+    hipLaunchKernelGGL((gdn_scan_kernel<2, 2>), dim3(n_wg), dim3(64 * (4 + 2)), 0, stream, q, k, v, S0, T, Hqk, Hv,
                        (int)n_chunks, wsb, out, S_out);
   else
-    hipLaunchKernelGGL((gdn_scan_kernel<1, 4>), dim3(n_wg), dim3(64 * (1 + 4)), 0, stream, q, k, v, S0, T, Hqk, Hv,
+    hipLaunchKernelGGL((gdn_scan_kernel<1, 4>), dim3(n_wg), dim3(64 * (2 + 4)), 0, stream, q, k, v, S0, T, Hqk, Hv,
                        (int)n_chunks, wsb, out, S_out);
   return hipGetLastError();
 }
