@@ -45,10 +45,12 @@ constexpr int kLP = kC + 8;   // LDS pitch of 64-wide fp32 rows (L)
 // Workspace record of one (sequence, value head, chunk), byte offsets. It is
 // the byte image of the scan's LDS staging of these three arrays (row pitches
 // included), so the scan copies it into LDS with direct global-to-LDS loads.
-constexpr int64_t kRecK = 0;                     // Kt, bf16 [64][kP], dk columns in state order
+constexpr int64_t kRecK = 0;                     // Kt^T, bf16 [128][kMP]: rows dk in state order,
+                                                 // columns tokens in accumulator order
 constexpr int64_t kRecM = kRecK + kC * kP * 2;   // MT, bf16 [64][kMP], columns in accumulator order
 constexpr int64_t kRecG = kRecM + kC * kMP * 2;  // gates, fp32 [256]: scale gam_i | gam_i | gam_C
 constexpr int64_t kRecBytes = kRecG + 256 * 4;   // 28 KB = 7 x 256 threads x 16 B
+static_assert(kD * kMP == kC * kP, "Kt^T fills the record's first part");
 static_assert(kRecBytes == 7 * 256 * 16, "record copied in 7 rounds of 16 B per thread");
 
 // Operand order of the k dimension. An MFMA 32x32x16 k-step takes, in lane
@@ -215,24 +217,30 @@ __global__ __launch_bounds__(256, 2) void gdn_prep_kernel(
         const u32x4 bk = *reinterpret_cast<const u32x4*>(&Ks[(32 * tj + col) * kP + 16 * ks + 8 * half]);
         const u32x4 ak = *reinterpret_cast<const u32x4*>(&Ks[(32 * ti + col) * kP + 16 * ks + 8 * half]);
         const u32x4 aq = *reinterpret_cast<const u32x4*>(&QTs[(32 * ti + col) * kP + 16 * ks + 8 * half]);
-        kk = mfma32x32x16(ak, bk, kk);
-        qk = mfma32x32x16(aq, bk, qk);
+        // the products taken transposed (K rows of tile tj as the A operand):
+        // lane col then holds row i = 32 ti + col of L and M, and accumulator
+        // values 4 qd .. 4 qd + 3 are its columns j = 32 tj + 8 qd + 4 half + 0..3
+        kk = mfma32x32x16(bk, ak, kk);
+        qk = mfma32x32x16(bk, aq, qk);
       }
-      const int j = 32 * tj + col;
-      const float gj = Gs[j];
+      const int i = 32 * ti + col;
+      const float gi = Gs[i], bi = Bs[i];
 #pragma unroll
       for (int qd = 0; qd < 4; ++qd) {
-        // rows 32 ti + 8 qd + 4 half + 0..3 of the tile
-        const int i0 = 32 * ti + 8 * qd + 4 * half;
-        const f32x4 gi = *reinterpret_cast<const f32x4*>(&Gs[i0]);
-        const f32x4 bi = *reinterpret_cast<const f32x4*>(&Bs[i0]);
+        const int j0 = 32 * tj + 8 * qd + 4 * half;
+        const f32x4 gj = *reinterpret_cast<const f32x4*>(&Gs[j0]);
+        f32x4 lv;
+        float mv[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int r = 4 * qd + e, i = i0 + e;
-          const float d = exp_hw(gi[e] - gj);  // only used where j <= i, so the exponent is <= 0
-          Lm[i * kLP + j] = j < i ? bi[e] * d * kk[r] : 0.0f;
-          Mb[i * kMP + perm16(j)] = (uint16_t)f32_to_bf16_bits(j <= i ? scale * d * qk[r] : 0.0f);
+          const int r = 4 * qd + e, j = j0 + e;
+          const float d = exp_hw(gi - gj[e]);  // only used where j <= i, so the exponent is <= 0
+          lv[e] = j < i ? bi * d * kk[r] : 0.0f;
+          mv[e] = j <= i ? scale * d * qk[r] : 0.0f;
         }
+        *reinterpret_cast<f32x4*>(&Lm[i * kLP + j0]) = lv;
+        *reinterpret_cast<uint2*>(&Mb[i * kMP + perm16(j0)]) =
+            make_uint2(pack_bf16x2_hw(mv[0], mv[1]), pack_bf16x2_hw(mv[2], mv[3]));
       }
     } else {
       // the tile above the diagonal (rows 0..31, columns 32..63) of M is zero
@@ -320,10 +328,12 @@ __global__ __launch_bounds__(256, 2) void gdn_prep_kernel(
     }
     __syncthreads();
 
-    // MT = M Tb (wave w: tile (w / 2, w % 2)) and Kt = Td^T K (wave w: columns
-    // 32w .. 32w+31). The record is assembled in LDS in its workspace layout
-    // (Kt over the dead T, MT over M once every wave has read M) and written
-    // out with coalesced 16-byte stores.
+    // MT = M Tb (wave w: tile (w / 2, w % 2), taken transposed so that a lane
+    // holds four consecutive columns of a row) and Kt = Td^T K (wave w: dk
+    // columns 32w .. 32w+31; a lane holds runs of four tokens of one dk, which
+    // go to the record's transposed Kt). The record is assembled in LDS in its
+    // workspace layout (Kt^T over the dead T, MT over M once every wave has
+    // read M) and written out with coalesced 16-byte stores.
     f32x16 mt = f32x16{};
     {
       const int ti = wave >> 1, tj = wave & 1;
@@ -331,11 +341,12 @@ __global__ __launch_bounds__(256, 2) void gdn_prep_kernel(
       for (int ks = 0; ks < 4; ++ks) {
         const u32x4 am = *reinterpret_cast<const u32x4*>(&Mb[(32 * ti + col) * kMP + 16 * ks + 8 * half]);
         const u32x4 bt2 = *reinterpret_cast<const u32x4*>(&TbT[(32 * tj + col) * kMP + 16 * ks + 8 * half]);
-        mt = mfma32x32x16(am, bt2, mt);
+        mt = mfma32x32x16(bt2, am, mt);
       }
     }
     {
-      uint16_t* Ktl = QTs;
+      uint16_t* KtTl = QTs;
+      const int p = 32 * wave + acc_of_slot(col);  // state position of dk 32 wave + col
       const int tro = tr_offset(lane);
 #pragma unroll
       for (int rt = 0; rt < 2; ++rt) {
@@ -348,20 +359,19 @@ __global__ __launch_bounds__(256, 2) void gdn_prep_kernel(
           acc = mfma32x32x16(at, u32x4{lo.x, lo.y, hi.x, hi.y}, acc);
         }
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int j = 32 * rt + acc_row(r, half);
-          Ktl[j * kP + 32 * wave + acc_of_slot(col)] = (uint16_t)f32_to_bf16_bits(acc[r]);
-        }
+        for (int qd = 0; qd < 4; ++qd)
+          *reinterpret_cast<uint2*>(&KtTl[p * kMP + 32 * rt + slot_of_acc(8 * qd + 4 * half)]) = make_uint2(
+              pack_bf16x2_hw(acc[4 * qd], acc[4 * qd + 1]), pack_bf16x2_hw(acc[4 * qd + 2], acc[4 * qd + 3]));
       }
     }
     __syncthreads();
     {
       const int ti = wave >> 1, tj = wave & 1;
+      const int i = 32 * ti + col;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int i = 32 * ti + acc_row(r, half);
-        Mb[i * kMP + 32 * tj + slot_of_acc(col)] = (uint16_t)f32_to_bf16_bits(mt[r]);
-      }
+      for (int qd = 0; qd < 4; ++qd)
+        *reinterpret_cast<uint2*>(&Mb[i * kMP + 32 * tj + slot_of_acc(8 * qd + 4 * half)]) =
+            make_uint2(pack_bf16x2_hw(mt[4 * qd], mt[4 * qd + 1]), pack_bf16x2_hw(mt[4 * qd + 2], mt[4 * qd + 3]));
     }
     __syncthreads();
     static_assert(sizeof(QTs) == kRecM - kRecK && sizeof(Mb) == kRecG - kRecM && sizeof(Rg) == kRecBytes - kRecG,
@@ -400,16 +410,17 @@ __global__ __launch_bounds__(256, 2) void gdn_prep_kernel(
 // into an operand therefore gives lane group g rows {4g .. 4g+3, 16+4g ..
 // 16+4g+3}: the "accumulator order" of each 32 indices (acc_of_slot /
 // slot_of_acc above). State row position q holds dk = slot_of_acc(q), so the
-// packed state meets K and Q in their natural dk order; Kt's columns are
-// stored in state order and MT's columns in accumulator order over the
-// tokens, as prep writes them.
+// packed state meets K and Q in their natural dk order; the record holds Kt
+// transposed (rows dk in state order) and MT, both with their token columns
+// in accumulator order, so the state update and MT R read plain 16-byte
+// rows, as prep writes them.
 // Per chunk, everything the chunk reads is copied straight from memory into
 // LDS (global-to-LDS loads: 16 bytes per lane, written at consecutive
 // addresses from the wave's base), double-buffered so the next chunk's copies
 // are in flight during the current one. K and Q rows (256 bytes) keep their
 // sixteen 16-byte pieces at piece ^ (row % 16), V rows (the staged columns)
 // at piece ^ (row % pieces per row), so a piece of 16 consecutive rows
-// spreads over the banks; the record (Kt, MT, gates) is copied as the image
+// spreads over the banks; the record (Kt^T, MT, gates) is copied as the image
 // prep wrote.
 template <int W>
 struct ScanStage {
@@ -420,7 +431,7 @@ struct ScanStage {
   uint16_t K[kC * kD];
   uint16_t Q[kC * kD];
   uint16_t V[kC * kVC];
-  uint16_t Kt[kC * kP];  // Kt, MT and gates: the workspace record image
+  uint16_t KtT[kD * kMP];  // Kt^T, MT and gates: the workspace record image
   uint16_t MT[kC * kMP];
   float gates[256];
   uint32_t sink[64];  // written by the L2 prefetches, never read
@@ -456,8 +467,8 @@ __global__ __launch_bounds__(64 * (2 * W + NC), 1) void gdn_scan_kernel(
   using Stage = ScanStage<W>;
   constexpr int kVC = Stage::kVC, kVB = 2 * kVC, kVP = kVB / 16;  // V row bytes, 16-byte pieces per row
   constexpr int kParts = 8 / W;
-  static_assert(offsetof(Stage, MT) - offsetof(Stage, Kt) == kRecM - kRecK &&
-                    offsetof(Stage, gates) - offsetof(Stage, Kt) == kRecG - kRecK,
+  static_assert(offsetof(Stage, MT) - offsetof(Stage, KtT) == kRecM - kRecK &&
+                    offsetof(Stage, gates) - offsetof(Stage, KtT) == kRecG - kRecK,
                 "stage holds the record image");
   __shared__ __attribute__((aligned(16))) Stage st0;
   __shared__ __attribute__((aligned(16))) Stage st1;
@@ -497,7 +508,7 @@ __global__ __launch_bounds__(64 * (2 * W + NC), 1) void gdn_scan_kernel(
       const int64_t t0 = (int64_t)c * kC;
       const int n = (int)min<int64_t>(kC, T - t0);
       const uint8_t* rec = recs + (int64_t)c * kRecBytes;
-      uint8_t* img = reinterpret_cast<uint8_t*>(dst.Kt);
+      uint8_t* img = reinterpret_cast<uint8_t*>(dst.KtT);
 #pragma unroll
       for (int u = 0; u < 28 / NC; ++u) {
         const int x = NC * u + cw;
@@ -635,9 +646,6 @@ __global__ __launch_bounds__(64 * (2 * W + NC), 1) void gdn_scan_kernel(
     };
     pack_state(0);
     r_ready[set] = 0;
-    // transposed reads of Kt (row dk, k = token): lane group g takes tokens
-    // 4g + j of the k-step's first and second 16, column lane % 16 of the window
-    const int tro = (4 * grp + (cl >> 2)) * kP + 4 * (cl & 3);
     auto step = [&](int c, const Stage& s, int parity) __attribute__((always_inline)) {
       barrier();  // the chunk is in `s`
       const uint8_t* sK = reinterpret_cast<const uint8_t*>(s.K);
@@ -682,9 +690,8 @@ __global__ __launch_bounds__(64 * (2 * W + NC), 1) void gdn_scan_kernel(
       for (int kk = 0; kk < 2; ++kk) {
 #pragma unroll
         for (int mt = 0; mt < 8; ++mt) {
-          const uint2 lo = ld_tr16(&s.Kt[(32 * kk) * kP + tro + 16 * mt]);
-          const uint2 hi = ld_tr16(&s.Kt[(32 * kk + 16) * kP + tro + 16 * mt]);
-          S[mt] = mfma16(u32x4{lo.x, lo.y, hi.x, hi.y}, Rb[kk], S[mt]);
+          S[mt] = mfma16(*reinterpret_cast<const u32x4*>(&s.KtT[(16 * mt + cl) * kMP + 32 * kk + 8 * grp]), Rb[kk],
+                         S[mt]);
         }
       }
       pack_state(parity ^ 1);  // the state entering the next chunk
