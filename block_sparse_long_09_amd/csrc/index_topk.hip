@@ -153,13 +153,14 @@ __device__ __noinline__ float compact_keys_staged(glb_u64* p, int n, int keep, l
 // is at least L, where L is the lower edge of the histogram bucket that holds
 // the keep-th largest key. The keys are staged in LDS and bucketed by their
 // offset from the smallest key (8 bits per pass below the offsets' leading
-// zeros); a second pass refines the bucket only if more than `limit` entries
-// would survive. At least `keep` entries survive, so the buffer stays a
+// zeros); further passes refine the bucket while more than keep + 64 entries
+// would survive (a tight threshold lets fewer later candidates in, and leaves
+// the buffer room for many before the next compaction). At least `keep` entries survive, so the buffer stays a
 // superset of the exact top `keep`; a later candidate with key <= L can never
 // enter it (at least `keep` entries with key >= L and a smaller block index
 // precede it). Returns L; *kept_out receives the number of entries kept.
-__device__ __noinline__ uint32_t compact_keys_approx(glb_u64* p, int n, int keep, int limit,
-                                                     lds_u32* hist, lds_u32* kstage, int* kept_out) {
+__device__ __noinline__ uint32_t compact_keys_approx(glb_u64* p, int n, int keep, lds_u32* hist,
+                                                     lds_u32* kstage, int* kept_out) {
   const int lane = lane_id();
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
   uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
@@ -193,7 +194,7 @@ __device__ __noinline__ uint32_t compact_keys_approx(glb_u64* p, int n, int keep
   uint32_t need = (uint32_t)keep;
   uint32_t above_all = 0;        // entries above the bucket
   uint32_t ge = (uint32_t)n;     // entries with key >= kbase
-  for (int pass = 0; pass < 2 && hi > 0 && ge > (uint32_t)limit; ++pass) {
+  for (int pass = 0; pass < 4 && hi > 0 && ge > (uint32_t)(keep + 64); ++pass) {
     const int lo = hi > 8 ? hi - 8 : 0;
     for (int i = lane; i < 256; i += kWave) hist[i] = 0;
     wave_sync();
@@ -585,7 +586,7 @@ __global__ __launch_bounds__(256, 2) void index_prefill_kernel(
         const int ch = __builtin_amdgcn_readlane(cs, 32 * hh);
         glb_u64* cb = (glb_u64*)buf_of(slot_query(s, hh));
         int kept;
-        uint32_t L = compact_keys_approx(cb, ch, keep, cap - 2 * TILE, hist_l, kstage_l, &kept);
+        uint32_t L = compact_keys_approx(cb, ch, keep, hist_l, kstage_l, &kept);
         if (kept > cap - 2 * TILE) {
           // the threshold's bucket is too full (many equal keys): compact exactly
           L = __float_as_uint(compact_keys_staged(cb, kept, keep, hist_l, kstage_l));
