@@ -20,9 +20,10 @@
 // factor exceeds 1. MT, Kt and the gates depend only on the chunk's own
 // tokens: gdn_prep_kernel computes them for every chunk in parallel. Then
 // gdn_scan_kernel walks the chunks of each (sequence, value head) in order,
-// carrying S in registers (four waves split the 128 value rows); per chunk it
-// forms X = K S^T and Q S^T, R = V - gam X, O, and the new state: the chain
-// from one state to the next is two products deep.
+// the 128 value rows (independent recurrences) split over workgroups in sets
+// of 16: per chunk a set's recurrence wave forms X = K S^T, R = V - gam X and
+// the new state (the chain from one state to the next is two products deep)
+// and its output wave forms O from the state and R handed over in LDS.
 // Decode (one token on a carried state) is gdn_decode_kernel: the recurrence
 // itself, one pass over the fp32 state in HBM.
 #include <algorithm>
@@ -78,11 +79,6 @@ __device__ __forceinline__ uint2 ld_tr16(const uint16_t* p) {
   return __builtin_bit_cast(uint2, v);
 }
 
-__device__ __forceinline__ void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-}
-
 // Offset (elements) of the transposed 64 x 16 read of a token-major tile with
 // pitch kP: lane group gr = lane / 16 covers columns +16 (gr % 2) of a
 // 32-column window and tokens +4 (gr / 2); source lane 4j + x addresses token
@@ -104,18 +100,9 @@ __device__ __forceinline__ int slot_of_acc(int x) {
   return x < 16 ? 8 * (x >> 2) + (x & 3) : 8 * ((x - 16) >> 2) + 4 + (x & 3);
 }
 
-// Pack 8 fp32 accumulator values (slots 8u .. 8u+7 of a tile) as bf16 pairs.
-__device__ __forceinline__ u32x4 pack8(const f32x16& x, int u) {
-  return u32x4{pack_bf16x2_hw(x[8 * u + 0], x[8 * u + 1]), pack_bf16x2_hw(x[8 * u + 2], x[8 * u + 3]),
-               pack_bf16x2_hw(x[8 * u + 4], x[8 * u + 5]), pack_bf16x2_hw(x[8 * u + 6], x[8 * u + 7])};
-}
-
 // exp(x) for x <= 0 on the hardware exp2 (about 1 ulp; the factors it makes
 // are rounded to bf16 or multiply fp32 products).
 __device__ __forceinline__ float exp_hw(float x) { return __builtin_amdgcn_exp2f(x * 1.4426950408889634f); }
-
-// Row of accumulator value r (0..15) in a 32-row tile, for lane half `half`.
-__device__ __forceinline__ int acc_row(int r, int half) { return 8 * (r >> 2) + 4 * half + (r & 3); }
 
 // ---------------------------------------------------------------- prep ----
 // Persistent: each workgroup (4 waves) takes (chunk, value head, sequence)
@@ -403,8 +390,8 @@ __global__ __launch_bounds__(256, 2) void gdn_prep_kernel(
 // neighbouring heads, which share a key head) are given consecutive
 // workgroup slots of one XCD, so the chunk data they all copy is fetched once
 // into that XCD's L2.
-// A wave holds its rows transposed (S^T, dk x 16) in eight 16 x 16
-// accumulator tiles of the 16x16x32 MFMA. Lane l of such a tile holds rows
+// A recurrence wave holds its set's rows transposed (S^T, dk x 16) in eight
+// 16 x 16 accumulator tiles of the 16x16x32 MFMA. Lane l of such a tile holds rows
 // 4(l/16) + r, r = 0..3, of column l % 16; a k-step reads, in lane group
 // g = l/16, the eight k indices 8g .. 8g+7. Packing two row-adjacent tiles
 // into an operand therefore gives lane group g rows {4g .. 4g+3, 16+4g ..
@@ -444,11 +431,11 @@ __device__ __forceinline__ f32x4 mfma16(const u32x4& a, const u32x4& b, const f3
 // Byte offset of 16-byte piece p of row i in a swizzled tile of 256-byte rows.
 __device__ __forceinline__ int swz16(int i, int p) { return i * 256 + (((p ^ i) & 15) << 4); }
 
-// s_waitcnt immediate that waits until at most n (< 64) vector memory
-// operations are outstanding and does not wait on the other counters.
 // Word 3 of a raw buffer resource (32-bit data format, no swizzle).
 constexpr int kBufferFlags = 0x00020000;
 
+// s_waitcnt immediate that waits until at most n (< 64) vector memory
+// operations are outstanding and does not wait on the other counters.
 constexpr int vmcnt_wait(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
 // s_waitcnt immediate that waits for every LDS operation of the wave and
 // does not wait on the other counters.
@@ -470,6 +457,8 @@ __global__ __launch_bounds__(64 * (2 * W + NC), 1) void gdn_scan_kernel(
   static_assert(offsetof(Stage, MT) - offsetof(Stage, KtT) == kRecM - kRecK &&
                     offsetof(Stage, gates) - offsetof(Stage, KtT) == kRecG - kRecK,
                 "stage holds the record image");
+  // the two chunk stages, each named statically by the chunk loops (unrolled
+  // by two)
   __shared__ __attribute__((aligned(16))) Stage st0;
   __shared__ __attribute__((aligned(16))) Stage st1;
   // handed from a set's recurrence wave to its output wave: the packed state
@@ -480,7 +469,7 @@ __global__ __launch_bounds__(64 * (2 * W + NC), 1) void gdn_scan_kernel(
   __shared__ int r_ready[W];  // chunks whose R has been handed over, per set
 
   const int tid = threadIdx.x;
-  // the wave index as a scalar: the copy wave and the compute waves take
+  // the wave index as a scalar: copy, recurrence and output waves take
   // different paths, each wave as a whole (their barriers pair up one per chunk)
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
