@@ -465,6 +465,7 @@ __global__ __launch_bounds__(256, 2) void index_prefill_kernel(
   __shared__ __attribute__((aligned(16))) unsigned char ring[NSLOT * TILE_BYTES];
   __shared__ uint32_t hist_all[4][256];
   __shared__ int wg_lim[4];
+  __shared__ int wg_compact;  // tile before which every wave compacts its fuller buffers
   extern __shared__ uint32_t kstage_all[];  // 4 x cap keys: each wave's compaction stage
 
   const int tid = threadIdx.x;
@@ -521,6 +522,7 @@ __global__ __launch_bounds__(256, 2) void index_prefill_kernel(
   }
   minlim = __builtin_amdgcn_readfirstlane(minlim);  // wave-uniform after the reduction
   if (lane == 0) wg_lim[wave] = maxlim;
+  if (tid == 0) wg_compact = -1;
   __syncthreads();
   const int wg_max = max(max(wg_lim[0], wg_lim[1]), max(wg_lim[2], wg_lim[3]));
 
@@ -602,7 +604,16 @@ __global__ __launch_bounds__(256, 2) void index_prefill_kernel(
         }
       }
     };
+    bool pending = false;  // this wave must compact before its next tile
     auto process = [&](int t, int slot) {
+      // A compaction one wave asked for while processing the previous tile is
+      // done by every wave at once, each compacting its buffers past a lower
+      // mark (they fill at similar rates): otherwise the waves would wait for
+      // each other at the tile barriers one compaction at a time. The wave
+      // that asked compacts for certain (another may already have moved the
+      // flag on); for the others the invitation is optional.
+      if (pending || wg_compact == t) compact_over(max(cap - 12 * TILE, cap / 2));
+      pending = false;
       const unsigned char* sl = ring + slot * TILE_BYTES;
       bool appended = false;
 #pragma unroll
@@ -668,7 +679,10 @@ __global__ __launch_bounds__(256, 2) void index_prefill_kernel(
         bool over = false;
 #pragma unroll
         for (int s = 0; s < NS; ++s) over |= cnt[s] > cap - TILE;
-        if (ballot(over)) compact_over(cap - TILE);
+        if (ballot(over)) {
+          pending = true;
+          if (lane == 0) wg_compact = t + 1;  // before the next tile (all waves read it after its barrier)
+        }
       }
     };
     // PF register sets and PF LDS slots: iteration t stores tile t + 1 (loaded
