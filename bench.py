@@ -140,8 +140,8 @@ def main():
                     help="token budget k*r of a variant run (default: the workload's, 2048)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU; --gpus {args.gpus} is not supported "
-              "(the path shards by sequence or query chunk, see DESIGN.md, but no multi-GPU run exists)",
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
+              "(the path would shard by sequence or query chunk; no multi-GPU run exists)",
               file=sys.stderr)
         sys.exit(2)
 
