@@ -10,9 +10,13 @@ Default workload: the 1M-token context configuration. One step =
                  query sits at position 1,048,575 (caches [4,1M,4,128], block
                  keys precomputed).
 All inputs are seeded synthetic tensors resident in HBM before timing starts.
-Prints one JSON line (see README of the fields in the design doc).
+Prints one JSON line: the metric and its value, per-phase times, the roofline
+of the dominant kernel (achieved over peak, and the HBM traffic its counters
+measured), the oracle's rate on a bounded sample of the same workload, and
+the sampled parity of the timed outputs.
 
-  python bench.py [--gpus 1] [--steps K] [--warmup W] [--config c5|c3|c4]
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--config c5|c3|c4|c6]
+  python bench.py --gdn | --kl       # gated delta rule; distillation loss
 """
 import argparse
 import hashlib
