@@ -9,7 +9,7 @@
 // Kept: the min(k - 1, b_t) best blocks j < b_t = t / r in (score desc,
 // index asc) order, plus b_t itself; emitted in ascending block order.
 //
-// Prefill (many queries per sequence):
+// Prefill, few queries per sequence (n_q < 64):
 //   index_stream_kernel: one wave owns QW consecutive queries (128 indexer rows
 //   = QW x H_i) and one candidate range ("split"). It streams the block keys
 //   in tiles of 32 through v_mfma_f32_32x32x16_bf16 (A = query rows held in
@@ -24,17 +24,22 @@
 //   so a later candidate that only ties the threshold can never displace a
 //   kept one: the buffer always holds a superset of the split's exact
 //   top-(k-1). Each split ends compacted to at most k-1 entries.
-//   index_select_kernel: one workgroup per query merges the split buffers
-//   (already in block order) in LDS, selects exactly and writes the output.
+// Prefill, many queries (n_q >= 64): index_prefill_kernel, the same scoring
+//   and buffers with workgroups of compute waves that share LDS tiles of block
+//   keys filled by a copy wave, and approximate compactions (see there).
+// Both end in index_select_kernel: one workgroup per query merges the split
+//   buffers (already in block order) in LDS, selects exactly and writes the
+//   output.
 //
 // Decode (one query per sequence):
-//   index_decode_scan_kernel: one wave per 1024-candidate split of one
-//   sequence streams the block keys (HBM bound), writes every score to the
-//   workspace, and keeps the split's exact top-32 plus the key of its best
-//   omitted candidate.
+//   index_decode_scan_kernel: one 8-wave workgroup per 2048-candidate split of
+//   one sequence streams the block keys (HBM bound), writes every score to the
+//   workspace and lists the split's entries at or above the lower edge of the
+//   histogram bucket holding its list_min-th largest key, with the largest
+//   key it left out.
 //   index_decode_select_kernel: one workgroup per sequence selects the top
 //   (k-1) of the union of the split lists. The result is exact when every
-//   split's best omitted score is below the selected threshold; otherwise the
+//   split's largest omitted key is below the selected threshold; otherwise the
 //   workgroup selects exactly from the stored scores of all candidates.
 #include "qsa_device.h"
 #include "qsa_internal.h"
@@ -158,9 +163,10 @@ __device__ __noinline__ float compact_keys_staged(glb_u64* p, int n, int keep, l
 // the buffer room for many before the next compaction). At least `keep` entries survive, so the buffer stays a
 // superset of the exact top `keep`; a later candidate with key <= L can never
 // enter it (at least `keep` entries with key >= L and a smaller block index
-// precede it). Returns L; *kept_out receives the number of entries kept.
-__device__ __noinline__ uint32_t compact_keys_approx(glb_u64* p, int n, int keep, lds_u32* hist,
-                                                     lds_u32* kstage, int* kept_out) {
+// precede it). Returns (L, the number of entries kept); a pair by value keeps
+// the caller free of private (scratch) memory.
+__device__ __noinline__ uint2 compact_keys_approx(glb_u64* p, int n, int keep, lds_u32* hist,
+                                                  lds_u32* kstage) {
   const int lane = lane_id();
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
   uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
@@ -234,8 +240,7 @@ __device__ __noinline__ uint32_t compact_keys_approx(glb_u64* p, int n, int keep
   }
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
   wave_sync();
-  *kept_out = kept;
-  return L;
+  return make_uint2(L, (uint32_t)kept);
 }
 
 }  // namespace
@@ -436,19 +441,29 @@ __global__ __launch_bounds__(256) void index_stream_kernel(
   }
 }
 
-// Prefill indexer for many queries per sequence (n_q >= 64): a workgroup of 4
-// waves (4 x QW queries) shares one candidate split. Block keys travel
-// HBM -> registers (one 64-candidate tile ahead) -> a 2-slot LDS ring
-// (XOR-swizzled 16-byte parts so the B-fragment reads hit distinct banks) ->
-// B fragments; one barrier per tile. Per query: running exact threshold and a
-// (score, block) buffer as in index_stream_kernel; a wave compacts its own
-// buffers (keys staged in its LDS area) when one nears capacity. Splits end
-// with at most `cap` entries; the select kernel takes them as they are.
-#ifndef QSA_PREFILL_PREFETCH
-#define QSA_PREFILL_PREFETCH 2  // 64-candidate tiles in flight in registers
-#endif
-template <int HI, int AT, bool SCALE_EPI>
-__global__ __launch_bounds__(256, 2) void index_prefill_kernel(
+// Prefill indexer for many queries per sequence (n_q >= 64): a workgroup of 8
+// compute waves (8 x QW queries) and one copy wave shares one candidate split,
+// one workgroup per CU (two compute waves per SIMD).
+// Block keys go HBM -> LDS directly (global_load_lds, issued by the copy wave
+// kPrefillDepth 64-candidate tiles ahead into a 4-slot ring, XOR-swizzled
+// 16-byte parts so the B-fragment reads hit distinct banks) -> B fragments;
+// one barrier per tile. Only the copy wave loads tiles and it waits on its own
+// counter alone: the compute waves' appends (global stores) are never waited
+// for before a tile is in place, as they would be if the compute waves loaded
+// the tiles (the memory counter is in order and counts stores too).
+// Per query: running threshold and a (score, block) buffer as in
+// index_stream_kernel; a wave compacts its own buffers (keys staged in its LDS
+// area) when one nears capacity. Splits end with at most `cap` entries; the
+// select kernel takes them as they are.
+constexpr int kPrefillDepth = 2;      // tiles the copy wave keeps in flight
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void glb_void_t;
+// s_waitcnt immediate: at most n (< 64) vector memory operations outstanding,
+// no wait on the other counters
+constexpr int prefill_vmcnt(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
+template <int HI, int AT, bool SCALE_EPI, int NW>
+__global__ __launch_bounds__(64 * (NW + 1)) __attribute__((amdgpu_waves_per_eu(NW == 4 ? 4 : 3)))
+void index_prefill_kernel(
     const uint16_t* __restrict__ idx_q, const uint16_t* __restrict__ cmp_k, int64_t cmp_stride,
     const int32_t* __restrict__ q_pos0, int n_q, int r, int keep, float a_scale, float w_epi,
     int n_qgroups, int splits, int split_len, int cap, uint2* __restrict__ buf,
@@ -459,25 +474,28 @@ __global__ __launch_bounds__(256, 2) void index_prefill_kernel(
   constexpr int NS = AT * QPH;
   constexpr int TILE = 64;                       // candidates per LDS tile
   constexpr int TILE_BYTES = TILE * 128;         // 8 KiB
-  constexpr int PF = QSA_PREFILL_PREFETCH;
-  static_assert(PF >= 2, "the LDS ring needs two slots at least");
-  constexpr int NSLOT = PF;                      // LDS slots
+  constexpr int PF = kPrefillDepth;
+  constexpr int NSLOT = 3;                       // LDS slots
+  static_assert(NSLOT >= PF + 1, "a slot is refilled only after its tile was processed");
   __shared__ __attribute__((aligned(16))) unsigned char ring[NSLOT * TILE_BYTES];
-  __shared__ uint32_t hist_all[4][256];
-  __shared__ int wg_lim[4];
+  __shared__ uint32_t hist_all[NW][256];
+  __shared__ int wg_lim[NW];
   __shared__ int wg_compact;  // tile before which every wave compacts its fuller buffers
   extern __shared__ uint32_t kstage_all[];  // 4 x cap keys: each wave's compaction stage
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // 4: the copy wave
+  const bool copier = wave == NW;
   const int lane = tid & 63;
   const int half = lane >> 5;
   const int col = lane & 31;
-  const int qg = blockIdx.x * 4 + wave;
+  // the last queries see the most candidates: their workgroups go out first,
+  // so the short ones fill in behind them when the grid takes several rounds
+  const int qg = (gridDim.x - 1 - blockIdx.x) * NW + wave;
   const int split = blockIdx.y;
   const int b = blockIdx.z;
-  lds_u32* hist_l = (lds_u32*)hist_all[wave];
-  lds_u32* kstage_l = (lds_u32*)(kstage_all + wave * cap);
+  lds_u32* hist_l = (lds_u32*)hist_all[copier ? 0 : wave];
+  lds_u32* kstage_l = (lds_u32*)(kstage_all + (copier ? 0 : wave) * cap);
 
   const int64_t pos0 = q_pos0[b];
   // this sequence's query rows: [row0, row0 + nqb) (packed rows when cu_q is given)
@@ -489,7 +507,7 @@ __global__ __launch_bounds__(256, 2) void index_prefill_kernel(
   auto buf_of = [&](int qi) {
     return buf + (((int64_t)b * n_q + qi) * splits + split) * (int64_t)cap;
   };
-  const bool wave_live = qg < n_qgroups;
+  const bool wave_live = !copier && qg < n_qgroups;
   // candidates of query qi in this split: [sbeg, lim_of(qi))
   auto lim_of = [&](int qi) {
     const int64_t bt = (pos0 + qi) / r;
@@ -521,14 +539,16 @@ __global__ __launch_bounds__(256, 2) void index_prefill_kernel(
     minlim = min(minlim, __shfl_xor(minlim, off));
   }
   minlim = __builtin_amdgcn_readfirstlane(minlim);  // wave-uniform after the reduction
-  if (lane == 0) wg_lim[wave] = maxlim;
+  if (lane == 0 && !copier) wg_lim[wave] = maxlim;
   if (tid == 0) wg_compact = -1;
   __syncthreads();
-  const int wg_max = max(max(wg_lim[0], wg_lim[1]), max(wg_lim[2], wg_lim[3]));
+  int wg_max = wg_lim[0];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) wg_max = max(wg_max, wg_lim[w]);
 
   if (keep > 0 && wg_max > sbeg) {
     u32x4 A[AT][4];
-    {
+    if (!copier) {
       const int m = col;
       const int i = 4 * (m >> 3) + (m & 3);
       const int hh = (m >> 2) & 1;
@@ -550,22 +570,19 @@ __global__ __launch_bounds__(256, 2) void index_prefill_kernel(
     }
     const unsigned char* kb = reinterpret_cast<const unsigned char*>(cmp_k + (int64_t)b * cmp_stride);
     const int ntiles = (wg_max - sbeg + TILE - 1) / TILE;
-    // this thread's two 16-byte parts of every tile: chunk c = tid + 256u,
-    // candidate row c / 8, part c % 8, stored at part (c % 8) ^ (row % 8)
-    auto load_tile = [&](int t, u32x4* R) {
+    // Tile t goes to LDS slot t % NSLOT, written by the copy wave's eight
+    // 1 KiB global_load_lds: piece u of lane l lands at byte 1024u + 16l of the
+    // slot, i.e. row 8u + l / 8, part l % 8, and carries the row's global part
+    // (l % 8) ^ (row % 8). Rows past the workgroup's last candidate read that
+    // candidate instead, so every load is in bounds.
+    auto issue_tile = [&](int t) __attribute__((always_inline)) {
+      unsigned char* dst = ring + (t % NSLOT) * TILE_BYTES;
+      const int part = (lane & 7) ^ (lane >> 3);
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int c = tid + 256 * u;
-        const int row = min(sbeg + t * TILE + (c >> 3), wg_max - 1);
-        R[u] = *reinterpret_cast<const u32x4*>(kb + (int64_t)row * 128 + (c & 7) * 16);
-      }
-    };
-    auto store_tile = [&](int slot, const u32x4* R) {
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int c = tid + 256 * u;
-        const int row = c >> 3;
-        *reinterpret_cast<u32x4*>(ring + slot * TILE_BYTES + row * 128 + (((c & 7) ^ (row & 7)) * 16)) = R[u];
+      for (int u = 0; u < 8; ++u) {
+        const int row = min(sbeg + t * TILE + 8 * u + (lane >> 3), wg_max - 1);
+        __builtin_amdgcn_global_load_lds((glb_void_t*)(kb + (int64_t)row * 128 + part * 16),
+                                         (lds_void_t*)(dst + 1024 * u), 16, 0, 0);
       }
     };
     // compact this wave's buffers holding more than `limit` entries
@@ -587,8 +604,9 @@ __global__ __launch_bounds__(256, 2) void index_prefill_kernel(
           if (s2 == s) cs = cnt[s2];
         const int ch = __builtin_amdgcn_readlane(cs, 32 * hh);
         glb_u64* cb = (glb_u64*)buf_of(slot_query(s, hh));
-        int kept;
-        uint32_t L = compact_keys_approx(cb, ch, keep, hist_l, kstage_l, &kept);
+        const uint2 lk = compact_keys_approx(cb, ch, keep, hist_l, kstage_l);
+        uint32_t L = lk.x;
+        int kept = (int)lk.y;
         if (kept > cap - 2 * TILE) {
           // the threshold's bucket is too full (many equal keys): compact exactly
           L = __float_as_uint(compact_keys_staged(cb, kept, keep, hist_l, kstage_l));
@@ -685,24 +703,26 @@ __global__ __launch_bounds__(256, 2) void index_prefill_kernel(
         }
       }
     };
-    // PF register sets and PF LDS slots: iteration t stores tile t + 1 (loaded
-    // PF - 1 iterations earlier), issues the load of tile t + PF and computes
-    // tile t; slot / set of tile t = t % PF, one barrier per iteration.
-    u32x4 R[PF][2];
+    // Iteration t opens with barrier B_t, after which the compute waves process
+    // tile t. The copy wave issues tile t + PF right after B_t, into the slot
+    // of tile t + PF - NSLOT <= t - 1 (processed before B_t), and before B_t
+    // waits until tile t has landed: the memory counter is in order and the
+    // 8 loads of each of tiles t + 1 .. t + PF - 1 were issued after it.
+    // Loads are issued for every t (past the end they reread the last
+    // candidate), so that count holds to the end.
+    if (copier) {
 #pragma unroll
-    for (int p = 0; p < PF; ++p)
-      if (p < ntiles) load_tile(p, R[p]);
-    store_tile(0, R[0]);
-    for (int t0 = 0; t0 < ntiles; t0 += PF) {
-#pragma unroll
-      for (int ph = 0; ph < PF; ++ph) {
-        const int t = t0 + ph;
-        if (t < ntiles) {
-          __syncthreads();
-          if (t + 1 < ntiles) store_tile((ph + 1) % PF, R[(ph + 1) % PF]);
-          if (t + PF < ntiles) load_tile(t + PF, R[ph]);
-          process(t, ph);
-        }
+      for (int t = 0; t < PF; ++t) issue_tile(t);
+      for (int t = 0; t < ntiles; ++t) {
+        __builtin_amdgcn_s_waitcnt(prefill_vmcnt(8 * (PF - 1)));
+        __builtin_amdgcn_s_barrier();
+        issue_tile(t + PF);
+      }
+      __builtin_amdgcn_s_waitcnt(prefill_vmcnt(0));  // no copy into LDS outlives the workgroup
+    } else {
+      for (int t = 0; t < ntiles; ++t) {
+        __syncthreads();
+        process(t, t % NSLOT);
       }
     }
   }
@@ -1082,18 +1102,24 @@ IndexPlan plan_index(int hi, int k, int batch, int n_q, int64_t max_q_end, int r
   p.decode = false;
   p.wide = n_q >= 64;
   // A tiles per wave in the LDS-pipelined kernel (8 query slots per lane, or
-  // 4 at 8 heads: 144 VGPRs instead of 219 lets 3 workgroups share a CU)
+  // 4 at 8 heads)
   p.at = p.wide ? (hi == 16 ? 4 : (hi == 8 ? 2 : (hi == 4 ? 2 : 1))) : 1;
+  // Compute waves per workgroup (plus one copy wave). Two 5-wave workgroups
+  // share a CU only when each takes at most 64 KiB of LDS and 128 VGPRs (both
+  // put two waves on one SIMD): true at 8 heads. Otherwise one 9-wave
+  // workgroup per CU (168 VGPRs).
+  p.nw = hi == 8 ? 4 : 8;
   p.qw = p.at * 32 / hi;
   p.n_qgroups = (n_q + p.qw - 1) / p.qw;
   int64_t splits;
   if (p.wide) {
-    // workgroups of 4 query groups; about two workgroups per CU in one round.
+    // workgroups of kPrefillWaves query groups; about one workgroup per CU in one round.
     // A packed batch (allow_decode false) sizes n_q for its longest sequence
     // and most other workgroups are empty: size the splits for one sequence.
-    const int64_t n_wg = ((int64_t)p.n_qgroups + 3) / 4;
+    const int64_t n_wg = ((int64_t)p.n_qgroups + p.nw - 1) / p.nw;
     const int64_t busy = allow_decode ? batch * n_wg : n_wg;
-    splits = (512 + busy - 1) / busy;
+    const int64_t slots = p.nw == 4 ? 512 : 256;  // workgroups the GPU holds at once
+    splits = (slots + busy - 1) / busy;
     const int64_t max_splits = (max_cand + 1023) / 1024;
     if (splits > max_splits) splits = max_splits;
   } else {
@@ -1117,8 +1143,8 @@ IndexPlan plan_index(int hi, int k, int batch, int n_q, int64_t max_q_end, int r
   p.buf_bytes = (size_t)batch * n_q * p.splits * (size_t)cap * sizeof(uint2);
   p.cnt_bytes = (size_t)batch * n_q * p.splits * sizeof(int);
   p.workspace = p.buf_bytes + ((p.cnt_bytes + 255) / 256 * 256);
-  // LDS per workgroup: the wide kernel stages 4 x cap keys, the other 4 x cap entries
-  p.stream_lds = (size_t)4 * cap * (p.wide ? sizeof(uint32_t) : sizeof(uint2));
+  // LDS per workgroup: the wide kernel stages nw x cap keys, the other 4 x cap entries
+  p.stream_lds = p.wide ? (size_t)p.nw * cap * sizeof(uint32_t) : (size_t)4 * cap * sizeof(uint2);
   // the wide kernel leaves up to `cap` entries per split; the other at most `keep`
   p.select_lds = (size_t)p.splits * (p.wide ? cap : (keep > 0 ? keep : 1)) * sizeof(uint2);
   return p;
@@ -1159,18 +1185,19 @@ hipError_t launch_index_topk(const IndexPlan& p, const uint16_t* idx_q, const ui
   uint2* buf = reinterpret_cast<uint2*>(wsb);
   int* cnt = reinterpret_cast<int*>(wsb + p.buf_bytes);
   if (p.wide) {
-    const dim3 g1((p.n_qgroups + 3) / 4, p.splits, batch);
-#define QSA_LAUNCH_PREFILL(HI_, AT_)                                                               \
-  hipLaunchKernelGGL((exact_scale ? index_prefill_kernel<HI_, AT_, false>                        \
-                                  : index_prefill_kernel<HI_, AT_, true>), g1, dim3(256), p.stream_lds, stream, idx_q, cmp_k,  \
+    const dim3 g1((p.n_qgroups + p.nw - 1) / p.nw, p.splits, batch);
+#define QSA_LAUNCH_PREFILL(HI_, AT_, NW_)                                                           \
+  hipLaunchKernelGGL((exact_scale ? index_prefill_kernel<HI_, AT_, false, NW_>                   \
+                                  : index_prefill_kernel<HI_, AT_, true, NW_>), g1, dim3(64 * (NW_ + 1)), p.stream_lds, \
+                     stream, idx_q, cmp_k,                                                         \
                      cmp_stride, q_pos0, n_q, r, k - 1, a_scale, w_epi, p.n_qgroups, p.splits,     \
                      p.split_len, p.cap, buf, cnt, cu_q)
     switch (p.hi) {
-      case 1: QSA_LAUNCH_PREFILL(1, 1); break;
-      case 2: QSA_LAUNCH_PREFILL(2, 1); break;
-      case 4: QSA_LAUNCH_PREFILL(4, 2); break;
-      case 8: QSA_LAUNCH_PREFILL(8, 2); break;
-      case 16: QSA_LAUNCH_PREFILL(16, 4); break;
+      case 1: QSA_LAUNCH_PREFILL(1, 1, 8); break;
+      case 2: QSA_LAUNCH_PREFILL(2, 1, 8); break;
+      case 4: QSA_LAUNCH_PREFILL(4, 2, 8); break;
+      case 8: QSA_LAUNCH_PREFILL(8, 2, 4); break;
+      case 16: QSA_LAUNCH_PREFILL(16, 4, 8); break;
       default: return hipErrorInvalidValue;
     }
 #undef QSA_LAUNCH_PREFILL

@@ -17,6 +17,7 @@ struct IndexPlan {
   bool wide;       // >= 64 queries per sequence: LDS-pipelined workgroup kernel
   int hi;          // indexer heads
   int at;          // 32-row A tiles per wave (4 for prefill, 1 for few queries)
+  int nw;          // wide kernel: compute waves per workgroup (4: two workgroups per CU, 8: one)
   int qw;          // queries per wave
   int n_qgroups;   // query groups per sequence
   int splits;      // candidate splits
