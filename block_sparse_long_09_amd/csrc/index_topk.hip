@@ -441,11 +441,12 @@ __global__ __launch_bounds__(256) void index_stream_kernel(
   }
 }
 
-// Prefill indexer for many queries per sequence (n_q >= 64): a workgroup of 8
-// compute waves (8 x QW queries) and one copy wave shares one candidate split,
-// one workgroup per CU (two compute waves per SIMD).
+// Prefill indexer for many queries per sequence (n_q >= 64): a workgroup of NW
+// compute waves (NW x QW queries; NW = 4, 3 or 8, chosen with the number of
+// workgroups a CU holds, see plan_index) and one copy wave shares one
+// candidate split.
 // Block keys go HBM -> LDS directly (global_load_lds, issued by the copy wave
-// kPrefillDepth 64-candidate tiles ahead into a 4-slot ring, XOR-swizzled
+// kPrefillDepth 64-candidate tiles ahead into a 3-slot ring, XOR-swizzled
 // 16-byte parts so the B-fragment reads hit distinct banks) -> B fragments;
 // one barrier per tile. Only the copy wave loads tiles and it waits on its own
 // counter alone: the compute waves' appends (global stores) are never waited
@@ -1106,9 +1107,12 @@ IndexPlan plan_index(int hi, int k, int batch, int n_q, int64_t max_q_end, int r
   p.at = p.wide ? (hi == 16 ? 4 : (hi == 8 ? 2 : (hi == 4 ? 2 : 1))) : 1;
   // Compute waves per workgroup (plus one copy wave). Two 5-wave workgroups
   // share a CU only when each takes at most 64 KiB of LDS and 128 VGPRs (both
-  // put two waves on one SIMD): true at 8 heads. Otherwise one 9-wave
-  // workgroup per CU (168 VGPRs).
-  p.nw = hi == 8 ? 4 : 8;
+  // put two waves on one SIMD): true at 8 heads, where a uniform batch then
+  // fills every CU with exactly two. A packed batch of unequal sequences runs
+  // many workgroups of unequal length over several rounds; there three 4-wave
+  // workgroups per CU (3 compute waves each, 51 KiB) keep more of them in
+  // flight. Other head counts: one 9-wave workgroup per CU (168 VGPRs).
+  p.nw = hi == 8 ? (allow_decode ? 4 : 3) : 8;
   p.qw = p.at * 32 / hi;
   p.n_qgroups = (n_q + p.qw - 1) / p.qw;
   int64_t splits;
@@ -1118,7 +1122,7 @@ IndexPlan plan_index(int hi, int k, int batch, int n_q, int64_t max_q_end, int r
     // and most other workgroups are empty: size the splits for one sequence.
     const int64_t n_wg = ((int64_t)p.n_qgroups + p.nw - 1) / p.nw;
     const int64_t busy = allow_decode ? batch * n_wg : n_wg;
-    const int64_t slots = p.nw == 4 ? 512 : 256;  // workgroups the GPU holds at once
+    const int64_t slots = p.nw == 4 ? 512 : (p.nw == 3 ? 768 : 256);  // workgroups the GPU holds at once
     splits = (slots + busy - 1) / busy;
     const int64_t max_splits = (max_cand + 1023) / 1024;
     if (splits > max_splits) splits = max_splits;
@@ -1196,7 +1200,7 @@ hipError_t launch_index_topk(const IndexPlan& p, const uint16_t* idx_q, const ui
       case 1: QSA_LAUNCH_PREFILL(1, 1, 8); break;
       case 2: QSA_LAUNCH_PREFILL(2, 1, 8); break;
       case 4: QSA_LAUNCH_PREFILL(4, 2, 8); break;
-      case 8: QSA_LAUNCH_PREFILL(8, 2, 4); break;
+      case 8: if (p.nw == 3) QSA_LAUNCH_PREFILL(8, 2, 3); else QSA_LAUNCH_PREFILL(8, 2, 4); break;
       case 16: QSA_LAUNCH_PREFILL(16, 4, 8); break;
       default: return hipErrorInvalidValue;
     }
