@@ -92,6 +92,23 @@ def test_index_topk_c1_full(qsa):
     _say("rows differing inside the tie band:", n_band)
 
 
+@pytest.mark.parametrize("Hi", [1, 2, 16])
+def test_index_topk_other_head_counts(qsa, Hi):
+    # the many-query kernel at indexer head counts the main workloads do not
+    # use (one 9-wave workgroup per CU; 1 and 16 heads also spill registers)
+    W = Workload(f"heads{Hi}", "prefill", 40 + Hi, 1, 3000, 3000, 0, 16, 2, Hi, k=96)
+    _say("index heads", Hi)
+    iq = gen.normal(W.seed, gen.STREAM_IDX_Q, (W.n_q, W.Hi, W.di))
+    ik = gen.idx_keys(W.seed, 0, W.L, 0, W.L, W.di, W.needle_window, W.r)
+    g_sel, g_cnt, g_cmp = _prefill_select(qsa, W, iq, ik)
+    blocks = oracle.compress(ik, W.r)
+    assert np.array_equal(g_cmp, blocks)
+    o_sel, o_cnt, band, _ = oracle.select(iq, blocks, 0, W.r, W.k, W.w)
+    n_band = check_selection(g_sel, g_cnt, o_sel, o_cnt, band,
+                             oracle_rows_scores(iq, blocks, np.arange(W.n_q), W.r, W.w))
+    _say("rows differing inside the tie band:", n_band)
+
+
 def test_index_topk_integer_ties_bitexact(qsa):
     # integer-valued inputs: every score is exact in fp32 on both sides, so the
     # selection (with its many exact ties, zeros included) must match bit for bit
