@@ -476,8 +476,11 @@ void index_prefill_kernel(
   constexpr int TILE = 64;                       // candidates per LDS tile
   constexpr int TILE_BYTES = TILE * 128;         // 8 KiB
   constexpr int PF = kPrefillDepth;
-  constexpr int NSLOT = 3;                       // LDS slots
-  static_assert(NSLOT >= PF + 1, "a slot is refilled only after its tile was processed");
+  // tiles per barrier: two at NW = 4, whose four compute waves otherwise wait
+  // for each other at every tile (their appends vary from tile to tile)
+  constexpr int TT = NW == 4 ? 2 : 1;
+  constexpr int NSLOT = TT == 2 ? 4 : 3;         // LDS slots
+  static_assert(NSLOT >= PF + 1 && NSLOT >= 2 * TT, "a slot is refilled only after its tile was processed");
   __shared__ __attribute__((aligned(16))) unsigned char ring[NSLOT * TILE_BYTES];
   __shared__ uint32_t hist_all[NW][256];
   __shared__ int wg_lim[NW];
@@ -631,8 +634,10 @@ void index_prefill_kernel(
       // each other at the tile barriers one compaction at a time. The wave
       // that asked compacts for certain (another may already have moved the
       // flag on); for the others the invitation is optional.
-      if (pending || wg_compact == t) compact_over(max(cap - 12 * TILE, cap / 2));
-      pending = false;
+      if (t % TT == 0 && (pending || wg_compact == t)) {
+        compact_over(max(cap - 12 * TILE, cap / 2));
+        pending = false;
+      }
       const unsigned char* sl = ring + slot * TILE_BYTES;
       bool appended = false;
 #pragma unroll
@@ -693,14 +698,16 @@ void index_prefill_kernel(
           appended = true;
         }
       }
-      // at most 64 appends per buffer per tile: keep room for the next tile
+      // at most 64 appends per buffer per tile: keep room for the tiles up to
+      // the next barrier, where compactions happen
       if (appended) {
         bool over = false;
 #pragma unroll
-        for (int s = 0; s < NS; ++s) over |= cnt[s] > cap - TILE;
+        for (int s = 0; s < NS; ++s) over |= cnt[s] > cap - TT * TILE;
         if (ballot(over)) {
           pending = true;
-          if (lane == 0) wg_compact = t + 1;  // before the next tile (all waves read it after its barrier)
+          // the first tile after the next barrier (all waves read it after that barrier)
+          if (lane == 0) wg_compact = (t | (TT - 1)) + 1;
         }
       }
     };
@@ -711,19 +718,35 @@ void index_prefill_kernel(
     // 8 loads of each of tiles t + 1 .. t + PF - 1 were issued after it.
     // Loads are issued for every t (past the end they reread the last
     // candidate), so that count holds to the end.
+    // With two tiles per barrier (TT = 2) the copy wave issues tiles t + 2 and
+    // t + 3 right after B_t, into the slots of tiles t - 2 and t - 1 (processed
+    // before B_t), and waits for both before the next barrier.
     if (copier) {
+      if constexpr (TT == 1) {
 #pragma unroll
-      for (int t = 0; t < PF; ++t) issue_tile(t);
-      for (int t = 0; t < ntiles; ++t) {
-        __builtin_amdgcn_s_waitcnt(prefill_vmcnt(8 * (PF - 1)));
-        __builtin_amdgcn_s_barrier();
-        issue_tile(t + PF);
+        for (int t = 0; t < PF; ++t) issue_tile(t);
+        for (int t = 0; t < ntiles; ++t) {
+          __builtin_amdgcn_s_waitcnt(prefill_vmcnt(8 * (PF - 1)));
+          __builtin_amdgcn_s_barrier();
+          issue_tile(t + PF);
+        }
+      } else {
+        issue_tile(0);
+        issue_tile(1);
+        for (int t = 0; t < ntiles; t += 2) {
+          __builtin_amdgcn_s_waitcnt(prefill_vmcnt(0));
+          __builtin_amdgcn_s_barrier();
+          issue_tile(t + 2);
+          issue_tile(t + 3);
+        }
       }
       __builtin_amdgcn_s_waitcnt(prefill_vmcnt(0));  // no copy into LDS outlives the workgroup
     } else {
-      for (int t = 0; t < ntiles; ++t) {
+      for (int t = 0; t < ntiles; t += TT) {
         __syncthreads();
-        process(t, t % NSLOT);
+#pragma unroll
+        for (int u = 0; u < TT; ++u)
+          if (t + u < ntiles) process(t + u, (t + u) % NSLOT);
       }
     }
   }
@@ -1139,7 +1162,9 @@ IndexPlan plan_index(int hi, int k, int batch, int n_q, int64_t max_q_end, int r
   if (split_len < 64) split_len = 64;
   p.splits = (int)splits;
   p.split_len = (int)split_len;
-  int cap = 2048;
+  // (4 compute waves: 4 x cap staged keys and a 32 KiB tile ring must stay
+  // within 64 KiB of LDS for two workgroups per CU)
+  int cap = p.wide && p.nw == 4 ? 1536 : 2048;
   if (cap < 2 * keep + 64) cap = (2 * keep + 64 + 63) / 64 * 64;
   if (cap < keep + 2 * 64) cap = keep + 2 * 64;
   if ((int64_t)split_len + 64 <= cap) cap = (int)split_len + 64;
