@@ -476,9 +476,10 @@ void index_prefill_kernel(
   constexpr int TILE = 64;                       // candidates per LDS tile
   constexpr int TILE_BYTES = TILE * 128;         // 8 KiB
   constexpr int PF = kPrefillDepth;
-  // tiles per barrier: two at NW = 4, whose four compute waves otherwise wait
-  // for each other at every tile (their appends vary from tile to tile)
-  constexpr int TT = NW == 4 ? 2 : 1;
+  // tiles per barrier: two, or else the compute waves wait for each other at
+  // every tile (their appends vary from tile to tile); one at NW = 3, whose
+  // three workgroups per CU leave no LDS for a fourth slot
+  constexpr int TT = NW == 3 ? 1 : 2;
   constexpr int NSLOT = TT == 2 ? 4 : 3;         // LDS slots
   static_assert(NSLOT >= PF + 1 && NSLOT >= 2 * TT, "a slot is refilled only after its tile was processed");
   __shared__ __attribute__((aligned(16))) unsigned char ring[NSLOT * TILE_BYTES];
