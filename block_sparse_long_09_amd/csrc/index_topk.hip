@@ -204,9 +204,22 @@ __device__ __noinline__ uint2 compact_keys_approx(glb_u64* p, int n, int keep, l
     const int lo = hi > 8 ? hi - 8 : 0;
     for (int i = lane; i < 256; i += kWave) hist[i] = 0;
     wave_sync();
-    for (int i = lane; i < n; i += kWave) {
-      const int d = range_digit(kstage[i], kbase, hi, lo);
-      if (d >= 0) __atomic_fetch_add(&hist[d], 1u, __ATOMIC_RELAXED);
+    // eight keys per lane read before their eight atomics: the reads cannot
+    // move past an LDS atomic by themselves (the compiler cannot tell the
+    // stage from the histogram), and one read-then-add per key would wait out
+    // the LDS latency once per key
+    for (int base = 0; base < n; base += 8 * kWave) {
+      uint32_t kk[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int i = base + u * kWave + lane;
+        kk[u] = i < n ? kstage[i] : 0u;
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int d = base + u * kWave + lane < n ? range_digit(kk[u], kbase, hi, lo) : -1;
+        if (d >= 0) __atomic_fetch_add(&hist[d], 1u, __ATOMIC_RELAXED);
+      }
     }
     wave_sync();
     int dig;

@@ -100,9 +100,20 @@ __device__ void wave_select(KeyFn key, int n, int keep, HistPtr hist, uint32_t& 
     const int lo = w > 8 ? w - 8 : 0;
     for (int i = lane; i < 256; i += kWave) hist[i] = 0;
     wave_sync();
-    for (int i = lane; i < n; i += kWave) {
-      const int d = range_digit(key(i), base, w, lo);
-      if (d >= 0) __atomic_fetch_add(&hist[d], 1u, __ATOMIC_RELAXED);
+    // eight keys per lane read before their eight atomics (one read-then-add
+    // per key would wait out the read latency once per key)
+    for (int b0 = 0; b0 < n; b0 += 8 * kWave) {
+      uint32_t kk[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int i = b0 + u * kWave + lane;
+        kk[u] = i < n ? key(i) : 0u;
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int d = b0 + u * kWave + lane < n ? range_digit(kk[u], base, w, lo) : -1;
+        if (d >= 0) __atomic_fetch_add(&hist[d], 1u, __ATOMIC_RELAXED);
+      }
     }
     wave_sync();
     int dig;
