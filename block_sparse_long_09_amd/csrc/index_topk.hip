@@ -459,9 +459,10 @@ __global__ __launch_bounds__(256) void index_stream_kernel(
 // workgroups a CU holds, see plan_index) and one copy wave shares one
 // candidate split.
 // Block keys go HBM -> LDS directly (global_load_lds, issued by the copy wave
-// kPrefillDepth 64-candidate tiles ahead into a 3-slot ring, XOR-swizzled
-// 16-byte parts so the B-fragment reads hit distinct banks) -> B fragments;
-// one barrier per tile. Only the copy wave loads tiles and it waits on its own
+// into a ring of 64-candidate tiles with XOR-swizzled 16-byte parts, so the
+// B-fragment reads hit distinct banks) -> B fragments: 4 slots refilled two
+// tiles per barrier, or at NW = 3 3 slots refilled kPrefillDepth tiles ahead,
+// one tile per barrier. Only the copy wave loads tiles and it waits on its own
 // counter alone: the compute waves' appends (global stores) are never waited
 // for before a tile is in place, as they would be if the compute waves loaded
 // the tiles (the memory counter is in order and counts stores too).
