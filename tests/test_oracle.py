@@ -349,6 +349,38 @@ def test_distill_kl_zero_when_both_uniform_and_trivial_cases():
     assert np.all(np.abs(kl[4:8]) < 1e-13)
 
 
+@pytest.mark.parametrize("peak", [1.0, 8.0])
+def test_distill_kl_target_mass_vs_torch_softmax(peak):
+    # The target built independently: torch's float64 softmax over the causal
+    # prefix with the KV heads repeated per query-head group (head h reads KV
+    # head h // G), the softmax scale 1/sqrt(D) applied to the logits, the
+    # attention of every head summed per candidate block j < b_t and
+    # renormalised; the indexer side as torch's log-softmax of the O2 scores.
+    # Non-zero queries (and peaked ones, Q x 8) make the attention non-uniform,
+    # so a wrong KV-head map, a missing scale or a block boundary off by a
+    # token all change the loss.
+    L, Hq, Hkv, Hi, r = 160, 8, 2, 8, 4
+    Q, K, iq, blocks = _kl_inputs(83, L, Hq, Hkv, Hi, r)
+    if peak != 1.0:
+        Q = gen.f32_to_bf16(gen.bf16_to_f64(Q).astype(np.float32) * np.float32(peak))
+    t0 = 9
+    kl = oracle.distill_kl(Q[t0:], K, iq[t0:], blocks, t0, r, 1.0 / Hi)
+    G = Hq // Hkv
+    Kt = torch.from_numpy(widen(K)).repeat_interleave(G, dim=1)  # [L, Hq, D]
+    scale = 1.0 / math.sqrt(128)
+    for i, t in enumerate(range(t0, L)):
+        bt = t // r
+        q = torch.from_numpy(widen(Q[t]))  # [Hq, D]
+        logits = torch.einsum("hd,shd->hs", q, Kt[: t + 1]) * scale
+        a = torch.softmax(logits, dim=1)  # [Hq, t + 1]
+        mass = a[:, : bt * r].sum(0).reshape(bt, r).sum(1)
+        p = mass / mass.sum()
+        s = torch.from_numpy(oracle.scores(iq[t], blocks[:bt], 1.0 / Hi).astype(np.float64))
+        logq = torch.log_softmax(s, dim=0)
+        want = float((p * (torch.log(p) - logq)).sum())
+        assert kl[i] == pytest.approx(want, abs=1e-12, rel=1e-12), (t, kl[i], want)
+
+
 def test_distill_kl_nonnegative_and_depends_on_scores():
     L, Hq, Hkv, Hi, r = 200, 8, 2, 8, 4
     Q, K, iq, blocks = _kl_inputs(79, L, Hq, Hkv, Hi, r)
