@@ -418,35 +418,19 @@ def run_paged_batch(args, torch, qsa):
     """Packed variable-length batch over a paged K/V pool (config 6)."""
     from block_sparse_long_09_amd.pipeline import PagedBatchPath
     from gen.configs import PAGED
-    from gen.device import idx_keys_to_device, normal_to_device
+    from gen.device import paged_batch_to_device
     W = PAGED[args.config]
     dev = "cuda"
-    B, page = W.batch, W.page_size
-    L = W.lengths
-    max_len = (max(L) + page - 1) // page * page
-    max_pages = max_len // page
-    pages_of = [(x + page - 1) // page for x in L]
-    n_pages = sum(pages_of)
+    B = W.batch
     t_setup = time.time()
-    log(f"generating paged pool {W.name}: {n_pages} pages of {page} tokens")
-    kpool = normal_to_device(W.seed, 2, (n_pages, page, W.Hkv, W.D))
-    vpool = normal_to_device(W.seed, 3, (n_pages, page, W.Hkv, W.D))
-    perm = np.random.default_rng(W.seed).permutation(n_pages).astype(np.int32)
-    table = np.zeros((B, max_pages), np.int32)
-    nxt = 0
-    for b in range(B):
-        table[b, :pages_of[b]] = perm[nxt:nxt + pages_of[b]]
-        nxt += pages_of[b]
-    table_d = torch.from_numpy(table).to(dev)
-    total = sum(W.new)
-    Q = normal_to_device(W.seed, 1, (total, W.Hq, W.D))
-    iq = normal_to_device(W.seed, 4, (total, W.Hi, W.di))
-    ik = idx_keys_to_device(W.seed, B, max_len, W.di, W.needle_window, W.r)
+    log(f"generating paged pool {W.name}")
+    I = paged_batch_to_device(W, dev)
+    kpool, vpool, table_d, Q, iq, ik, cu, p0 = (I[n] for n in ("kpool", "vpool", "table", "Q", "iq", "ik", "cu",
+                                                              "q_pos0"))
+    total, max_len = I["total"], I["max_len"]
     cmp = torch.zeros((B, max_len // W.r, W.di), dtype=torch.bfloat16, device=dev)
     for b in range(B):  # the cached prefixes' block keys
         qsa.qsa_compress_keys(ik[b], cmp[b], W.r, 0, W.prefix[b] // W.r)
-    cu = torch.tensor(np.concatenate([[0], np.cumsum(W.new)]), dtype=torch.int32, device=dev)
-    p0 = torch.tensor(W.prefix, dtype=torch.int32, device=dev)
     path = PagedBatchPath(W.Hq, W.Hkv, W.Hi, B, max(W.new), max_len, r=W.r, k=W.k, D=W.D, di=W.di, device=dev)
     torch.cuda.synchronize()
     log(f"setup {time.time() - t_setup:.1f}s")
@@ -498,7 +482,7 @@ def run_paged_batch(args, torch, qsa):
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": W.name, "sequences": B, "cached_prefix": list(W.prefix), "new_rows": list(W.new),
-                   "page_size": page, "budget_tokens": W.k * W.r, "block_size": W.r,
+                   "page_size": W.page_size, "budget_tokens": W.k * W.r, "block_size": W.r,
                    "heads_q_kv_idx": [W.Hq, W.Hkv, W.Hi]},
         "phase_ms": phase,
         "phase_sum_ms": step_ms,
@@ -509,7 +493,56 @@ def run_paged_batch(args, torch, qsa):
         "cpu_baseline": None,
         "sample_parity": None,
     }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"], out["sample_parity"] = paged_cpu_baseline(W, I["table_host"], path, total)
     print(json.dumps(out), flush=True)
+
+
+def paged_cpu_baseline(W, table, path, total):
+    """The oracle (select + attend) on two or three new rows of every sequence
+    of a packed paged batch, on the host cores, and the parity of those rows
+    against the GPU's outputs (selections bit-exact or inside the near-tie
+    band, outputs within 2e-2 max / 1e-3 mean, lse within 2e-4)."""
+    import gen
+    import oracle
+    from gen.device import paged_batch_layout, paged_sequence_host
+    g_sel = path.sel[:total].cpu().numpy()
+    g_cnt = path.cnt[:total].cpu().numpy()
+    g_out = path.out[:total].float().cpu().numpy()
+    g_lse = path.lse[:total].cpu().numpy()
+    cu = np.concatenate([[0], np.cumsum(W.new)])
+    key_len = paged_batch_layout(W)[2]
+    rng = np.random.default_rng(17)
+    t_or = 0.0
+    n_rows = same = 0
+    err = lerr = 0.0
+    for b in range(W.batch):
+        n = W.new[b]
+        loc = sorted({0, n - 1} | ({int(rng.integers(0, n))} if n > 2 else set()))
+        L_b = W.prefix[b] + n
+        ik = gen.idx_keys(W.seed, b, key_len, 0, L_b, W.di, W.needle_window, W.r)
+        Kb = paged_sequence_host(W, table, b, 2, L_b)
+        Vb = paged_sequence_host(W, table, b, 3, L_b)
+        tc = time.perf_counter()
+        blocks = oracle.compress(ik, W.r)
+        for i in loc:
+            row = int(cu[b] + i)
+            t = W.prefix[b] + i
+            q = gen.normal(W.seed, 1, (1, W.Hq, W.D), e0=row * W.Hq * W.D)
+            iqr = gen.normal(W.seed, 4, (1, W.Hi, W.di), e0=row * W.Hi * W.di)
+            s, c, _, _ = oracle.select(iqr, blocks, t, W.r, W.k, W.w)
+            o, lo = oracle.sparse_attn(q, Kb, Vb, t, W.r, s, c)
+            n_rows += 1
+            if np.array_equal(g_sel[row], s[0]) and g_cnt[row] == c[0]:
+                same += 1
+                err = max(err, float(np.abs(g_out[row] - o[0]).max()))
+                lerr = max(lerr, float(np.abs(g_lse[row] - lo[0]).max()))
+        t_or += time.perf_counter() - tc
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    cpu = {"value": n_rows / t_or, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+           "sample": f"{n_rows} of {total} new rows (first, last and one random row of each sequence) of {W.name}: "
+                     f"block compression of each sequence's keys, selection and attention ({t_or:.2f}s)"}
+    return cpu, {"rows": n_rows, "selection_identical_rows": same, "out_max_abs": err, "lse_max_abs": lerr}
 
 
 def run_distill_kl(args, torch, qsa):
@@ -560,7 +593,42 @@ def run_distill_kl(args, torch, qsa):
         "kl_mean": float(kl.mean().item()),
         "roofline": dict(roof, kernel="distill_kl"), "dense": None, "cpu_baseline": None, "sample_parity": None,
     }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"], out["sample_parity"] = distill_cpu_baseline(W, q0, n_q, kl)
     print(json.dumps(out), flush=True)
+
+
+def distill_cpu_baseline(W, q0, n_q, kl):
+    """The oracle's loss on 16 rows of the timed call (the first rows, rows
+    near the end, random rows), timed on the host cores, and their parity
+    (1e-4 absolute + 1e-4 relative)."""
+    import gen
+    import oracle
+    g = kl.cpu().numpy().astype(np.float64)
+    rng = np.random.default_rng(13)
+    rows = np.unique(np.concatenate([[0, 4, n_q // 2, n_q - 2, n_q - 1], rng.integers(n_q - 1024, n_q, 6),
+                                     rng.integers(0, n_q, 5)]))
+    K = gen.normal(W.seed, 2, (W.L, W.Hkv, W.D))
+    blocks = oracle.compress(gen.idx_keys(W.seed, 0, W.L, 0, W.L, W.di, W.needle_window, W.r), W.r)
+    first = W.n_q - n_q  # row of the generated tensors that the call's row 0 is
+    worst = 0.0
+    ok = 0
+    tc = time.perf_counter()
+    for i in rows:
+        i = int(i)
+        gi = first + i
+        q = gen.normal(W.seed, 1, (1, W.Hq, W.D), e0=gi * W.Hq * W.D)
+        iqr = gen.normal(W.seed, 4, (1, W.Hi, W.di), e0=gi * W.Hi * W.di)
+        o = float(oracle.distill_kl(q, K, iqr, blocks, q0 + i, W.r, W.w)[0])
+        e = abs(g[i] - o)
+        worst = max(worst, e)
+        ok += int(e <= 1e-4 + 1e-4 * abs(o))
+    el = time.perf_counter() - tc
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    cpu = {"value": len(rows) / el, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+           "sample": f"{len(rows)} of {n_q} query rows of {W.name} (first rows, rows near the end, random rows), "
+                     f"loss per row ({el:.2f}s)"}
+    return cpu, {"rows": int(len(rows)), "within_tolerance_rows": ok, "kl_max_abs_err": worst}
 
 
 def gdn_work(W):
