@@ -536,7 +536,11 @@ void index_prefill_kernel(
   float tau[NS];
   int cnt[NS];
   int lim[NS];        // candidate bound of this lane's query in slot s
-  glb_u64* bp[NS];    // its buffer
+  // buffer of slot 0 of this lane-half; slot s's query is d(s) queries later
+  // (an absent query's buffer is never written: its threshold is +inf)
+  glb_u64* const bp0 = (glb_u64*)(buf + (((int64_t)b * n_q + slot_query(0, half)) * splits + split) * (int64_t)cap);
+  const int64_t qstride = (int64_t)splits * cap;
+  auto buf_slot = [&](int s) { return bp0 + (int64_t)((s / QPH) * QPT + s % QPH) * qstride; };
   int maxlim = 0, minlim = 0x7FFFFFFF;
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
@@ -549,7 +553,6 @@ void index_prefill_kernel(
     tau[s] = (wave_live && qi < nqb) ? -1.0f : INFINITY;  // an absent query takes nothing
     cnt[s] = 0;
     lim[s] = l;
-    bp[s] = (glb_u64*)buf_of(wave_live && qi < nqb ? qi : 0);
     maxlim = max(maxlim, l);
   }
 #pragma unroll
@@ -626,7 +629,7 @@ void index_prefill_kernel(
         const uint2 lk = compact_keys_approx(cb, ch, keep, hist_l, kstage_l);
         uint32_t L = lk.x;
         int kept = (int)lk.y;
-        if (kept > cap - 2 * TILE) {
+        if (kept > keep && kept > cap - 3 * TILE) {
           // the threshold's bucket is too full (many equal keys): compact exactly
           L = __float_as_uint(compact_keys_staged(cb, kept, keep, hist_l, kstage_l));
           kept = keep;
@@ -641,88 +644,127 @@ void index_prefill_kernel(
         }
       }
     };
-    bool pending = false;  // this wave must compact before its next tile
-    auto process = [&](int t, int slot) {
-      // A compaction one wave asked for while processing the previous tile is
-      // done by every wave at once, each compacting its buffers past a lower
-      // mark (they fill at similar rates): otherwise the waves would wait for
-      // each other at the tile barriers one compaction at a time. The wave
-      // that asked compacts for certain (another may already have moved the
-      // flag on); for the others the invitation is optional.
-      if (t % TT == 0 && (pending || wg_compact == t)) {
-        compact_over(max(cap - 12 * TILE, cap / 2));
-        pending = false;
-      }
+    // The compute waves run a two-stage pipeline over 32-candidate subtiles:
+    // the MFMAs of subtile u are issued next to the epilogue (ReLU, head sum,
+    // threshold test) of subtile u - 1, which does not depend on them, so
+    // the matrix unit and the VALU work side by side. The last subtile of a
+    // barrier group is scored after the next barrier, beside the next group's
+    // first MFMAs. Accumulator sets alternate: even subtiles write accA, odd
+    // ones accB, so a group always ends with its last subtile pending in accB.
+    f32x16 accA[AT], accB[AT];
+    int cA = 0, cB = 0;    // first candidate of the subtile held in accA / accB
+    bool pendB = false;    // accB holds a subtile not yet scored
+    bool pending = false;  // this wave must compact before its next group
+    // MFMAs of subtile nt (0, 1) of the tile in LDS slot `slot` into acc
+    auto mfma_sub = [&](int slot, int nt, f32x16* acc) __attribute__((always_inline)) {
       const unsigned char* sl = ring + slot * TILE_BYTES;
-      bool appended = false;
+      const int row = nt * 32 + col;
+      u32x4 B[4];
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-        const int c = sbeg + t * TILE + nt * 32;
-        const int row = nt * 32 + col;
-        u32x4 B[4];
+      for (int ks = 0; ks < 4; ++ks) {
+        const int part = 2 * ks + half;
+        B[ks] = *reinterpret_cast<const u32x4*>(sl + row * 128 + ((part ^ (row & 7)) * 16));
+      }
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-          const int part = 2 * ks + half;
-          B[ks] = *reinterpret_cast<const u32x4*>(sl + row * 128 + ((part ^ (row & 7)) * 16));
+      for (int a = 0; a < AT; ++a) {
+        acc[a] = f32x16{};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) acc[a] = mfma32x32x16(A[a][ks], B[ks], acc[a]);
+      }
+    };
+    // Score the subtile at candidate c held in acc and append every candidate
+    // that beats its query's threshold to the query's buffer (lanes of one
+    // half share a query, so the ballot's half gives the positions). Nothing
+    // passes when `live` is false (an empty pipeline stage). Returns whether
+    // anything was appended.
+    auto epilogue = [&](const f32x16* acc, int c, bool live) __attribute__((always_inline)) -> bool {
+      const int j = c + col;
+      const bool interior = c + 32 <= minlim;  // every query of the wave sees the whole subtile
+      const uint64_t live_mask = live ? ~0ull : 0ull;
+      float sc[NS];
+      uint64_t m64[NS];
+      uint64_t any = 0;
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        const int a = s / QPH, qq = s % QPH;
+        float sum = relu_bits(acc[a][qq * HI]);
+#pragma unroll
+        for (int hd = 1; hd < HI; ++hd) sum += relu_bits(acc[a][qq * HI + hd]);
+        sc[s] = SCALE_EPI ? sum * w_epi : sum;
+        m64[s] = ballot(sc[s] > tau[s]) & live_mask;
+        any |= m64[s];
+      }
+      if (!any) return false;
+      const uint32_t below = (1u << col) - 1u;
+      auto append = [&](int s, uint64_t mm, bool pass) {
+        if (mm) {
+          const uint32_t mh = half ? (uint32_t)(mm >> 32) : (uint32_t)mm;
+          if (pass)
+            buf_slot(s)[cnt[s] + __popc(mh & below)] =
+                (unsigned long long)__float_as_uint(sc[s]) | ((unsigned long long)(uint32_t)j << 32);
+          cnt[s] += __popc(mh);
         }
-        f32x16 acc[AT];
+      };
+      if (interior) {
 #pragma unroll
-        for (int a = 0; a < AT; ++a) {
-          acc[a] = f32x16{};
-#pragma unroll
-          for (int ks = 0; ks < 4; ++ks) acc[a] = mfma32x32x16(A[a][ks], B[ks], acc[a]);
-        }
-        const int j = c + col;
-        const bool interior = c + 32 <= minlim;  // every query of the wave sees the whole tile
-        float sc[NS];
-        uint64_t m64[NS];
-        uint64_t any = 0;
+        for (int s = 0; s < NS; ++s) append(s, m64[s], sc[s] > tau[s]);
+      } else {
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
-          const int a = s / QPH, qq = s % QPH;
-          float sum = relu_bits(acc[a][qq * HI]);
-#pragma unroll
-          for (int hd = 1; hd < HI; ++hd) sum += relu_bits(acc[a][qq * HI + hd]);
-          sc[s] = SCALE_EPI ? sum * w_epi : sum;
-          m64[s] = ballot(sc[s] > tau[s]);
-          any |= m64[s];
-        }
-        if (any) {
-          // append each passing (score, block) to its query's buffer: lanes of
-          // one half share a query, so the ballot's half gives the positions
-          const uint32_t below = (1u << col) - 1u;
-          auto append = [&](int s, uint64_t mm, bool pass) {
-            if (mm) {
-              const uint32_t mh = half ? (uint32_t)(mm >> 32) : (uint32_t)mm;
-              if (pass)
-                bp[s][cnt[s] + __popc(mh & below)] =
-                    (unsigned long long)__float_as_uint(sc[s]) | ((unsigned long long)(uint32_t)j << 32);
-              cnt[s] += __popc(mh);
-            }
-          };
-          if (interior) {
-#pragma unroll
-            for (int s = 0; s < NS; ++s) append(s, m64[s], sc[s] > tau[s]);
-          } else {
-#pragma unroll
-            for (int s = 0; s < NS; ++s) {
-              const bool pass = sc[s] > tau[s] && j < lim[s];
-              append(s, ballot(pass), pass);
-            }
-          }
-          appended = true;
+          const bool pass = sc[s] > tau[s] && j < lim[s];
+          append(s, ballot(pass), pass);
         }
       }
-      // at most 64 appends per buffer per tile: keep room for the tiles up to
-      // the next barrier, where compactions happen
+      return true;
+    };
+    // One barrier group: TT tiles, 2 TT subtiles (fewer at the end). A
+    // compaction one wave asked for while processing the previous group is
+    // done by every wave at once, each compacting its buffers past a lower
+    // mark (they fill at similar rates): otherwise the waves would wait for
+    // each other at the barriers one compaction at a time. The wave that
+    // asked compacts for certain (another may already have moved the flag
+    // on); for the others the invitation is optional. The pending subtile is
+    // scored first, so the buffers hold every candidate before the next one.
+    auto process_group = [&](int t) __attribute__((always_inline)) {
+      if (pending || wg_compact == t) {
+        if (pendB) epilogue(accB, cB, true);
+        pendB = false;
+        // only buffers past k - 1 entries: a shorter one still needs every
+        // later candidate, so its threshold must stay where it is
+        compact_over(max(max(cap - 12 * TILE, cap / 2), keep));
+        pending = false;
+      }
+      const int nsub = 2 * min(TT, ntiles - t);
+      bool appended = false;
+#pragma unroll
+      for (int u = 0; u < 2 * TT; ++u) {
+        if (u < nsub) {
+          const int tt = t + (u >> 1);
+          const int c = sbeg + tt * TILE + (u & 1) * 32;
+          if ((u & 1) == 0) {
+            mfma_sub(tt % NSLOT, 0, accA);
+            cA = c;
+            appended |= epilogue(accB, cB, pendB);
+            pendB = false;
+          } else {
+            mfma_sub(tt % NSLOT, 1, accB);
+            cB = c;
+            appended |= epilogue(accA, cA, true);
+            pendB = true;
+          }
+        }
+      }
+      // at most 32 appends per buffer per subtile: keep room for the subtiles
+      // up to the next compaction point (this group's pending one, the next
+      // group's, and that group's pending one, scored before a compaction)
       if (appended) {
         bool over = false;
 #pragma unroll
-        for (int s = 0; s < NS; ++s) over |= cnt[s] > cap - TT * TILE;
+        for (int s = 0; s < NS; ++s) over |= cnt[s] > cap - (TT * TILE + 32);
         if (ballot(over)) {
           pending = true;
-          // the first tile after the next barrier (all waves read it after that barrier)
-          if (lane == 0) wg_compact = (t | (TT - 1)) + 1;
+          // the next group (all waves read the flag after that group's barrier)
+          if (lane == 0) wg_compact = t + TT;
         }
       }
     };
@@ -759,10 +801,9 @@ void index_prefill_kernel(
     } else {
       for (int t = 0; t < ntiles; t += TT) {
         __syncthreads();
-#pragma unroll
-        for (int u = 0; u < TT; ++u)
-          if (t + u < ntiles) process(t + u, (t + u) % NSLOT);
+        process_group(t);
       }
+      if (pendB) epilogue(accB, cB, true);
     }
   }
   if (wave_live && col == 0) {
@@ -1140,17 +1181,19 @@ IndexPlan plan_index(int hi, int k, int batch, int n_q, int64_t max_q_end, int r
   }
   p.decode = false;
   p.wide = n_q >= 64;
-  // A tiles per wave in the LDS-pipelined kernel (8 query slots per lane, or
-  // 4 at 8 heads)
-  p.at = p.wide ? (hi == 16 ? 4 : (hi == 8 ? 2 : (hi == 4 ? 2 : 1))) : 1;
-  // Compute waves per workgroup (plus one copy wave). Two 5-wave workgroups
-  // share a CU only when each takes at most 64 KiB of LDS and 128 VGPRs (both
-  // put two waves on one SIMD): true at 8 heads, where a uniform batch then
-  // fills every CU with exactly two. A packed batch of unequal sequences runs
+  // A tiles per wave in the LDS-pipelined kernel: two at 8 and 16 heads (8 and
+  // 4 queries per wave), one otherwise (32 / H_i queries).
+  p.at = p.wide ? (hi >= 8 ? 2 : 1) : 1;
+  // Compute waves per workgroup (plus one copy wave). The pipelined scan
+  // keeps two accumulator sets, ~160 VGPRs at two A tiles: one 9-wave
+  // workgroup per CU (168 VGPRs at most), which for a uniform batch of 8-head
+  // queries at 1M fills each CU once. A packed batch of unequal sequences runs
   // many workgroups of unequal length over several rounds; there three 4-wave
-  // workgroups per CU (3 compute waves each, 51 KiB) keep more of them in
-  // flight. Other head counts: one 9-wave workgroup per CU (168 VGPRs).
-  p.nw = hi == 8 ? (allow_decode ? 4 : 3) : 8;
+  // workgroups per CU (3 compute waves each) keep more of them in flight. At 4
+  // heads one A tile (~120 VGPRs) lets two 5-wave workgroups share a CU (at
+  // most 128 VGPRs and 64 KiB of LDS each: a 5-wave workgroup puts two waves
+  // on one SIMD, and the second workgroup's land on the same SIMD).
+  p.nw = hi == 8 ? (allow_decode ? 8 : 3) : (hi == 4 ? 4 : 8);
   p.qw = p.at * 32 / hi;
   p.n_qgroups = (n_q + p.qw - 1) / p.qw;
   int64_t splits;
@@ -1239,9 +1282,9 @@ hipError_t launch_index_topk(const IndexPlan& p, const uint16_t* idx_q, const ui
     switch (p.hi) {
       case 1: QSA_LAUNCH_PREFILL(1, 1, 8); break;
       case 2: QSA_LAUNCH_PREFILL(2, 1, 8); break;
-      case 4: QSA_LAUNCH_PREFILL(4, 2, 8); break;
-      case 8: if (p.nw == 3) QSA_LAUNCH_PREFILL(8, 2, 3); else QSA_LAUNCH_PREFILL(8, 2, 4); break;
-      case 16: QSA_LAUNCH_PREFILL(16, 4, 8); break;
+      case 4: QSA_LAUNCH_PREFILL(4, 1, 4); break;
+      case 8: if (p.nw == 3) QSA_LAUNCH_PREFILL(8, 2, 3); else QSA_LAUNCH_PREFILL(8, 2, 8); break;
+      case 16: QSA_LAUNCH_PREFILL(16, 2, 8); break;
       default: return hipErrorInvalidValue;
     }
 #undef QSA_LAUNCH_PREFILL
