@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(_HERE, "libqsa.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
-        f"{LIB_PATH} is not built; run `python -m block_sparse_long_09_amd.build` (hipcc, gfx950)")
+        f"{LIB_PATH} is not built; run `python block_sparse_long_09_amd/build.py` (hipcc, gfx950)")
 
 _lib = ctypes.CDLL(LIB_PATH)
 
@@ -37,6 +37,12 @@ class AttnDesc(ctypes.Structure):
 class GdnDesc(ctypes.Structure):
     _fields_ = [("n_qk_heads", _i32), ("n_v_heads", _i32), ("key_dim", _i32), ("value_dim", _i32),
                 ("scale", _f32)]
+
+
+class PlanInfo(ctypes.Structure):
+    _fields_ = [("n_launches", _i32), ("grid", (ctypes.c_uint32 * 3) * 3), ("block", ctypes.c_uint32 * 3),
+                ("lds", ctypes.c_uint64 * 3), ("max_int32_value", _i64), ("max_offset", _i64),
+                ("workspace_bytes", ctypes.c_uint64), ("splits", _i32), ("cap", _i32), ("fits", _i32)]
 
 
 _PI, _PA, _PG = ctypes.POINTER(IndexDesc), ctypes.POINTER(AttnDesc), ctypes.POINTER(GdnDesc)
@@ -70,6 +76,8 @@ _sig("qsa_distill_kl_prefill", ctypes.c_int, [_PA, _PI, _vp, _vp, _vp, _vp, _i64
 _sig("qsa_gdn_prefill_workspace_size", _sz, [_PG, _i32, _i64])
 _sig("qsa_gdn_prefill", ctypes.c_int, [_PG, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i64, _vp, _vp, _vp, _sz, _vp])
 _sig("qsa_gdn_decode", ctypes.c_int, [_PG, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp])
+_sig("qsa_index_topk_plan_info", ctypes.c_int, [_PI, _i32, _i32, _i64, _i32, ctypes.POINTER(PlanInfo)])
+_sig("qsa_sparse_attn_plan_info", ctypes.c_int, [_PA, _i32, _i32, _i32, _i32, ctypes.POINTER(PlanInfo)])
 _sig("qsa_status_string", ctypes.c_char_p, [ctypes.c_int])
 _sig("qsa_last_error_message", ctypes.c_char_p, [])
 _sig("qsa_abi_version", ctypes.c_int, [])
@@ -83,6 +91,7 @@ EXPORTS = (
     "qsa_index_topk_varlen_workspace_size", "qsa_index_topk_varlen", "qsa_sparse_attn_prefill_paged",
     "qsa_distill_kl_workspace_size", "qsa_distill_kl_prefill",
     "qsa_gdn_prefill_workspace_size", "qsa_gdn_prefill", "qsa_gdn_decode",
+    "qsa_index_topk_plan_info", "qsa_sparse_attn_plan_info",
 )
 
 
@@ -322,3 +331,20 @@ def qsa_gdn_decode(desc, q, k, v, g, beta, state, out, stream=None):
     _check(_lib.qsa_gdn_decode(ctypes.byref(desc), _bf16(q, "q"), _bf16(k, "k"), _bf16(v, "v"), _f32t(g, "g"),
                                _f32t(beta, "beta"), _f32t(state, "state"), v.shape[0], _bf16(out, "out"),
                                _stream(stream)))
+
+
+def qsa_index_topk_plan_info(desc, batch, n_q, max_q_end, packed=False):
+    """The launch plan qsa_index_topk (or, packed, qsa_index_topk_varlen) would
+    use for these sizes (host only)."""
+    info = PlanInfo()
+    _check(_lib.qsa_index_topk_plan_info(ctypes.byref(desc), batch, n_q, max_q_end, int(bool(packed)),
+                                         ctypes.byref(info)))
+    return info
+
+
+def qsa_sparse_attn_plan_info(desc, rows, top_k_blocks, block_size, decode=False):
+    """The launch plan of the sparse attention calls for these sizes (host only)."""
+    info = PlanInfo()
+    _check(_lib.qsa_sparse_attn_plan_info(ctypes.byref(desc), rows, top_k_blocks, block_size, int(bool(decode)),
+                                          ctypes.byref(info)))
+    return info

@@ -1,6 +1,8 @@
 """Build libqsa.so (all HIP sources, gfx950) in place with hipcc.
 
-Usage: python -m block_sparse_long_09_amd.build
+Usage (from the repository root): python block_sparse_long_09_amd/build.py
+The script is run by path, not as a module of the package: importing the
+package needs the library this script builds.
 """
 import os
 import subprocess

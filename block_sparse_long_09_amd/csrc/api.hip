@@ -154,6 +154,8 @@ qsa_status_t qsa_index_topk(const qsa_index_desc_t* desc, const uint16_t* idx_q,
   }
   const qsa::IndexPlan p =
       qsa::plan_index(desc->n_idx_heads, desc->top_k_blocks, batch, n_q, max_q_end, r);
+  const qsa::PlanCheck pc = qsa::check_index_plan(p, batch, n_q);
+  if (pc.unfit) return fail(QSA_ERR_UNSUPPORTED, "index_topk: %s", pc.unfit);
   if (workspace_bytes < p.workspace || (p.workspace && !workspace))
     return fail(QSA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", workspace_bytes, p.workspace);
   if (!aligned(workspace, 16)) return fail(QSA_ERR_MISALIGNED, "workspace must be 16-byte aligned");
@@ -205,6 +207,8 @@ qsa_status_t qsa_sparse_attn_prefill(const qsa_attn_desc_t* desc, int32_t block_
   if (!aligned(sel_blocks, 4) || !aligned(sel_count, 4) || !aligned(lse, 4))
     return fail(QSA_ERR_MISALIGNED, "int32/fp32 arrays must be 4-byte aligned");
   const qsa::AttnPlan p = qsa::plan_attn(n_q, (int64_t)top_k_blocks * block_size, false);
+  const qsa::PlanCheck pc = qsa::check_attn_plan(p, desc->n_q_heads, desc->n_kv_heads, top_k_blocks, block_size);
+  if (pc.unfit) return fail(QSA_ERR_UNSUPPORTED, "sparse_attn_prefill: %s", pc.unfit);
   (void)workspace;
   (void)workspace_bytes;
   return hip_status(qsa::launch_attn(p, q, k, v, 0, q_pos0, nullptr, desc->n_q_heads,
@@ -233,6 +237,8 @@ qsa_status_t qsa_sparse_attn_decode(const qsa_attn_desc_t* desc, int32_t block_s
   if (!aligned(kv_len, 4) || !aligned(sel_blocks, 4) || !aligned(sel_count, 4) || !aligned(lse, 4))
     return fail(QSA_ERR_MISALIGNED, "int32/fp32 arrays must be 4-byte aligned");
   const qsa::AttnPlan p = qsa::plan_attn(batch, (int64_t)top_k_blocks * block_size, true);
+  const qsa::PlanCheck pc = qsa::check_attn_plan(p, desc->n_q_heads, desc->n_kv_heads, top_k_blocks, block_size);
+  if (pc.unfit) return fail(QSA_ERR_UNSUPPORTED, "sparse_attn_decode: %s", pc.unfit);
   const size_t need = qsa::attn_workspace_bytes(p, desc->n_q_heads);
   if (workspace_bytes < need || (need && !workspace))
     return fail(QSA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", workspace_bytes, need);
@@ -243,6 +249,50 @@ qsa_status_t qsa_sparse_attn_decode(const qsa_attn_desc_t* desc, int32_t block_s
                                      sel_count, desc->softmax_scale, out, lse, workspace,
                                      (hipStream_t)stream),
                     "sparse_attn_decode launch");
+}
+
+/* ---------------------------------------------------------- diagnostics --- */
+
+static void fill_info(const qsa::PlanCheck& c, size_t ws, int splits, int cap, qsa_plan_info_t* info) {
+  *info = qsa_plan_info_t{};
+  info->n_launches = c.n;
+  for (int i = 0; i < c.n && i < 3; ++i) {
+    for (int d = 0; d < 3; ++d) info->grid[i][d] = c.l[i].grid[d];
+    info->block[i] = c.l[i].block;
+    info->lds[i] = c.l[i].lds;
+  }
+  info->max_int32_value = c.max_i32;
+  info->max_offset = c.max_offset;
+  info->workspace_bytes = ws;
+  info->splits = splits;
+  info->cap = cap;
+  info->fits = c.unfit ? 0 : 1;
+}
+
+qsa_status_t qsa_index_topk_plan_info(const qsa_index_desc_t* desc, int32_t batch, int32_t n_q, int64_t max_q_end,
+                                      int32_t packed, qsa_plan_info_t* info) {
+  qsa_status_t s = check_index_desc(desc);
+  if (s != QSA_OK) return s;
+  if (!info) return fail(QSA_ERR_INVALID_ARGUMENT, "NULL info");
+  if (batch < 1 || n_q < 1 || max_q_end < n_q || max_q_end > kMaxPos)
+    return fail(QSA_ERR_INVALID_ARGUMENT, "need batch, n_q >= 1 and n_q <= max_q_end < 2^31");
+  const qsa::IndexPlan p = qsa::plan_index(desc->n_idx_heads, desc->top_k_blocks, batch, n_q, max_q_end,
+                                           desc->block_size, packed == 0);
+  const qsa::PlanCheck c = qsa::check_index_plan(p, batch, n_q);
+  fill_info(c, p.workspace, p.splits, p.decode ? p.list_cap : p.cap, info);
+  return ok();
+}
+
+qsa_status_t qsa_sparse_attn_plan_info(const qsa_attn_desc_t* desc, int32_t rows, int32_t top_k_blocks,
+                                       int32_t block_size, int32_t decode, qsa_plan_info_t* info) {
+  qsa_status_t s = check_attn_common(desc, block_size, top_k_blocks);
+  if (s != QSA_OK) return s;
+  if (!info) return fail(QSA_ERR_INVALID_ARGUMENT, "NULL info");
+  if (rows < 1) return fail(QSA_ERR_INVALID_ARGUMENT, "rows must be >= 1");
+  const qsa::AttnPlan p = qsa::plan_attn(rows, (int64_t)top_k_blocks * block_size, decode != 0);
+  const qsa::PlanCheck c = qsa::check_attn_plan(p, desc->n_q_heads, desc->n_kv_heads, top_k_blocks, block_size);
+  fill_info(c, qsa::attn_workspace_bytes(p, desc->n_q_heads), p.splits, (int)p.split_tokens, info);
+  return ok();
 }
 
 /* ----------------------------------------------------------- comparator --- */
@@ -348,6 +398,8 @@ qsa_status_t qsa_index_topk_varlen(const qsa_index_desc_t* desc, const uint16_t*
   }
   const qsa::IndexPlan p =
       qsa::plan_index(desc->n_idx_heads, desc->top_k_blocks, batch, max_q, max_q_end, r, false);
+  const qsa::PlanCheck pc = qsa::check_index_plan(p, batch, max_q);
+  if (pc.unfit) return fail(QSA_ERR_UNSUPPORTED, "index_topk_varlen: %s", pc.unfit);
   if (workspace_bytes < p.workspace || (p.workspace && !workspace))
     return fail(QSA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", workspace_bytes, p.workspace);
   if (!aligned(workspace, 16)) return fail(QSA_ERR_MISALIGNED, "workspace must be 16-byte aligned");
@@ -384,6 +436,8 @@ qsa_status_t qsa_sparse_attn_prefill_paged(const qsa_attn_desc_t* desc, int32_t 
       !aligned(sel_count, 4) || !aligned(lse, 4))
     return fail(QSA_ERR_MISALIGNED, "int32/fp32 arrays must be 4-byte aligned");
   const qsa::AttnPlan p = qsa::plan_attn(total_q, (int64_t)top_k_blocks * block_size, false);
+  const qsa::PlanCheck pc = qsa::check_attn_plan(p, desc->n_q_heads, desc->n_kv_heads, top_k_blocks, block_size);
+  if (pc.unfit) return fail(QSA_ERR_UNSUPPORTED, "sparse_attn_prefill_paged: %s", pc.unfit);
   const qsa::PagedRows pg{cu_q, q_pos0, batch, page_table, max_pages, __builtin_ctz((unsigned)page_size)};
   return hip_status(qsa::launch_attn(p, q, k_pages, v_pages, 0, 0, nullptr, desc->n_q_heads,
                                      desc->n_kv_heads, block_size, top_k_blocks, sel_blocks, sel_count,

@@ -728,9 +728,14 @@ __global__ __launch_bounds__(64 * (2 * W + NC), 1) void gdn_scan_kernel(
       for (int r = 0; r < 4; ++r) O[rt][r] *= sg;
     }
     // wait for the chunk's R (the recurrence wave always gets there; the
-    // bound only keeps a fault from turning into a hang)
+    // bound only keeps a fault from turning into a hang, and if it ever ran
+    // out the chunk's output is stored as NaN rather than from a stale R)
+    bool handed = false;
     for (int spin = 0; spin < (1 << 24); ++spin) {
-      if (__hip_atomic_load(&r_ready[set], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) > c) break;
+      if (__hip_atomic_load(&r_ready[set], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) > c) {
+        handed = true;
+        break;
+      }
       __builtin_amdgcn_s_sleep(1);
     }
     asm volatile("" ::: "memory");
@@ -739,6 +744,10 @@ __global__ __launch_bounds__(64 * (2 * W + NC), 1) void gdn_scan_kernel(
     for (int rt = 0; rt < 4; ++rt) {
       O[rt] = mfma16(Rb0, *reinterpret_cast<const u32x4*>(&s.MT[(16 * rt + cl) * kMP + 8 * grp]), O[rt]);
       O[rt] = mfma16(Rb1, *reinterpret_cast<const u32x4*>(&s.MT[(16 * rt + cl) * kMP + 32 + 8 * grp]), O[rt]);
+    }
+    if (!handed) {
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) O[rt] = f32x4{NAN, NAN, NAN, NAN};
     }
     const int64_t t0 = (int64_t)c * kC;
     const int n = (int)min<int64_t>(kC, T - t0);

@@ -45,6 +45,8 @@
 #include "qsa_internal.h"
 #include "select.h"
 
+#include <algorithm>
+
 namespace qsa {
 
 namespace {
@@ -1235,6 +1237,69 @@ IndexPlan plan_index(int hi, int k, int batch, int n_q, int64_t max_q_end, int r
   // the wide kernel leaves up to `cap` entries per split; the other at most `keep`
   p.select_lds = (size_t)p.splits * (p.wide ? cap : (keep > 0 ? keep : 1)) * sizeof(uint2);
   return p;
+}
+
+// Device limits the plans are checked against (MI355X / gfx950).
+constexpr int64_t kMaxGridX = 0x7FFFFFFF, kMaxGridYZ = 65535;
+constexpr size_t kMaxLds = 160 * 1024;
+
+// Upper bounds of the kernels' static LDS (their __shared__ arrays, plus
+// alignment slack).
+constexpr size_t kLdsSlack = 64;
+constexpr size_t prefill_static_lds(int nw) {
+  return (size_t)(nw == 3 ? 3 : 4) * 64 * 128 + (size_t)nw * (256 * 4 + 4) + 4 + kLdsSlack;
+}
+constexpr size_t kStreamStaticLds = 4 * 256 * 4 + kLdsSlack;
+constexpr size_t kSelectStaticLds = (256 + 10 + kSelScratch + 9) * 4 + kLdsSlack;
+constexpr size_t kDecodeScanStaticLds =
+    (256 + 2 + 2 * (kScanThreads / kWave) + kDecodeSplit + 3 * (kScanThreads / kWave)) * 4 + kLdsSlack;
+constexpr size_t kDecodeSelectStaticLds =
+    (256 + 2 + 2 * (kMergeThreads / kWave) + kSelScratch + 2 * (kMergeThreads / kWave)) * 4 + kLdsSlack;
+
+static PlanCheck finish_check(PlanCheck c) {
+  c.unfit = nullptr;
+  for (int i = 0; i < c.n; ++i) {
+    const LaunchShape& l = c.l[i];
+    if (l.grid[0] < 1 || (int64_t)l.grid[0] > kMaxGridX || l.grid[1] > kMaxGridYZ || l.grid[2] > kMaxGridYZ ||
+        l.grid[1] < 1 || l.grid[2] < 1)
+      c.unfit = "a launch grid exceeds the device's limits";
+    else if (l.block > 1024)
+      c.unfit = "a workgroup exceeds 1024 threads";
+    else if (l.lds > kMaxLds)
+      c.unfit = "a workgroup exceeds 160 KiB of LDS";
+  }
+  if (!c.unfit && c.max_i32 >= ((int64_t)1 << 31)) c.unfit = "a kernel index would exceed 32 bits";
+  if (!c.unfit && c.max_offset >= ((int64_t)1 << 62)) c.unfit = "a workspace offset would exceed 2^62";
+  return c;
+}
+
+static uint32_t grid_dim(int64_t v) { return v > 0xFFFFFFFFll ? 0xFFFFFFFFu : (uint32_t)v; }
+
+PlanCheck check_index_plan(const IndexPlan& p, int batch, int n_q) {
+  PlanCheck c{};
+  if (p.decode) {
+    c.n = 2;
+    c.l[0] = LaunchShape{{grid_dim(p.splits), grid_dim(batch), 1}, (uint32_t)kScanThreads, kDecodeScanStaticLds};
+    c.l[1] = LaunchShape{{grid_dim(batch), 1, 1}, (uint32_t)kMergeThreads, kDecodeSelectStaticLds + p.select_lds};
+    c.max_i32 = std::max<int64_t>({(int64_t)p.splits * kDecodeSplit, p.max_cand, (int64_t)p.splits * p.list_cap,
+                                   (int64_t)batch});
+    c.max_offset = std::max<int64_t>((int64_t)batch * p.score_stride,
+                                     (int64_t)batch * p.splits * (int64_t)p.list_cap);
+    return finish_check(c);
+  }
+  c.n = 2;
+  if (p.wide) {
+    c.l[0] = LaunchShape{{grid_dim(((int64_t)p.n_qgroups + p.nw - 1) / p.nw), grid_dim(p.splits), grid_dim(batch)},
+                         (uint32_t)(64 * (p.nw + 1)), prefill_static_lds(p.nw) + p.stream_lds};
+  } else {
+    c.l[0] = LaunchShape{{grid_dim(((int64_t)p.n_qgroups * p.splits + 3) / 4), grid_dim(batch), 1}, 256u,
+                         kStreamStaticLds + p.stream_lds};
+  }
+  c.l[1] = LaunchShape{{grid_dim((int64_t)batch * n_q), 1, 1}, 256u, kSelectStaticLds + p.select_lds};
+  c.max_i32 = std::max<int64_t>({(int64_t)n_q + p.qw, (int64_t)p.n_qgroups * p.splits,
+                                 p.max_cand + p.split_len, (int64_t)p.splits * p.cap});
+  c.max_offset = (int64_t)batch * n_q * p.splits * (int64_t)p.cap;
+  return finish_check(c);
 }
 
 hipError_t launch_index_topk(const IndexPlan& p, const uint16_t* idx_q, const uint16_t* cmp_k,

@@ -11,6 +11,26 @@ hipError_t launch_compress(const uint16_t* idx_k, int64_t k_stride, int batch, i
                            int64_t first, int64_t n, uint16_t* cmp, int64_t c_stride,
                            hipStream_t stream);
 
+// One kernel launch of a plan: grid, threads and LDS bytes per workgroup.
+struct LaunchShape {
+  uint32_t grid[3];
+  uint32_t block;
+  size_t lds;  // static (an upper bound from the kernel's __shared__ arrays) + dynamic
+};
+
+// The launches of a plan and the largest values its kernels hold: a plan is
+// refused (the calls return QSA_ERR_UNSUPPORTED) unless every grid, block and
+// LDS size is within the device's limits, every value held in a 32-bit int
+// is below 2^31, and every element offset into the workspace (64-bit in the
+// kernels) is below 2^62.
+struct PlanCheck {
+  int n;
+  LaunchShape l[3];
+  int64_t max_i32;     // largest value a kernel holds in an int (query, task, candidate, slot)
+  int64_t max_offset;  // largest element offset into a workspace region
+  const char* unfit;   // nullptr when the plan fits
+};
+
 // How qsa_index_topk cuts its work: wave tasks = (query group, candidate split).
 struct IndexPlan {
   bool decode;     // one query per sequence: split scan + verified merge
@@ -36,6 +56,8 @@ struct IndexPlan {
 IndexPlan plan_index(int hi, int k, int batch, int n_q, int64_t max_q_end, int r,
                      bool allow_decode = true);
 
+PlanCheck check_index_plan(const IndexPlan& p, int batch, int n_q);
+
 hipError_t launch_index_topk(const IndexPlan& p, const uint16_t* idx_q, const uint16_t* cmp_k,
                              int64_t cmp_stride, const int32_t* q_pos0, int batch, int n_q, int r,
                              int k, float w, int32_t* sel, int32_t* sel_cnt, void* ws,
@@ -50,6 +72,7 @@ struct AttnPlan {
 
 AttnPlan plan_attn(int batch_rows, int64_t max_tokens, bool split_kv);
 size_t attn_workspace_bytes(const AttnPlan& p, int Hq);
+PlanCheck check_attn_plan(const AttnPlan& p, int Hq, int Hkv, int top_k, int r);
 
 // Packed variable-length rows over a paged K/V pool (all null: not used).
 // Sequence b owns rows [cu_q[b], cu_q[b + 1]) at positions q_pos[b] + i; its

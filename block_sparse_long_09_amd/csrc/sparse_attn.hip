@@ -28,6 +28,8 @@
 #include "qsa_device.h"
 #include "qsa_internal.h"
 
+#include <algorithm>
+
 namespace qsa {
 
 namespace {
@@ -399,6 +401,31 @@ size_t attn_workspace_bytes(const AttnPlan& p, int Hq) {
   if (p.splits == 1) return 0;
   const size_t n = (size_t)p.rows * p.splits * Hq;
   return n * kD * sizeof(float) + ((n * sizeof(float2) + 255) / 256 * 256) + 256;
+}
+
+PlanCheck check_attn_plan(const AttnPlan& p, int Hq, int Hkv, int top_k, int r) {
+  PlanCheck c{};
+  // static LDS of attn_gather_kernel: V tiles, block ids and their pages,
+  // and (fewer than four KV heads) the cross-wave merge of (m, l, O)
+  const size_t gather_lds = (size_t)4 * kChunk * kVPitch * 2 + 2 * kSelLds * 4 +
+                            (Hkv < 4 ? (size_t)4 * 16 * kD * 4 + 2 * 4 * 16 * 4 : 0) + 64;
+  c.n = p.splits > 1 ? 2 : 1;
+  c.l[0] = LaunchShape{{p.rows > 0xFFFFFFFF ? 0xFFFFFFFFu : (uint32_t)p.rows, (uint32_t)p.splits, 1}, 256u,
+                       gather_lds};
+  c.l[1] = LaunchShape{{p.rows > 0xFFFFFFFF ? 0xFFFFFFFFu : (uint32_t)p.rows, (uint32_t)Hq, 1}, (uint32_t)kD,
+                       (size_t)kMaxMergeSplits * 4 + 4 * 4 + 64};
+  c.max_i32 = std::max<int64_t>({(int64_t)p.split_tokens, (int64_t)top_k * r, (int64_t)p.splits});
+  c.max_offset = (int64_t)p.rows * p.splits * Hq * (int64_t)kD;
+  c.unfit = nullptr;
+  for (int i = 0; i < c.n; ++i) {
+    const LaunchShape& l = c.l[i];
+    if (l.grid[0] < 1 || l.grid[0] > 0x7FFFFFFFu || l.grid[1] < 1 || l.grid[1] > 65535u) c.unfit = "a launch grid exceeds the device's limits";
+    else if (l.lds > 160 * 1024) c.unfit = "a workgroup exceeds 160 KiB of LDS";
+  }
+  if (!c.unfit && top_k > kSelLds) c.unfit = "more kept blocks than the gather stages";
+  if (!c.unfit && p.splits > kMaxMergeSplits) c.unfit = "more splits than the merge takes";
+  if (!c.unfit && c.max_i32 >= ((int64_t)1 << 31)) c.unfit = "a kernel index would exceed 32 bits";
+  return c;
 }
 
 hipError_t launch_attn(const AttnPlan& p, const uint16_t* q, const uint16_t* k, const uint16_t* v,

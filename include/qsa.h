@@ -49,7 +49,8 @@ extern "C" {
 typedef enum {
   QSA_OK = 0,
   QSA_ERR_INVALID_ARGUMENT = 1, /* null pointer, negative size, inconsistent shapes */
-  QSA_ERR_UNSUPPORTED = 2,      /* a shape outside the supported set above */
+  QSA_ERR_UNSUPPORTED = 2,      /* a shape outside the supported set above, or sizes whose launch
+                                   plan does not fit the device (qsa_bench.h, diagnostics) */
   QSA_ERR_MISALIGNED = 3,       /* a tensor pointer or stride breaks 16-byte alignment */
   QSA_ERR_WORKSPACE_TOO_SMALL = 4,
   QSA_ERR_HIP = 5               /* the HIP runtime reported an error at launch */
@@ -86,7 +87,10 @@ qsa_status_t qsa_compress_keys(const uint16_t* idx_k, int64_t idx_k_batch_stride
                                void* stream);
 
 /* Bytes of workspace qsa_index_topk needs for these sizes (0 on bad input).
- * max_q_end: an upper bound on q_pos0[b] + n_q over the batch. */
+ * max_q_end: an upper bound on q_pos0[b] + n_q over the batch. The positions
+ * q_pos0 live in device memory, which the host does not read (no
+ * synchronisation), so the candidate range that sizes the buffers and the
+ * split plan comes from this bound. */
 size_t qsa_index_topk_workspace_size(const qsa_index_desc_t* desc, int32_t batch, int32_t n_q,
                                      int64_t max_q_end);
 
@@ -111,7 +115,10 @@ qsa_status_t qsa_index_topk(const qsa_index_desc_t* desc, const uint16_t* idx_q,
                             int32_t* sel_blocks, int32_t* sel_count, void* workspace,
                             size_t workspace_bytes, void* stream);
 
-/* Bytes of workspace the sparse attention calls need (0 on bad input). */
+/* Bytes of workspace the sparse attention calls need (0 on bad input). The
+ * decode call splits each sequence's token list (top_k_blocks * block_size
+ * tokens) over several workgroups and merges their partial results in the
+ * workspace, so its size depends on block_size as well. */
 size_t qsa_sparse_attn_workspace_size(const qsa_attn_desc_t* desc, int32_t batch, int32_t n_q,
                                       int32_t top_k_blocks, int32_t block_size);
 
@@ -132,7 +139,11 @@ qsa_status_t qsa_sparse_attn_prefill(const qsa_attn_desc_t* desc, int32_t block_
                                      uint16_t* out, float* lse, void* workspace,
                                      size_t workspace_bytes, void* stream);
 
-/* Sparse attention, decode: one query per sequence at position kv_len[b] - 1.
+/* Sparse attention, decode (news page, section 2 item 1: QSA speeds up the
+ * decoding of long contexts as well as their prefill; explainer page,
+ * sparse-attention section: each new token attends only to the tokens of its
+ * kept blocks): one query per sequence at position kv_len[b] - 1, the newest
+ * token, already in the cache.
  *   q        [batch][Hq][D]
  *   k_cache, v_cache [batch][max_len][Hkv][D]
  *   kv_len   DEVICE int32 [batch], 1 <= kv_len[b] <= max_len.
