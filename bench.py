@@ -130,6 +130,8 @@ def main():
     ap.add_argument("--config", default="c5", choices=["c5", "c3", "c4", "c6"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="default workload only: skip the 256K prefill and 128K decode sections")
     ap.add_argument("--cpu-sample", type=int, default=256, help="queries in the oracle's timed sample")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="also run one plain device copy of this size (counter calibration runs)")
@@ -142,7 +144,12 @@ def main():
                     help="micro-block size r of a variant run (default: the workload's, 4)")
     ap.add_argument("--budget", type=int, default=0,
                     help="token budget k*r of a variant run (default: the workload's, 2048)")
+    ap.add_argument("--summarize-traffic", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "KEY"),
+                    help="write profiles/traffic.json entries KEY (c5, c3 or c4) from two rocprofv3 --pmc "
+                         "output folders (FETCH_SIZE, WRITE_SIZE) of a run with --calibrate-copy-mib")
     args = ap.parse_args()
+    if args.summarize_traffic:
+        return summarize_traffic(*args.summarize_traffic)
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
               "(the path would shard by sequence or query chunk; no multi-GPU run exists)",
@@ -156,7 +163,6 @@ def main():
     from gen.device import idx_keys_to_device, normal_to_device
 
     torch.cuda.set_device(0)
-    dev = "cuda"
     if args.config == "c6":
         return run_paged_batch(args, torch, qsa)
     if args.kl:
@@ -183,6 +189,27 @@ def main():
         def variant(W):
             return dataclasses.replace(W, name=f"{W.name}_r{r}_budget{budget}", r=r, k=budget // r) if W else None
         Wp, Wd = variant(Wp), variant(Wd)
+
+    out = measure(Wp, Wd, args, torch, qsa, args.steps, args.warmup, headline=True)
+    if args.config == "c5" and not (args.block_size or args.budget) and not args.no_extra:
+        # the rest of the metric: the 256K chunked prefill and the 128K decode batch
+        out["extra"] = {}
+        for key, (Wp2, Wd2, steps) in {"c3": (CONFIGS["c3"], None, 2), "c4": (None, CONFIGS["c4"], 10)}.items():
+            torch.cuda.empty_cache()
+            r = measure(Wp2, Wd2, args, torch, qsa, steps, 1, headline=False)
+            out["extra"][key] = {k: r[k] for k in ("config", "ms_per_step", "prefill_ms", "prefill_tokens_per_s",
+                                                   "decode_us_per_step", "phase_ms", "roofline", "rooflines",
+                                                   "cpu_baseline", "sample_parity") if k in r}
+    print(json.dumps(out), flush=True)
+
+
+def measure(Wp, Wd, args, torch, qsa, steps, warmup, headline):
+    """One prefill workload (Wp, chunked as it says) and/or one decode workload
+    (Wd): inputs generated into HBM, `warmup` untimed steps, `steps` timed
+    ones; returns the fields of the JSON line."""
+    from block_sparse_long_09_amd.pipeline import DecodePath, PrefillPath
+    from gen.device import idx_keys_to_device, normal_to_device
+    dev = "cuda"
 
     t_setup = time.time()
     # ------------------------------------------------------------- inputs --
@@ -244,22 +271,22 @@ def main():
                 lambda: dp.attend(D["Q"], D["Kc"], D["Vc"], D["kv_len"])]
     timer = PhaseTimer(torch, names)
 
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         timer.run(fns)
     torch.cuda.synchronize()
     # phase timing (events between launches, on the launch stream)
-    recorded = [timer.run(fns) for _ in range(args.steps)]
+    recorded = [timer.run(fns) for _ in range(steps)]
     torch.cuda.synchronize()
     for evs in recorded:
         timer.collect(evs)
     # whole-step wall clock over exactly `steps` steps
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
+    for _ in range(steps):
         for f in fns:
             f()
     torch.cuda.synchronize()
-    wall = (time.perf_counter() - t0) / args.steps
+    wall = (time.perf_counter() - t0) / steps
     phase = timer.mean_ms()
 
     def ssum(prefix):
@@ -284,14 +311,15 @@ def main():
                 work[key] += wk[key]
         n_ch = W.n_q // chunk
         ms_attn, ms_idx = ssum("attn_prefill"), ssum("index_prefill")
+        wkey = "c5" if Wp.name.startswith("c5a") else Wp.name.split("_")[0]
         roof["attn_prefill"] = {
             "bound": "hbm", "achieved": work["attn_bytes"] / (ms_attn * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
-            "unit": "GB/s", "traffic": load_traffic(f"attn_prefill_{args.config}", sha_attn),
+            "unit": "GB/s", "traffic": load_traffic(f"attn_prefill_{wkey}", sha_attn),
             "bytes_per_launch": work["attn_bytes"] // n_ch, "avg_launch_ms": ms_attn / n_ch,
             "mfma_tflops": work["attn_flops"] / (ms_attn * 1e-3) / 1e12}
         roof["index_prefill"] = {
             "bound": "mfma", "achieved": work["index_flops"] / (ms_idx * 1e-3) / 1e12, "peak": MFMA_BF16_PEAK_TFS,
-            "unit": "TFLOP/s", "traffic": load_traffic(f"index_prefill_{args.config}", sha_idx),
+            "unit": "TFLOP/s", "traffic": load_traffic(f"index_prefill_{wkey}", sha_idx),
             "flops_per_launch": work["index_flops"] // n_ch, "avg_launch_ms": ms_idx / n_ch}
         P["work"] = work
     if Wd is not None:
@@ -299,7 +327,8 @@ def main():
         wd = decode_work(W)
         ms = decode_ms
         roof["decode"] = {"bound": "hbm", "achieved": (wd["index_bytes"] + wd["attn_bytes"]) / (ms * 1e-3) / 1e9,
-                          "peak": HBM_PEAK_GBS, "unit": "GB/s", "traffic": None,
+                          "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                          "traffic": decode_traffic(args.config if headline else "c4", sha_idx, sha_attn),
                           "bytes_per_step": wd["index_bytes"] + wd["attn_bytes"]}
         D["work"] = wd
     for v in roof.values():
@@ -310,7 +339,7 @@ def main():
 
     # -------------------------------------------------------------- dense ----
     dense = None
-    if not args.no_dense:
+    if not args.no_dense and headline:
         dense = {}
         if Wd is not None:
             W = Wd
@@ -354,7 +383,7 @@ def main():
             dense["prefill_attention_only_speedup"] = pms / ssum("attn_prefill")
 
     # --------------------------------------------------------- calibration ---
-    if args.calibrate_copy_mib:
+    if args.calibrate_copy_mib and headline:
         n = args.calibrate_copy_mib << 20
         a = torch.empty(n, dtype=torch.uint8, device=dev)
         b = torch.empty_like(a)
@@ -364,8 +393,15 @@ def main():
     # ---------------------------------------------------------- CPU oracle ---
     cpu = None
     sample_parity = None
-    if not args.no_cpu_baseline and Wp is not None and P["chunk"] == Wp.n_q:
-        cpu, sample_parity = cpu_baseline(Wp, P, args.cpu_sample)
+    if not args.no_cpu_baseline and Wp is not None:
+        cpu, sample_parity = cpu_baseline(Wp, P, args.cpu_sample if headline else 128)
+    if not args.no_cpu_baseline and Wd is not None:
+        dcpu, dpar = decode_cpu_baseline(Wd, D, Wd.batch if Wd.batch <= 8 else 2)
+        if cpu is None:
+            cpu, sample_parity = dcpu, dpar
+        else:
+            cpu = dict(cpu, decode=dcpu)
+            sample_parity = dict(sample_parity, decode=dpar)
 
     W = Wp if Wp is not None else Wd
     value = (Wp.n_q if Wp is not None else Wd.batch) / wall
@@ -374,8 +410,8 @@ def main():
         "value": value,
         "unit": "tokens/s",
         "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
+        "steps": steps,
+        "warmup": warmup,
         "ms_per_step": wall * 1e3,
         "higher_is_better": True,
         "scaling": "weak",
@@ -386,7 +422,7 @@ def main():
                    "prefill_queries": Wp.n_q if Wp else 0, "context": W.L, "budget_tokens": W.k * W.r,
                    "block_size": W.r, "heads_q_kv_idx": [W.Hq, W.Hkv, W.Hi],
                    "decode_batch": Wd.batch if Wd else 0},
-        "prefill_ms": prefill_ms,
+        "prefill_ms": prefill_ms if Wp else None,
         "prefill_tokens_per_s": (Wp.n_q / (prefill_ms * 1e-3)) if Wp else None,
         "decode_us_per_step": decode_ms * 1e3 if Wd else None,
         "phase_ms": phase,
@@ -397,7 +433,7 @@ def main():
         "cpu_baseline": cpu,
         "sample_parity": sample_parity,
     }
-    print(json.dumps(out), flush=True)
+    return out
 
 
 def paged_work(W):
@@ -735,7 +771,10 @@ def cpu_baseline(W, P, n_sample):
     import gen
     import oracle
 
-    n_q = W.n_q
+    # the path's buffers hold the last chunk's outputs: sample its rows
+    n_q = P["chunk"]
+    first = W.n_q - n_q  # generated row of the chunk's row 0
+    q0 = W.q_pos0 + first
     run = 32  # consecutive queries per oracle call (OpenMP parallelises over them)
     n_runs = max(1, n_sample // run)
     starts = np.unique(np.linspace(0, n_q - run, n_runs).astype(np.int64))
@@ -744,26 +783,26 @@ def cpu_baseline(W, P, n_sample):
     ik = gen.idx_keys(W.seed, 0, W.L, 0, W.L, W.di, W.needle_window, W.r)
     K = gen.normal(W.seed, 2, (W.L, W.Hkv, W.D))
     V = gen.normal(W.seed, 3, (W.L, W.Hkv, W.D))
-    Qr = [gen.normal(W.seed, 1, (run, W.Hq, W.D), e0=int(s0) * W.Hq * W.D) for s0 in starts]
-    iqr = [gen.normal(W.seed, 4, (run, W.Hi, W.di), e0=int(s0) * W.Hi * W.di) for s0 in starts]
-    n_prefix = W.q_pos0 // W.r
-    blocks = np.empty((W.n_blk, W.di), np.uint16)
+    Qr = [gen.normal(W.seed, 1, (run, W.Hq, W.D), e0=(first + int(s0)) * W.Hq * W.D) for s0 in starts]
+    iqr = [gen.normal(W.seed, 4, (run, W.Hi, W.di), e0=(first + int(s0)) * W.Hi * W.di) for s0 in starts]
+    n_prefix = q0 // W.r
+    blocks = np.empty(((q0 + n_q) // W.r, W.di), np.uint16)
     blocks[:n_prefix] = oracle.compress(ik[:n_prefix * W.r], W.r)  # cached prefix, like the GPU's
     threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
     t0 = time.perf_counter()
-    blocks[n_prefix:] = oracle.compress(ik[n_prefix * W.r:], W.r)
+    blocks[n_prefix:] = oracle.compress(ik[n_prefix * W.r:(q0 + n_q) // W.r * W.r], W.r)
     t_comp = time.perf_counter() - t0
     sels, cnts = [], []
     t1 = time.perf_counter()
     for i, s0 in enumerate(starts):
-        s, c, _, _ = oracle.select(iqr[i], blocks, W.q_pos0 + int(s0), W.r, W.k, W.w)
+        s, c, _, _ = oracle.select(iqr[i], blocks, q0 + int(s0), W.r, W.k, W.w)
         sels.append(s)
         cnts.append(c)
     t_sel = time.perf_counter() - t1
     t2 = time.perf_counter()
     outs, lses = [], []
     for i, s0 in enumerate(starts):
-        o, l = oracle.sparse_attn(Qr[i], K, V, W.q_pos0 + int(s0), W.r, sels[i], cnts[i])
+        o, l = oracle.sparse_attn(Qr[i], K, V, q0 + int(s0), W.r, sels[i], cnts[i])
         outs.append(o)
         lses.append(l)
     t_att = time.perf_counter() - t2
@@ -771,8 +810,9 @@ def cpu_baseline(W, P, n_sample):
     outs = list(zip(np.concatenate(outs), np.concatenate(lses)))
     # per-query time of the sample, plus the chunk compression amortised over all queries
     per_q = (t_sel + t_att) / len(rows) + t_comp / n_q
-    cpu = {"value": 1.0 / per_q, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-           "sample": f"{len(rows)} of {n_q} prefill queries ({len(starts)} runs of {run} consecutive, evenly "
+    what = f"{n_q} queries of the last chunk" if n_q != W.n_q else f"{n_q} prefill queries"
+    cpu = {"value": 1.0 / per_q, "unit": "tokens/s", "cores": threads, "kind": "oracle", "cpu_model": cpu_model(),
+           "sample": f"{len(rows)} of {what} ({len(starts)} runs of {run} consecutive, evenly "
                      f"spaced) of {W.name}, plus the chunk's block compression; select {t_sel:.2f}s, "
                      f"attend {t_att:.2f}s, compress {t_comp:.2f}s"}
     # parity of the sampled rows (the GPU ran the same inputs)
@@ -787,6 +827,125 @@ def cpu_baseline(W, P, n_sample):
     lerr = max(float(np.abs(g_lse[r_] - outs[i][1]).max()) for i, r_ in enumerate(rows)
                if np.array_equal(g_sel[r_], sel[i]))
     return cpu, {"rows": len(rows), "selection_identical_rows": same_sel, "out_max_abs": err, "lse_max_abs": lerr}
+
+
+def summarize_traffic(fetch_dir, write_dir, key):
+    """Per-launch HBM bytes of the step's kernels from the counters of two
+    rocprofv3 runs of bench.py (FETCH_SIZE, then WRITE_SIZE, both with
+    --calibrate-copy-mib N), scaled by what the same counters read for the
+    plain device copy of N MiB in the same run; merged into
+    profiles/traffic.json under names ending in _KEY, each with the source
+    hash of its kernel file."""
+    import csv
+    import glob
+
+    def read(d, counter):
+        rows = {}
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            for r in csv.DictReader(open(f)):
+                if r["Counter_Name"] != counter:
+                    continue
+                wgs = int(r["Grid_Size"]) // max(1, int(r["Workgroup_Size"]))
+                k = (r["Kernel_Name"], wgs)
+                rows.setdefault(k, []).append(float(r["Counter_Value"]))
+        return rows
+
+    fetch, write = read(fetch_dir, "FETCH_SIZE"), read(write_dir, "WRITE_SIZE")
+    # the calibration copy: the non-library kernel that writes the most
+    copies = [(k, v) for k, v in write.items() if "qsa::" not in k[0]]
+    (ck, cw) = max(copies, key=lambda kv: max(kv[1]))
+    w_kib = max(cw)
+    f_kib = max(fetch.get(ck, [0.0]))
+    copy_bytes = round(w_kib * 1024 / (1 << 20)) << 20  # the copy writes its size once
+    roles = [("index_prefill_kernel", "index_prefill", "index_topk.hip"),
+             ("index_select_kernel", "index_select", "index_topk.hip"),
+             ("index_decode_scan_kernel", "decode_scan", "index_topk.hip"),
+             ("index_decode_select_kernel", "decode_merge", "index_topk.hip"),
+             ("attn_merge_kernel", "decode_attn_merge", "sparse_attn.hip"),
+             ("compress_kernel", "compress", "compress.hip")]
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    d = json.load(open(path)) if os.path.exists(path) else {}
+    d["calibration"] = {"copy_bytes": copy_bytes, "fetch_kib": f_kib, "write_kib": w_kib,
+                        "fetch_factor": copy_bytes / (f_kib * 1024), "write_factor": copy_bytes / (w_kib * 1024)}
+    ff, wf = d["calibration"]["fetch_factor"], d["calibration"]["write_factor"]
+    for (name, wgs), fv in fetch.items():
+        if "qsa::" not in name:
+            continue
+        role = None
+        for pat, r, src in roles:
+            if pat in name:
+                role, file = r, src
+        if "attn_gather_kernel" in name:
+            role, file = ("attn_prefill" if wgs >= 1024 else "decode_attn"), "sparse_attn.hip"
+        if role is None:
+            continue
+        wv = write.get((name, wgs), [0.0])
+        fk, wk = float(np.mean(fv)), float(np.mean(wv))
+        d[f"{role}_{key}"] = {"kernel": name.split("(")[0], "workgroups": wgs, "source_sha": source_sha(file),
+                              "fetch_kib_raw": fk, "write_kib_raw": wk, "fetch_bytes": fk * 1024 * ff,
+                              "write_bytes": wk * 1024 * wf, "bytes_per_launch": fk * 1024 * ff + wk * 1024 * wf}
+    with open(path, "w") as f:
+        json.dump(d, f, indent=1)
+    print(json.dumps({k: v.get("bytes_per_launch") for k, v in d.items() if k.endswith(key)}, indent=1))
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def decode_cpu_baseline(W, D, n_seq):
+    """The oracle's whole decode step (block keys of the cache compressed,
+    selection over every candidate, attention over the kept tokens) for the
+    first n_seq sequences, timed on the host cores, and the parity of those
+    sequences against the GPU's selection and output."""
+    import gen
+    import oracle
+    path = D["path"]
+    g_sel = path.sel[:, 0].cpu().numpy()
+    g_cnt = path.cnt[:, 0].cpu().numpy()
+    g_out = path.out.float().cpu().numpy()
+    g_lse = path.lse.cpu().numpy()
+    t = W.L - 1
+    t_or = 0.0
+    same = 0
+    err = lerr = 0.0
+    for b in range(n_seq):
+        ik = gen.idx_keys(W.seed, b, W.L, 0, W.L, W.di, W.needle_window, W.r)
+        Kb = gen.normal(W.seed, 2, (W.L, W.Hkv, W.D), e0=b * W.L * W.Hkv * W.D)
+        Vb = gen.normal(W.seed, 3, (W.L, W.Hkv, W.D), e0=b * W.L * W.Hkv * W.D)
+        qb = gen.normal(W.seed, 1, (1, W.Hq, W.D), e0=b * W.Hq * W.D)
+        iqb = gen.normal(W.seed, 4, (1, W.Hi, W.di), e0=b * W.Hi * W.di)
+        tc = time.perf_counter()
+        blocks = oracle.compress(ik, W.r)
+        s, c, _, _ = oracle.select(iqb, blocks, t, W.r, W.k, W.w)
+        o, lo = oracle.sparse_attn(qb, Kb, Vb, t, W.r, s, c)
+        t_or += time.perf_counter() - tc
+        if np.array_equal(g_sel[b], s[0]) and g_cnt[b] == c[0]:
+            same += 1
+            err = max(err, float(np.abs(g_out[b] - o[0]).max()))
+            lerr = max(lerr, float(np.abs(g_lse[b] - lo[0]).max()))
+        del Kb, Vb, ik
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    cpu = {"value_us_per_step": t_or / n_seq * W.batch * 1e6, "unit": "us/step", "cores": threads,
+           "kind": "oracle", "cpu_model": cpu_model(),
+           "sample": f"{n_seq} of {W.batch} sequences of {W.name}, whole step each (compress the cache's "
+                     f"{W.n_blk} block keys, select, attend: {t_or:.2f}s), scaled to the batch"}
+    return cpu, {"sequences": n_seq, "selection_identical": same, "out_max_abs": err, "lse_max_abs": lerr}
+
+
+def decode_traffic(key, sha_idx, sha_attn):
+    """Counter-derived HBM bytes of one decode step (every decode kernel of
+    the step), if the counters were taken on the current sources."""
+    parts = [load_traffic(f"decode_scan_{key}", sha_idx), load_traffic(f"decode_merge_{key}", sha_idx),
+             load_traffic(f"decode_attn_{key}", sha_attn), load_traffic(f"decode_attn_merge_{key}", sha_attn)]
+    return None if any(p is None for p in parts) else sum(parts)
 
 
 if __name__ == "__main__":
