@@ -63,6 +63,8 @@ _sig("qsa_sparse_attn_prefill", ctypes.c_int,
      [_PA, _i32, _i32, _vp, _vp, _vp, _i64, _i32, _i64, _vp, _vp, _vp, _vp, _vp, _sz, _vp])
 _sig("qsa_sparse_attn_decode", ctypes.c_int,
      [_PA, _i32, _i32, _vp, _vp, _vp, _i64, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _sz, _vp])
+_sig("qsa_sparse_attn_decode_noalloc", ctypes.c_int,
+     [_PA, _i32, _i32, _vp, _vp, _vp, _i64, _vp, _i32, _vp, _vp, _vp, _vp, _vp])
 _sig("qsa_dense_attn_workspace_size", _sz, [_PA, _i32, _i32, _i64])
 _sig("qsa_dense_attn_prefill", ctypes.c_int, [_PA, _vp, _vp, _vp, _i64, _i32, _i64, _vp, _vp, _vp, _sz, _vp])
 _sig("qsa_dense_attn_decode", ctypes.c_int, [_PA, _vp, _vp, _vp, _i64, _vp, _i32, _vp, _vp, _vp, _sz, _vp])
@@ -86,6 +88,7 @@ _sig("qsa_abi_version", ctypes.c_int, [])
 EXPORTS = (
     "qsa_compress_keys", "qsa_index_topk_workspace_size", "qsa_index_topk",
     "qsa_sparse_attn_workspace_size", "qsa_sparse_attn_prefill", "qsa_sparse_attn_decode",
+    "qsa_sparse_attn_decode_noalloc",
     "qsa_status_string", "qsa_last_error_message", "qsa_abi_version",
     "qsa_dense_attn_workspace_size", "qsa_dense_attn_prefill", "qsa_dense_attn_decode",
     "qsa_index_topk_varlen_workspace_size", "qsa_index_topk_varlen", "qsa_sparse_attn_prefill_paged",
@@ -264,6 +267,21 @@ def qsa_sparse_attn_decode(desc, block_size, q, k_cache, v_cache, kv_len, sel_bl
                                        _i32t(kv_len, "kv_len"), B, _i32t(sel_blocks, "sel_blocks"),
                                        _i32t(sel_count, "sel_count"), _bf16(out, "out"), _ptr(lse), ws, nbytes,
                                        _stream(stream)))
+
+
+def qsa_sparse_attn_decode_noalloc(desc, block_size, q, k_cache, v_cache, kv_len, sel_blocks, sel_count, out,
+                                   lse=None, stream=None):
+    """qsa_sparse_attn_decode without a workspace (the library's scratch on the
+    device; calls that overlap on one device race)."""
+    B = q.shape[0]
+    top_k = sel_blocks.shape[-1]
+    if lse is not None and lse.dtype != torch.float32:
+        raise TypeError("lse must be float32")
+    _check(_lib.qsa_sparse_attn_decode_noalloc(ctypes.byref(desc), block_size, top_k, _bf16(q, "q"),
+                                               _bf16(k_cache, "k_cache"), _bf16(v_cache, "v_cache"),
+                                               k_cache.shape[1], _i32t(kv_len, "kv_len"), B,
+                                               _i32t(sel_blocks, "sel_blocks"), _i32t(sel_count, "sel_count"),
+                                               _bf16(out, "out"), _ptr(lse), _stream(stream)))
 
 
 # ------------------------------------------------------------- comparator --

@@ -5,9 +5,18 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <mutex>
+
 #include "qsa.h"
 #include "qsa_bench.h"
 #include "qsa_internal.h"
+
+// Library-owned scratch of qsa_sparse_attn_decode_noalloc: the split-KV
+// partial results of a decode step. Each device holds its own copy (zero at
+// load) until the process ends; host code reaches it only through the address
+// hipGetSymbolAddress returns for the current device.
+constexpr size_t kNoAllocScratchBytes = 8u << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
 
 namespace {
 
@@ -293,6 +302,70 @@ qsa_status_t qsa_sparse_attn_plan_info(const qsa_attn_desc_t* desc, int32_t rows
   const qsa::PlanCheck c = qsa::check_attn_plan(p, desc->n_q_heads, desc->n_kv_heads, top_k_blocks, block_size);
   fill_info(c, qsa::attn_workspace_bytes(p, desc->n_q_heads), p.splits, (int)p.split_tokens, info);
   return ok();
+}
+
+/* --------------------------------------------------- allocation-free -------- */
+
+namespace {
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept.
+static qsa_status_t scratch_address(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(QSA_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(QSA_ERR_UNSUPPORTED, "device %d beyond %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(QSA_ERR_HIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return QSA_OK;
+}
+}  // namespace
+
+qsa_status_t qsa_sparse_attn_decode_noalloc(const qsa_attn_desc_t* desc, int32_t block_size,
+                                            int32_t top_k_blocks, const uint16_t* q, const uint16_t* k_cache,
+                                            const uint16_t* v_cache, int64_t max_len, const int32_t* kv_len,
+                                            int32_t batch, const int32_t* sel_blocks, const int32_t* sel_count,
+                                            uint16_t* out, float* lse, void* stream) {
+  qsa_status_t s = check_attn_common(desc, block_size, top_k_blocks);
+  if (s != QSA_OK) return s;
+  if (batch < 0 || max_len < 1 || max_len > kMaxPos)
+    return fail(QSA_ERR_INVALID_ARGUMENT, "need batch >= 0 and 1 <= max_len < 2^31");
+  if (batch == 0) return ok();
+  if (!q || !k_cache || !v_cache || !kv_len || !sel_blocks || !sel_count || !out)
+    return fail(QSA_ERR_INVALID_ARGUMENT, "NULL pointer argument");
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16))
+    return fail(QSA_ERR_MISALIGNED, "q/k_cache/v_cache/out must be 16-byte aligned");
+  if (!aligned(kv_len, 4) || !aligned(sel_blocks, 4) || !aligned(sel_count, 4) || !aligned(lse, 4))
+    return fail(QSA_ERR_MISALIGNED, "int32/fp32 arrays must be 4-byte aligned");
+  const qsa::AttnPlan p = qsa::plan_attn(batch, (int64_t)top_k_blocks * block_size, true);
+  const qsa::PlanCheck pc = qsa::check_attn_plan(p, desc->n_q_heads, desc->n_kv_heads, top_k_blocks, block_size);
+  if (pc.unfit) return fail(QSA_ERR_UNSUPPORTED, "sparse_attn_decode_noalloc: %s", pc.unfit);
+  const size_t need = qsa::attn_workspace_bytes(p, desc->n_q_heads);
+  if (need > kNoAllocScratchBytes)
+    return fail(QSA_ERR_UNSUPPORTED,
+                "sparse_attn_decode_noalloc: the step's partial results need %zu bytes, beyond the library's "
+                "%zu-byte scratch (use qsa_sparse_attn_decode with a workspace)",
+                need, kNoAllocScratchBytes);
+  void* ws = nullptr;
+  if (need) {
+    s = scratch_address(&ws);
+    if (s != QSA_OK) return s;
+  }
+  const int64_t stride = max_len * desc->n_kv_heads * desc->head_dim;
+  return hip_status(qsa::launch_attn(p, q, k_cache, v_cache, stride, 0, kv_len, desc->n_q_heads,
+                                     desc->n_kv_heads, block_size, top_k_blocks, sel_blocks, sel_count,
+                                     desc->softmax_scale, out, lse, ws, (hipStream_t)stream),
+                    "sparse_attn_decode_noalloc launch");
 }
 
 /* ----------------------------------------------------------- comparator --- */

@@ -157,6 +157,21 @@ qsa_status_t qsa_sparse_attn_decode(const qsa_attn_desc_t* desc, int32_t block_s
                                     uint16_t* out, float* lse, void* workspace,
                                     size_t workspace_bytes, void* stream);
 
+/* Sparse attention, decode, for callers that cannot allocate memory (code
+ * under stream or graph capture, tight serving loops, harnesses that forbid
+ * allocation): the same call and results as qsa_sparse_attn_decode without a
+ * workspace. The step's split partial results go to a scratch array the
+ * library holds on each device (8 MiB, allocated at load, kept until the
+ * process ends); nothing is allocated per call. Sizes whose partial results
+ * need more than that return QSA_ERR_UNSUPPORTED. Every call on one device
+ * shares that scratch: calls that may overlap on a device (other streams,
+ * other threads) race, so the caller serialises them. */
+qsa_status_t qsa_sparse_attn_decode_noalloc(const qsa_attn_desc_t* desc, int32_t block_size,
+                                            int32_t top_k_blocks, const uint16_t* q, const uint16_t* k_cache,
+                                            const uint16_t* v_cache, int64_t max_len, const int32_t* kv_len,
+                                            int32_t batch, const int32_t* sel_blocks, const int32_t* sel_count,
+                                            uint16_t* out, float* lse, void* stream);
+
 /* ---- Packed variable-length batches over a paged K/V cache (serving) ----
  * A batch of `batch` sequences whose new queries are packed row after row:
  * sequence b owns rows [cu_q[b], cu_q[b + 1]) of idx_q / q / sel / out, its
