@@ -100,41 +100,47 @@ __device__ __forceinline__ float compact_buffer(uint2* p, int n, int keep, uint3
 }
 
 typedef __attribute__((address_space(3))) uint32_t lds_u32;
+typedef __attribute__((address_space(3))) unsigned long long lds_u64;
 typedef __attribute__((address_space(1))) unsigned long long glb_u64;
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void glb_void_t;
 
-// Same as compact_buffer, staging only the keys in LDS (cap words) and
-// streaming the entries from global memory eight chunks at a time. Not
-// inlined (one copy serves every call site); its operands are typed with
-// their address spaces so LDS is addressed with ds_* and the buffer with
-// global_* instructions. An entry is one 64-bit word: key low, block high.
-__device__ __noinline__ float compact_keys_staged(glb_u64* p, int n, int keep, lds_u32* hist,
-                                                  lds_u32* kstage) {
+// s_waitcnt immediate: at most n (< 64) vector memory operations outstanding,
+// no wait on the other counters
+constexpr int vmcnt_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
+
+// Copy the n entries of a buffer into the wave's LDS stage (entry i to st[i])
+// with global_load_lds: 16 bytes (two entries) per lane per instruction, all
+// issued before one wait, no registers held. The buffer holds at least n
+// rounded up to 128 entries (its capacity is a multiple of 128), so every
+// load is in bounds. The wave's earlier appends to it have completed first.
+__device__ __forceinline__ void stage_entries(const glb_u64* p, int n, lds_u64* st) {
   const int lane = lane_id();
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
-  for (int base = 0; base < n; base += 8 * kWave) {
-    uint32_t v[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int i = base + u * kWave + lane;
-      v[u] = i < n ? (uint32_t)p[i] : 0u;
-    }
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int i = base + u * kWave + lane;
-      if (i < n) kstage[i] = v[u];
-    }
-  }
+  for (int base = 0; base < n; base += 128)
+    __builtin_amdgcn_global_load_lds((const glb_void_t*)(p + base + 2 * lane), (lds_void_t*)(st + base), 16, 0, 0);
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
   wave_sync();
+}
+
+// Exact compaction: reduce one query's buffer of n entries (block order) to
+// its exact top `keep` in place, keeping block order; returns the new
+// threshold. The entries are staged in LDS once; the selection and the keep
+// pass read them there. An entry is one 64-bit word: key low, block high. Not
+// inlined (one copy serves every call site).
+__device__ __noinline__ float compact_keys_staged(glb_u64* p, int n, int keep, lds_u32* hist, lds_u64* st) {
+  const int lane = lane_id();
+  stage_entries(p, n, st);
   uint32_t tk;
   int need;
-  wave_select([&](int i) { return (uint32_t)kstage[i]; }, n, keep, hist, tk, need);
+  wave_select([&](int i) { return (uint32_t)st[i]; }, n, keep, hist, tk, need);
   int kept = 0, ties = 0;
   for (int base = 0; base < n; base += 8 * kWave) {
     unsigned long long e[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const int i = base + u * kWave + lane;
-      e[u] = i < n ? p[i] : 0ull;
+      e[u] = i < n ? st[i] : 0ull;
     }
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
@@ -158,32 +164,31 @@ __device__ __noinline__ float compact_keys_staged(glb_u64* p, int n, int keep, l
 
 // Approximate in-loop compaction: keep, in block order, every entry whose key
 // is at least L, where L is the lower edge of the histogram bucket that holds
-// the keep-th largest key. The keys are staged in LDS and bucketed by their
-// offset from the smallest key (8 bits per pass below the offsets' leading
-// zeros); further passes refine the bucket while more than keep + 64 entries
-// would survive (a tight threshold lets fewer later candidates in, and leaves
-// the buffer room for many before the next compaction). At least `keep` entries survive, so the buffer stays a
+// the keep-th largest key. The entries are staged in LDS once and bucketed by
+// their key's offset from the smallest key (8 bits per pass below the
+// offsets' leading zeros); further passes refine the bucket while more than
+// keep + 64 entries would survive (a tight threshold lets fewer later
+// candidates in, and leaves the buffer room for many before the next
+// compaction). At least `keep` entries survive, so the buffer stays a
 // superset of the exact top `keep`; a later candidate with key <= L can never
 // enter it (at least `keep` entries with key >= L and a smaller block index
 // precede it). Returns (L, the number of entries kept); a pair by value keeps
 // the caller free of private (scratch) memory.
-__device__ __noinline__ uint2 compact_keys_approx(glb_u64* p, int n, int keep, lds_u32* hist,
-                                                  lds_u32* kstage) {
+__device__ __noinline__ uint2 compact_keys_approx(glb_u64* p, int n, int keep, lds_u32* hist, lds_u64* st) {
   const int lane = lane_id();
-  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+  stage_entries(p, n, st);
   uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
   for (int base = 0; base < n; base += 16 * kWave) {
     uint32_t v[16];
 #pragma unroll
     for (int u = 0; u < 16; ++u) {
       const int i = base + u * kWave + lane;
-      v[u] = i < n ? (uint32_t)p[i] : 0u;
+      v[u] = i < n ? (uint32_t)st[i] : 0u;
     }
 #pragma unroll
     for (int u = 0; u < 16; ++u) {
       const int i = base + u * kWave + lane;
       if (i < n) {
-        kstage[i] = v[u];
         kmin = min(kmin, v[u]);
         kmax = max(kmax, v[u]);
       }
@@ -194,7 +199,6 @@ __device__ __noinline__ uint2 compact_keys_approx(glb_u64* p, int n, int keep, l
     kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, off));
     kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, off));
   }
-  wave_sync();
   // radix passes on key - kmin: the bucket [kbase, kbase + 2^hi) holds the
   // keep-th largest key
   uint32_t kbase = kmin;
@@ -215,7 +219,7 @@ __device__ __noinline__ uint2 compact_keys_approx(glb_u64* p, int n, int keep, l
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         const int i = base + u * kWave + lane;
-        kk[u] = i < n ? kstage[i] : 0u;
+        kk[u] = i < n ? (uint32_t)st[i] : 0u;
       }
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
@@ -242,7 +246,7 @@ __device__ __noinline__ uint2 compact_keys_approx(glb_u64* p, int n, int keep, l
 #pragma unroll
     for (int u = 0; u < 16; ++u) {
       const int i = base + u * kWave + lane;
-      e[u] = i < n ? p[i] : 0ull;
+      e[u] = i < n ? st[i] : 0ull;
     }
 #pragma unroll
     for (int u = 0; u < 16; ++u) {
@@ -473,11 +477,7 @@ __global__ __launch_bounds__(256) void index_stream_kernel(
 // area) when one nears capacity. Splits end with at most `cap` entries; the
 // select kernel takes them as they are.
 constexpr int kPrefillDepth = 2;      // tiles the copy wave keeps in flight
-typedef __attribute__((address_space(3))) void lds_void_t;
-typedef __attribute__((address_space(1))) void glb_void_t;
-// s_waitcnt immediate: at most n (< 64) vector memory operations outstanding,
-// no wait on the other counters
-constexpr int prefill_vmcnt(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
+constexpr int prefill_vmcnt(int n) { return vmcnt_imm(n); }
 template <int HI, int AT, bool SCALE_EPI, int NW>
 __global__ __launch_bounds__(64 * (NW + 1)) __attribute__((amdgpu_waves_per_eu(NW == 4 ? 4 : 3)))
 void index_prefill_kernel(
@@ -502,7 +502,7 @@ void index_prefill_kernel(
   __shared__ uint32_t hist_all[NW][256];
   __shared__ int wg_lim[NW];
   __shared__ int wg_compact;  // tile before which every wave compacts its fuller buffers
-  extern __shared__ uint32_t kstage_all[];  // 4 x cap keys: each wave's compaction stage
+  extern __shared__ unsigned long long kstage_all[];  // NW x cap entries: each wave's compaction stage
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // 4: the copy wave
@@ -516,7 +516,7 @@ void index_prefill_kernel(
   const int split = blockIdx.y;
   const int b = blockIdx.z;
   lds_u32* hist_l = (lds_u32*)hist_all[copier ? 0 : wave];
-  lds_u32* kstage_l = (lds_u32*)(kstage_all + (copier ? 0 : wave) * cap);
+  lds_u64* kstage_l = (lds_u64*)(kstage_all + (copier ? 0 : wave) * cap);
 
   const int64_t pos0 = q_pos0[b];
   // this sequence's query rows: [row0, row0 + nqb) (packed rows when cu_q is given)
@@ -1222,18 +1222,26 @@ IndexPlan plan_index(int hi, int k, int batch, int n_q, int64_t max_q_end, int r
   if (split_len < 64) split_len = 64;
   p.splits = (int)splits;
   p.split_len = (int)split_len;
-  // (4 compute waves: 4 x cap staged keys and a 32 KiB tile ring must stay
-  // within 64 KiB of LDS for two workgroups per CU)
-  int cap = p.wide && p.nw == 4 ? 1536 : 2048;
-  if (cap < 2 * keep + 64) cap = (2 * keep + 64 + 63) / 64 * 64;
-  if (cap < keep + 2 * 64) cap = keep + 2 * 64;
+  // Buffer entries per (query, split). The many-query kernel stages a whole
+  // buffer in its wave's LDS to compact it (8 bytes per entry), so the
+  // capacity follows the LDS left per wave: 1792 at 8 compute waves (one
+  // workgroup per CU), 1280 at 4 (two per CU), 1024 at 3 (three per CU). It
+  // must exceed k - 1 by room for a compaction interval (kept entries stay
+  // below cap - 192, see the exact fallback) and a margin; a split shorter
+  // than the capacity never needs more than its candidates. A multiple of 128:
+  // staging copies whole 128-entry pieces.
+  int cap = p.wide ? (p.nw == 8 ? 1792 : (p.nw == 4 ? 1280 : 1024)) : 2048;
+  if (!p.wide && cap < 2 * keep + 64) cap = 2 * keep + 64;
+  if (cap < keep + 448) cap = keep + 448;
   if ((int64_t)split_len + 64 <= cap) cap = (int)split_len + 64;
+  cap = (cap + 127) / 128 * 128;
   p.cap = cap;
   p.buf_bytes = (size_t)batch * n_q * p.splits * (size_t)cap * sizeof(uint2);
   p.cnt_bytes = (size_t)batch * n_q * p.splits * sizeof(int);
   p.workspace = p.buf_bytes + ((p.cnt_bytes + 255) / 256 * 256);
-  // LDS per workgroup: the wide kernel stages nw x cap keys, the other 4 x cap entries
-  p.stream_lds = p.wide ? (size_t)p.nw * cap * sizeof(uint32_t) : (size_t)4 * cap * sizeof(uint2);
+  // LDS per workgroup: each wave's compaction stage of cap entries (nw waves
+  // in the wide kernel, 4 in the other)
+  p.stream_lds = (size_t)(p.wide ? p.nw : 4) * cap * sizeof(uint2);
   // the wide kernel leaves up to `cap` entries per split; the other at most `keep`
   p.select_lds = (size_t)p.splits * (p.wide ? cap : (keep > 0 ? keep : 1)) * sizeof(uint2);
   return p;
