@@ -99,6 +99,41 @@ def test_prefill_full_size_sampled_rows(qsa, name):
     _say(name, "rows in the tie band:", n_band, "of", len(rows))
 
 
+def test_prefill_attention_two_chunks_in_flight(qsa):
+    """K and V of 300,000 tokens (614 MB, past the 512 MiB from which each
+    wave keeps two chunks in flight): rows at the start of the context (lists
+    of 1..12 blocks, ragged against the 32-token chunks) and at its end match
+    the oracle on the oracle's selections, and rows given only the K/V prefix
+    they need (one chunk in flight) give the same bits."""
+    Hq, Hkv, Hi, D, di, r, k, seed = 32, 4, 8, 128, 64, 4, 512, 4242
+    L = 300_000
+    _say("prefill attention, two chunks in flight, L", L)
+    K = normal_to_device(seed, 2, (L, Hkv, D))
+    V = normal_to_device(seed, 3, (L, Hkv, D))
+    Kh = gen.normal(seed, 2, (L, Hkv, D))
+    Vh = gen.normal(seed, 3, (L, Hkv, D))
+    blocks = oracle.compress(gen.idx_keys(seed, 0, L, 0, L, di, 4096, r), r)
+    desc = qsa.attn_desc(Hq, Hkv, D)
+    for q0, n in [(0, 45), (150_001, 37), (L - 29, 29)]:
+        _say("rows", q0, "..", q0 + n - 1)
+        Qh = gen.normal(seed, 1, (n, Hq, D), e0=q0 * Hq * D)
+        iqh = gen.normal(seed, 4, (n, Hi, di), e0=q0 * Hi * di)
+        o_sel, o_cnt, _, _ = oracle.select(iqh, blocks, q0, r, k, 1.0 / Hi)
+        sel = torch.from_numpy(np.ascontiguousarray(o_sel)).cuda()
+        cnt = torch.from_numpy(np.ascontiguousarray(o_cnt)).cuda()
+        Q = dev(Qh)
+        out = torch.empty((n, Hq, D), dtype=torch.bfloat16, device="cuda")
+        lse = torch.empty((n, Hq), dtype=torch.float32, device="cuda")
+        qsa.qsa_sparse_attn_prefill(desc, r, Q, K, V, q0, sel, cnt, out, lse)
+        out1 = torch.empty_like(out)
+        lse1 = torch.empty_like(lse)
+        qsa.qsa_sparse_attn_prefill(desc, r, Q, K[:q0 + n], V[:q0 + n], q0, sel, cnt, out1, lse1)
+        torch.cuda.synchronize()
+        o_out, o_lse = oracle.sparse_attn(Qh, Kh, Vh, q0, r, o_sel, o_cnt)
+        check_attention(out, lse, o_out, o_lse, f"rows {q0}..")
+        assert torch.equal(out.view(torch.int16), out1.view(torch.int16)) and torch.equal(lse, lse1)
+
+
 @pytest.mark.parametrize("name", ["c4", "c5b"])
 def test_decode_full_size_sampled_rows(qsa, name):
     from block_sparse_long_09_amd.pipeline import DecodePath
