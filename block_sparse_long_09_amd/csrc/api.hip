@@ -215,8 +215,7 @@ qsa_status_t qsa_sparse_attn_prefill(const qsa_attn_desc_t* desc, int32_t block_
     return fail(QSA_ERR_MISALIGNED, "q/k/v/out must be 16-byte aligned");
   if (!aligned(sel_blocks, 4) || !aligned(sel_count, 4) || !aligned(lse, 4))
     return fail(QSA_ERR_MISALIGNED, "int32/fp32 arrays must be 4-byte aligned");
-  const qsa::AttnPlan p = qsa::plan_attn(n_q, (int64_t)top_k_blocks * block_size, false,
-                                         kv_len * desc->n_kv_heads * desc->head_dim * 4);
+  const qsa::AttnPlan p = qsa::plan_attn(n_q, (int64_t)top_k_blocks * block_size, false);
   const qsa::PlanCheck pc = qsa::check_attn_plan(p, desc->n_q_heads, desc->n_kv_heads, top_k_blocks, block_size);
   if (pc.unfit) return fail(QSA_ERR_UNSUPPORTED, "sparse_attn_prefill: %s", pc.unfit);
   (void)workspace;
@@ -509,8 +508,7 @@ qsa_status_t qsa_sparse_attn_prefill_paged(const qsa_attn_desc_t* desc, int32_t 
   if (!aligned(page_table, 4) || !aligned(cu_q, 4) || !aligned(q_pos0, 4) || !aligned(sel_blocks, 4) ||
       !aligned(sel_count, 4) || !aligned(lse, 4))
     return fail(QSA_ERR_MISALIGNED, "int32/fp32 arrays must be 4-byte aligned");
-  const qsa::AttnPlan p = qsa::plan_attn(total_q, (int64_t)top_k_blocks * block_size, false,
-                                         n_pages * page_size * desc->n_kv_heads * desc->head_dim * 4);
+  const qsa::AttnPlan p = qsa::plan_attn(total_q, (int64_t)top_k_blocks * block_size, false);
   const qsa::PlanCheck pc = qsa::check_attn_plan(p, desc->n_q_heads, desc->n_kv_heads, top_k_blocks, block_size);
   if (pc.unfit) return fail(QSA_ERR_UNSUPPORTED, "sparse_attn_prefill_paged: %s", pc.unfit);
   const qsa::PagedRows pg{cu_q, q_pos0, batch, page_table, max_pages, __builtin_ctz((unsigned)page_size)};

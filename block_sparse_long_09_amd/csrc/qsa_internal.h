@@ -68,11 +68,9 @@ struct AttnPlan {
   int rows;
   int splits;
   int64_t split_tokens;
-  int prefetch;  // chunks each wave keeps in flight (1 or 2)
 };
 
-// kv_bytes: bytes of the K and V the rows gather from (0 when not known).
-AttnPlan plan_attn(int batch_rows, int64_t max_tokens, bool split_kv, int64_t kv_bytes = 0);
+AttnPlan plan_attn(int batch_rows, int64_t max_tokens, bool split_kv);
 size_t attn_workspace_bytes(const AttnPlan& p, int Hq);
 PlanCheck check_attn_plan(const AttnPlan& p, int Hq, int Hkv, int top_k, int r);
 

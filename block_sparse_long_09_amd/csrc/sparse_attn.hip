@@ -18,9 +18,10 @@
 //                 in A-operand layout (token order inside the chunk is permuted
 //                 consistently for P and V), V goes HBM -> registers -> LDS and
 //                 is read back transposed, 2 bytes per lane.
-// The next chunk's K and V loads are issued before the current chunk is
-// computed. The kernel is bound by the HBM gather of K/V rows: each block of
-// r tokens is r * Hkv * D * 2 bytes contiguous in K and in V.
+// The next chunk's K and V loads are issued as soon as the current chunk's
+// K has gone through its MFMAs and its V into LDS, and are in flight during
+// its softmax and P V. The kernel is bound by the HBM gather of K/V rows:
+// each block of r tokens is r * Hkv * D * 2 bytes contiguous in K and in V.
 //
 // Decode splits the token list over many workgroups (split-KV) and a second
 // kernel merges the partial (m, l, O) per head. Dense attention is the same
@@ -37,17 +38,13 @@ constexpr int kD = 128;        // head dim
 constexpr int kChunk = 32;     // tokens per chunk
 constexpr int kVPitch = 132;   // LDS row pitch of the V tile (elements)
 constexpr int kSelLds = 1024;  // kept block ids per split staged in LDS (top_k <= 1024)
-// A second chunk in flight per wave pays once the K/V the rows gather from
-// is well beyond the 256 MiB last-level cache. Measured on MI355X (8192
-// queries, 32/4 and 16/2 heads, 128K..1M tokens): from 1 GiB of K/V on it
-// saves 2-6%, at 512 MiB it ties, below it costs up to 5% (the gathers then
-// partly hit that cache and the wait is short). Split-KV decode gained
-// nothing from two or three chunks in flight.
-constexpr int64_t kDeepPrefetchBytes = (int64_t)512 << 20;
 }  // namespace
 
-template <int HKV, int PF>
-__global__ __launch_bounds__(256) void attn_gather_kernel(
+// Two waves per SIMD: with one chunk's K and V registers (loaded into once
+// the previous chunk's are consumed) the kernel fits 256 registers, and the
+// second wave hides each wave's wait for its next chunk.
+template <int HKV>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void attn_gather_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
     const uint16_t* __restrict__ vc, int64_t kv_batch_stride, int64_t q_pos0,
     const int32_t* __restrict__ kv_len, int Hq, int G, int r, int k,
@@ -141,28 +138,26 @@ __global__ __launch_bounds__(256) void attn_gather_kernel(
     return valid ? s : t;
   };
 
-  // Chunk loader: K fragments (rows 16mt + l16) and V rows (4x + quad) into
-  // ring slot u. PF slots: the loads of the next PF chunks are in flight
-  // while a chunk is computed.
-  u32x4 Kn[PF][2][4], Vn[PF][8];
-  uint32_t vmask_n[PF];
-  auto load_chunk = [&](int64_t c, int u) {
+  // Chunk loader: K fragments (rows 16mt + l16) and V rows (4x + quad).
+  u32x4 Kn[2][4], Vn[8];
+  uint32_t vmask_n = 0;
+  auto load_chunk = [&](int64_t c) {
     bool valid;
     const int64_t s_mine = token_of(c + (lane & 31), valid);
     const uint64_t vm = ballot(valid);
-    vmask_n[u] = (uint32_t)vm;
+    vmask_n = (uint32_t)vm;
     const int s_lo = (int)s_mine;  // positions fit in 31 bits
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
       const int64_t s = __shfl(s_lo, 16 * mt + l16);
       const uint16_t* kp = kb + (s * HKV + g) * kD + 8 * quad;
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) Kn[u][mt][ks] = ld16(kp + 32 * ks);
+      for (int ks = 0; ks < 4; ++ks) Kn[mt][ks] = ld16(kp + 32 * ks);
     }
 #pragma unroll
     for (int x = 0; x < 8; ++x) {
       const int64_t s = __shfl(s_lo, 4 * x + quad);
-      Vn[u][x] = ld16(vb + (s * HKV + g) * kD + 8 * l16);
+      Vn[x] = ld16(vb + (s * HKV + g) * kD + 8 * l16);
     }
   };
 
@@ -173,42 +168,29 @@ __global__ __launch_bounds__(256) void attn_gather_kernel(
   for (int nt = 0; nt < 8; ++nt) O[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
   uint16_t* vt = vtile[wave];
 
-  const int64_t step = (int64_t)WPH * kChunk;  // this wave's chunks are step apart
-  const int64_t c0 = p_beg + (int64_t)sub * kChunk;
-#pragma unroll
-  for (int u = 0; u < PF; ++u)
-    if (c0 + u * step < p_end) load_chunk(c0 + u * step, u);
-  for (int64_t cb = c0; cb < p_end; cb += PF * step)
-#pragma unroll
-  for (int u = 0; u < PF; ++u) {
-    const int64_t c = cb + u * step;
-    if (c >= p_end) break;
-    u32x4 K[2][4], V[8];
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) K[mt][ks] = Kn[u][mt][ks];
-#pragma unroll
-    for (int x = 0; x < 8; ++x) V[x] = Vn[u][x];
-    const uint32_t vmask = vmask_n[u];
-    const int64_t cn = c + PF * step;
-    if (cn < p_end) load_chunk(cn, u);
-
+  int64_t c = p_beg + (int64_t)sub * kChunk;
+  if (c < p_end) load_chunk(c);
+  for (; c < p_end; c += (int64_t)WPH * kChunk) {
+    const uint32_t vmask = vmask_n;
     // S^T for the 32 tokens of the chunk
     f32x4 S[2];
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
       S[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) S[mt] = mfma16x16x32(K[mt][ks], Qf[ks], S[mt]);
+      for (int ks = 0; ks < 4; ++ks) S[mt] = mfma16x16x32(Kn[mt][ks], Qf[ks], S[mt]);
     }
     // stage V rows in LDS
 #pragma unroll
     for (int x = 0; x < 8; ++x) {
       uint16_t* dst = vt + (4 * x + quad) * kVPitch + 8 * l16;
-      *reinterpret_cast<uint2*>(dst) = make_uint2(V[x][0], V[x][1]);
-      *reinterpret_cast<uint2*>(dst + 4) = make_uint2(V[x][2], V[x][3]);
+      *reinterpret_cast<uint2*>(dst) = make_uint2(Vn[x][0], Vn[x][1]);
+      *reinterpret_cast<uint2*>(dst + 4) = make_uint2(Vn[x][2], Vn[x][3]);
     }
+    // this chunk's K and V are consumed: their registers take the next
+    // chunk's loads, in flight during the softmax and P V below
+    const int64_t cn = c + (int64_t)WPH * kChunk;
+    if (cn < p_end) load_chunk(cn);
     // online softmax (rows of S^T are tokens 16mt + 4quad + i, column = head l16)
     float x[8];
     float cmax = -INFINITY;
@@ -390,10 +372,9 @@ __global__ __launch_bounds__(128) void attn_merge_kernel(const float* __restrict
   if (lse && d == 0) lse[row * Hq + h] = (M + log2f(L)) * 0.69314718055994531f;
 }
 
-AttnPlan plan_attn(int batch_rows, int64_t max_tokens, bool split_kv, int64_t kv_bytes) {
+AttnPlan plan_attn(int batch_rows, int64_t max_tokens, bool split_kv) {
   AttnPlan p{};
   p.rows = batch_rows;
-  p.prefetch = !split_kv && kv_bytes > kDeepPrefetchBytes ? 2 : 1;
   int64_t splits = 1;
   if (split_kv) {
     // about 256 workgroups: enough to spread the gathers over the chip while
@@ -461,15 +442,14 @@ hipError_t launch_attn(const AttnPlan& p, const uint16_t* q, const uint16_t* k, 
     part_ml = reinterpret_cast<float2*>(reinterpret_cast<char*>(ws) + n * kD * sizeof(float));
   }
   const dim3 grid((unsigned)p.rows, (unsigned)p.splits);
-#define QSA_LAUNCH_ATTN(HKV_, PF_)                                                                   \
-  hipLaunchKernelGGL((attn_gather_kernel<HKV_, PF_>), grid, dim3(256), 0, stream, q, k, v,          \
-                     kv_batch_stride, q_pos0, kv_len, Hq, G, r, top_k, sel, sel_cnt, p.splits,      \
+#define QSA_LAUNCH_ATTN(HKV_)                                                                   \
+  hipLaunchKernelGGL(attn_gather_kernel<HKV_>, grid, dim3(256), 0, stream, q, k, v,            \
+                     kv_batch_stride, q_pos0, kv_len, Hq, G, r, top_k, sel, sel_cnt, p.splits, \
                      (int)p.split_tokens, scale_log2, out, lse, part_o, part_ml, pg)
-  const bool deep = p.prefetch == 2;
   switch (Hkv) {
-    case 1: if (deep) QSA_LAUNCH_ATTN(1, 2); else QSA_LAUNCH_ATTN(1, 1); break;
-    case 2: if (deep) QSA_LAUNCH_ATTN(2, 2); else QSA_LAUNCH_ATTN(2, 1); break;
-    case 4: if (deep) QSA_LAUNCH_ATTN(4, 2); else QSA_LAUNCH_ATTN(4, 1); break;
+    case 1: QSA_LAUNCH_ATTN(1); break;
+    case 2: QSA_LAUNCH_ATTN(2); break;
+    case 4: QSA_LAUNCH_ATTN(4); break;
     default: return hipErrorInvalidValue;
   }
 #undef QSA_LAUNCH_ATTN

@@ -99,15 +99,14 @@ def test_prefill_full_size_sampled_rows(qsa, name):
     _say(name, "rows in the tie band:", n_band, "of", len(rows))
 
 
-def test_prefill_attention_two_chunks_in_flight(qsa):
-    """K and V of 300,000 tokens (614 MB, past the 512 MiB from which each
-    wave keeps two chunks in flight): rows at the start of the context (lists
-    of 1..12 blocks, ragged against the 32-token chunks) and at its end match
-    the oracle on the oracle's selections, and rows given only the K/V prefix
-    they need (one chunk in flight) give the same bits."""
+def test_prefill_attention_large_kv_sampled_rows(qsa):
+    """K and V of 300,000 tokens (614 MB): rows at the start of the context
+    (lists of 1..12 blocks, ragged against the 32-token chunks), in the middle
+    and at the end match the oracle on the oracle's selections, and the same
+    rows given only the K/V prefix they need give the same bits."""
     Hq, Hkv, Hi, D, di, r, k, seed = 32, 4, 8, 128, 64, 4, 512, 4242
     L = 300_000
-    _say("prefill attention, two chunks in flight, L", L)
+    _say("prefill attention, large K/V, L", L)
     K = normal_to_device(seed, 2, (L, Hkv, D))
     V = normal_to_device(seed, 3, (L, Hkv, D))
     Kh = gen.normal(seed, 2, (L, Hkv, D))
