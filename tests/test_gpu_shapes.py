@@ -1,7 +1,8 @@
 """GPU parity for the shapes the C ABI accepts beyond the benchmarked ones:
 every supported query-heads-per-KV-head group size on the prefill and the
-split-KV decode attention, and the smallest budgets (k = 1: the own block
-only; k = 2: one candidate) through the whole path."""
+split-KV decode attention, the smallest budgets (k = 1: the own block only;
+k = 2: one candidate) through the whole path, and the prefill indexer on
+several sequences with their own first positions in one call."""
 import numpy as np
 import pytest
 import torch
@@ -126,3 +127,32 @@ def test_smallest_budgets_end_to_end(qsa, k):
                         lambda i: oracle.scores(iqd[b], bl[: t // r], 1.0 / Hi))
         o_out, o_lse = oracle.sparse_attn(Qd[b][None], Kc[b], Vc[b], t, r, d_sel[b:b + 1], d_cnt[b:b + 1])
         check_attention(dout[b:b + 1], dlse[b:b + 1], o_out, o_lse, f"decode k={k} seq {b}")
+
+
+@pytest.mark.parametrize("n_q", [20, 200])
+def test_index_topk_batched_prefill(qsa, n_q):
+    # three sequences, each with its own first query position (one from 0,
+    # two ragged ones), in one call: the few-query kernel at 20 rows, the
+    # many-query one at 200
+    B, Hi, r, k, seed = 3, 8, 4, 128, 960 + n_q
+    pos = [0, 3000, 1517]
+    end = max(pos) + n_q
+    N = end // r + 1
+    _say("batched prefill indexer", n_q)
+    iq = gen.normal(seed, 4, (B, n_q, Hi, 64))
+    ik = np.stack([gen.idx_keys(seed, b, N * r, 0, N * r, 64, 512, r) for b in range(B)])
+    blocks = [oracle.compress(ik[b], r) for b in range(B)]
+    cmp = torch.zeros((B, N, 64), dtype=torch.bfloat16, device="cuda")
+    qsa.qsa_compress_keys(dev(ik), cmp, r, 0, N)
+    d = qsa.index_desc(r, k, Hi)
+    sel = torch.empty((B, n_q, k), dtype=torch.int32, device="cuda")
+    cnt = torch.empty((B, n_q), dtype=torch.int32, device="cuda")
+    ws = qsa.workspace(qsa.qsa_index_topk_workspace_size(d, B, n_q, end))
+    q_pos0 = torch.tensor(pos, dtype=torch.int32, device="cuda")
+    qsa.qsa_index_topk(d, dev(iq), cmp, q_pos0, end, sel, cnt, ws)
+    torch.cuda.synchronize()
+    g_sel, g_cnt = sel.cpu().numpy(), cnt.cpu().numpy()
+    for b in range(B):
+        o_sel, o_cnt, band, _ = oracle.select(iq[b], blocks[b], pos[b], r, k, 1.0 / Hi)
+        check_selection(g_sel[b], g_cnt[b], o_sel, o_cnt, band,
+                        lambda i: oracle.scores(iq[b][i], blocks[b][: (pos[b] + i) // r], 1.0 / Hi))
