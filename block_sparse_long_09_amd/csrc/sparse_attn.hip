@@ -24,8 +24,9 @@
 // each block of r tokens is r * Hkv * D * 2 bytes contiguous in K and in V.
 //
 // Decode splits the token list over many workgroups (split-KV) and a second
-// kernel merges the partial (m, l, O) per head. Dense attention is the same
-// kernel with the token list 0..t.
+// kernel merges the partial (m, l, O) per head. Dense decode attention (the
+// comparator) is the same kernel with the token list 0..t; dense prefill has
+// its own kernel.
 #include "qsa_device.h"
 #include "qsa_internal.h"
 
