@@ -483,7 +483,7 @@ __global__ __launch_bounds__(64 * (NW + 1)) __attribute__((amdgpu_waves_per_eu(N
 void index_prefill_kernel(
     const uint16_t* __restrict__ idx_q, const uint16_t* __restrict__ cmp_k, int64_t cmp_stride,
     const int32_t* __restrict__ q_pos0, int n_q, int r, int keep, float a_scale, float w_epi,
-    int n_qgroups, int splits, int split_len, int cap, uint2* __restrict__ buf,
+    int n_qgroups, int splits, int split_len, int cap, int seed_stride, uint2* __restrict__ buf,
     int* __restrict__ buf_cnt, const int32_t* __restrict__ cu_q) {
   constexpr int QPH = 16 / HI;
   constexpr int QPT = 32 / HI;
@@ -502,6 +502,7 @@ void index_prefill_kernel(
   __shared__ uint32_t hist_all[NW][256];
   __shared__ int wg_lim[NW];
   __shared__ int wg_compact;  // tile before which every wave compacts its fuller buffers
+  __shared__ int wg_rerun;    // a seeded buffer of the workgroup ended short: scan again
   extern __shared__ unsigned long long kstage_all[];  // NW x cap entries: each wave's compaction stage
 
   const int tid = threadIdx.x;
@@ -564,12 +565,16 @@ void index_prefill_kernel(
   }
   minlim = __builtin_amdgcn_readfirstlane(minlim);  // wave-uniform after the reduction
   if (lane == 0 && !copier) wg_lim[wave] = maxlim;
-  if (tid == 0) wg_compact = -1;
+  if (tid == 0) {
+    wg_compact = -1;
+    wg_rerun = 0;
+  }
   __syncthreads();
   int wg_max = wg_lim[0];
 #pragma unroll
   for (int w = 1; w < NW; ++w) wg_max = max(wg_max, wg_lim[w]);
 
+  uint32_t frozen = 0;  // bit s: slot s's count was written before a second scan
   if (keep > 0 && wg_max > sbeg) {
     u32x4 A[AT][4];
     if (!copier) {
@@ -594,17 +599,29 @@ void index_prefill_kernel(
     }
     const unsigned char* kb = reinterpret_cast<const unsigned char*>(cmp_k + (int64_t)b * cmp_stride);
     const int ntiles = (wg_max - sbeg + TILE - 1) / TILE;
-    // Tile t goes to LDS slot t % NSLOT, written by the copy wave's eight
-    // 1 KiB global_load_lds: piece u of lane l lands at byte 1024u + 16l of the
-    // slot, i.e. row 8u + l / 8, part l % 8, and carries the row's global part
-    // (l % 8) ^ (row % 8). Rows past the workgroup's last candidate read that
-    // candidate instead, so every load is in bounds.
+    // The tiles go through the LDS ring as one stream of "virtual" tiles in up
+    // to three phases, each padded to whole barrier groups: [0, P1) the
+    // sample (split tiles 0, rho, 2 rho, ...) that seeds the thresholds,
+    // [P1, P1 + P2) the scan of every tile, [P1 + P2, P1 + 2 P2) a second scan,
+    // run only when a seeded buffer ended short. Without seeding P1 = 0.
+    const int rho = seed_stride;
+    const int n1 = rho > 0 ? (ntiles + rho - 1) / rho : 0;
+    const int P1 = (n1 + TT - 1) / TT * TT;
+    const int P2 = (ntiles + TT - 1) / TT * TT;
+    auto real_tile = [&](int v) { return v < P1 ? v * rho : (v < P1 + P2 ? v - P1 : v - P1 - P2); };
+    // Virtual tile v goes to LDS slot v % NSLOT, written by the copy wave's
+    // eight 1 KiB global_load_lds: piece u of lane l lands at byte 1024u + 16l
+    // of the slot, i.e. row 8u + l / 8, part l % 8, and carries the row's
+    // global part (l % 8) ^ (row % 8). Rows past the workgroup's last candidate
+    // (also those of the padding tiles) read that candidate instead, so every
+    // load is in bounds.
     auto issue_tile = [&](int t) __attribute__((always_inline)) {
       unsigned char* dst = ring + (t % NSLOT) * TILE_BYTES;
       const int part = (lane & 7) ^ (lane >> 3);
+      const int first = sbeg + real_tile(t) * TILE;
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        const int row = min(sbeg + t * TILE + 8 * u + (lane >> 3), wg_max - 1);
+        const int row = min(first + 8 * u + (lane >> 3), wg_max - 1);
         __builtin_amdgcn_global_load_lds((glb_void_t*)(kb + (int64_t)row * 128 + part * 16),
                                          (lds_void_t*)(dst + 1024 * u), 16, 0, 0);
       }
@@ -719,6 +736,28 @@ void index_prefill_kernel(
       }
       return true;
     };
+    // Sample phase: each lane keeps, per slot, the four largest scores of the
+    // sampled candidates it scored (descending; -1 while empty). Appends nothing.
+    float top[NS][4];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) top[s][0] = top[s][1] = top[s][2] = top[s][3] = -1.0f;
+    auto seed_epi = [&](const f32x16* acc, int c, bool live) __attribute__((always_inline)) {
+      const int j = c + col;
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        const int a = s / QPH, qq = s % QPH;
+        float sum = relu_bits(acc[a][qq * HI]);
+#pragma unroll
+        for (int hd = 1; hd < HI; ++hd) sum += relu_bits(acc[a][qq * HI + hd]);
+        float y = (live && j < lim[s]) ? (SCALE_EPI ? sum * w_epi : sum) : -1.0f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float hi = fmaxf(top[s][i], y);
+          y = fminf(top[s][i], y);
+          top[s][i] = hi;
+        }
+      }
+    };
     // One barrier group: TT tiles, 2 TT subtiles (fewer at the end). A
     // compaction one wave asked for while processing the previous group is
     // done by every wave at once, each compacting its buffers past a lower
@@ -727,7 +766,9 @@ void index_prefill_kernel(
     // asked compacts for certain (another may already have moved the flag
     // on); for the others the invitation is optional. The pending subtile is
     // scored first, so the buffers hold every candidate before the next one.
-    auto process_group = [&](int t) __attribute__((always_inline)) {
+    // t: the group's first virtual tile; t0: the first of its scan (split
+    // tile 0); left: tiles of the scan from t on (at least one).
+    auto process_group = [&](int t, int t0, int left) __attribute__((always_inline)) {
       if (pending || wg_compact == t) {
         if (pendB) epilogue(accB, cB, true);
         pendB = false;
@@ -736,13 +777,13 @@ void index_prefill_kernel(
         compact_over(max(max(cap - 12 * TILE, cap / 2), keep));
         pending = false;
       }
-      const int nsub = 2 * min(TT, ntiles - t);
+      const int nsub = 2 * min(TT, left);
       bool appended = false;
 #pragma unroll
       for (int u = 0; u < 2 * TT; ++u) {
         if (u < nsub) {
           const int tt = t + (u >> 1);
-          const int c = sbeg + tt * TILE + (u & 1) * 32;
+          const int c = sbeg + (tt - t0) * TILE + (u & 1) * 32;
           if ((u & 1) == 0) {
             mfma_sub(tt % NSLOT, 0, accA);
             cA = c;
@@ -770,6 +811,28 @@ void index_prefill_kernel(
         }
       }
     };
+    // A group of the sample phase: the same pipeline, the sample epilogue.
+    auto seed_group = [&](int t, int left) __attribute__((always_inline)) {
+      const int nsub = 2 * min(TT, left);
+#pragma unroll
+      for (int u = 0; u < 2 * TT; ++u) {
+        if (u < nsub) {
+          const int tt = t + (u >> 1);
+          const int c = sbeg + tt * rho * TILE + (u & 1) * 32;
+          if ((u & 1) == 0) {
+            mfma_sub(tt % NSLOT, 0, accA);
+            cA = c;
+            seed_epi(accB, cB, pendB);
+            pendB = false;
+          } else {
+            mfma_sub(tt % NSLOT, 1, accB);
+            cB = c;
+            seed_epi(accA, cA, true);
+            pendB = true;
+          }
+        }
+      }
+    };
     // Iteration t opens with barrier B_t, after which the compute waves process
     // tile t. The copy wave issues tile t + PF right after B_t, into the slot
     // of tile t + PF - NSLOT <= t - 1 (processed before B_t), and before B_t
@@ -780,39 +843,121 @@ void index_prefill_kernel(
     // With two tiles per barrier (TT = 2) the copy wave issues tiles t + 2 and
     // t + 3 right after B_t, into the slots of tiles t - 2 and t - 1 (processed
     // before B_t), and waits for both before the next barrier.
+    // t runs over the virtual tiles of the sample and the scan; after the
+    // scan, when seeded, one more barrier (R) tells every wave whether the
+    // second scan runs; the tiles the copy wave issued last are already its
+    // first ones. Both sides pass the same barriers in the same order.
     if (copier) {
-      if constexpr (TT == 1) {
+      auto copy_run = [&](int t0, int t1) __attribute__((always_inline)) {
+        if constexpr (TT == 1) {
+          for (int t = t0; t < t1; ++t) {
+            __builtin_amdgcn_s_waitcnt(prefill_vmcnt(8 * (PF - 1)));
+            __builtin_amdgcn_s_barrier();
+            issue_tile(t + PF);
+          }
+        } else {
+          for (int t = t0; t < t1; t += 2) {
+            __builtin_amdgcn_s_waitcnt(prefill_vmcnt(0));
+            __builtin_amdgcn_s_barrier();
+            issue_tile(t + 2);
+            issue_tile(t + 3);
+          }
+        }
+      };
 #pragma unroll
-        for (int t = 0; t < PF; ++t) issue_tile(t);
-        for (int t = 0; t < ntiles; ++t) {
-          __builtin_amdgcn_s_waitcnt(prefill_vmcnt(8 * (PF - 1)));
-          __builtin_amdgcn_s_barrier();
-          issue_tile(t + PF);
-        }
-      } else {
-        issue_tile(0);
-        issue_tile(1);
-        for (int t = 0; t < ntiles; t += 2) {
-          __builtin_amdgcn_s_waitcnt(prefill_vmcnt(0));
-          __builtin_amdgcn_s_barrier();
-          issue_tile(t + 2);
-          issue_tile(t + 3);
-        }
+      for (int t = 0; t < (TT == 1 ? PF : 2); ++t) issue_tile(t);
+      copy_run(0, P1 + P2);
+      if (P1 > 0) {
+        __builtin_amdgcn_s_waitcnt(prefill_vmcnt(0));
+        __syncthreads();  // R
+        if (wg_rerun) copy_run(P1 + P2, P1 + 2 * P2);
       }
       __builtin_amdgcn_s_waitcnt(prefill_vmcnt(0));  // no copy into LDS outlives the workgroup
     } else {
-      for (int t = 0; t < ntiles; t += TT) {
+      for (int t = 0; t < n1; t += TT) {  // as far as P1
         __syncthreads();
-        process_group(t);
+        seed_group(t, n1 - t);
       }
-      if (pendB) epilogue(accB, cB, true);
+      uint32_t seeded = 0;  // bit s: slot s starts from a seeded threshold
+      if (P1 > 0) {
+        if (pendB) seed_epi(accB, cB, true);
+        pendB = false;
+        // Seed: with n candidates of this split, S of them sampled, take the
+        // m-th largest sampled score, m = ceil(2.5 keep S / n), as a lower
+        // estimate of the split's keep-th largest (about 2.5 keep candidates
+        // reach it). The m-th largest of the lane-half's 128 kept scores is
+        // at most the sample's m-th largest. The buffer takes every candidate
+        // at or above it (threshold one float step below). Only for splits of
+        // at least 4 keep candidates; m <= 96 of the 128.
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+          const int n = max(lim[s] - sbeg, 0);
+          const int per = TILE * rho;
+          const int S = (n / per) * TILE + min(n % per, TILE);
+          const int m = (int)(((int64_t)5 * keep * S + 2 * (int64_t)n - 1) / (2 * (int64_t)max(n, 1)));
+          // largest key x with at least m of the lane-half's kept scores >= x
+          uint32_t x = 0;
+          for (int bit = 30; bit >= 0; --bit) {
+            const uint32_t tr = x | (1u << bit);
+            int c = 0;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const uint64_t bm = ballot(__float_as_int(top[s][i]) >= (int)tr);
+              c += __popc(half ? (uint32_t)(bm >> 32) : (uint32_t)bm);
+            }
+            if (c >= m) x = tr;
+          }
+          if (n >= 4 * keep && m <= 96) {
+            tau[s] = x > 0 ? __uint_as_float(x - 1) : -1.0f;
+            seeded |= 1u << s;
+          }
+        }
+      }
+      // the scan, and once more if a seeded buffer ended short
+      for (int t0 = P1;; t0 += P2) {
+        for (int t = t0; t < t0 + ntiles; t += TT) {  // as far as t0 + P2
+          __syncthreads();
+          process_group(t, t0, t0 + ntiles - t);
+        }
+        if (pendB) epilogue(accB, cB, true);
+        if (P1 == 0 || t0 > P1) break;
+        // A seeded buffer holds every candidate at or above its seed until
+        // it first compacts (then at least keep entries). One that ended
+        // with fewer than keep entries may have missed some of the split's
+        // best: its split is scanned again from an unseeded threshold.
+        uint32_t short_m = 0;
+#pragma unroll
+        for (int s = 0; s < NS; ++s)
+          if (((seeded >> s) & 1u) && cnt[s] < keep) short_m |= 1u << s;
+        if (ballot(short_m != 0) && lane == 0) wg_rerun = 1;
+        __syncthreads();  // R
+        if (!wg_rerun) break;
+        // the other buffers are final: their counts are written now, and
+        // they take nothing more
+        frozen = ~short_m & ((1u << NS) - 1u);
+        if (wave_live && col == 0) {
+#pragma unroll
+          for (int s = 0; s < NS; ++s) {
+            const int qi = slot_query(s, half);
+            if (qi < nqb && ((frozen >> s) & 1u)) buf_cnt[((int64_t)b * n_q + qi) * splits + split] = cnt[s];
+          }
+        }
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+          tau[s] = ((short_m >> s) & 1u) ? -1.0f : INFINITY;
+          cnt[s] = 0;
+        }
+        pending = false;
+        pendB = false;
+        if (tid == 0) wg_compact = -1;  // read after the next barrier
+      }
     }
   }
   if (wave_live && col == 0) {
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
       const int qi = slot_query(s, half);
-      if (qi < nqb) buf_cnt[((int64_t)b * n_q + qi) * splits + split] = cnt[s];
+      if (qi < nqb && !((frozen >> s) & 1u)) buf_cnt[((int64_t)b * n_q + qi) * splits + split] = cnt[s];
     }
   }
 }
@@ -1236,6 +1381,17 @@ IndexPlan plan_index(int hi, int k, int batch, int n_q, int64_t max_q_end, int r
   if ((int64_t)split_len + 64 <= cap) cap = (int)split_len + 64;
   cap = (cap + 127) / 128 * 128;
   p.cap = cap;
+  // Seeded thresholds in the many-query kernel: every rho-th tile of a split
+  // is scored first, rho the smallest power of two with 2.5 keep / rho <= 96
+  // (the seed is the m-th largest of at most 128 kept sample scores per
+  // query, m about 2.5 keep / rho); only where rho >= 16, so that the sample
+  // adds at most 1/16 to the scoring.
+  p.seed_stride = 0;
+  if (p.wide) {
+    int rho = 1;
+    while (5 * keep > 192 * rho) rho *= 2;
+    if (rho >= 16) p.seed_stride = rho;
+  }
   p.buf_bytes = (size_t)batch * n_q * p.splits * (size_t)cap * sizeof(uint2);
   p.cnt_bytes = (size_t)batch * n_q * p.splits * sizeof(int);
   p.workspace = p.buf_bytes + ((p.cnt_bytes + 255) / 256 * 256);
@@ -1255,7 +1411,7 @@ constexpr size_t kMaxLds = 160 * 1024;
 // alignment slack).
 constexpr size_t kLdsSlack = 64;
 constexpr size_t prefill_static_lds(int nw) {
-  return (size_t)(nw == 3 ? 3 : 4) * 64 * 128 + (size_t)nw * (256 * 4 + 4) + 4 + kLdsSlack;
+  return (size_t)(nw == 3 ? 3 : 4) * 64 * 128 + (size_t)nw * (256 * 4 + 4) + 8 + kLdsSlack;
 }
 constexpr size_t kStreamStaticLds = 4 * 256 * 4 + kLdsSlack;
 constexpr size_t kSelectStaticLds = (256 + 10 + kSelScratch + 9) * 4 + kLdsSlack;
@@ -1305,7 +1461,8 @@ PlanCheck check_index_plan(const IndexPlan& p, int batch, int n_q) {
   }
   c.l[1] = LaunchShape{{grid_dim((int64_t)batch * n_q), 1, 1}, 256u, kSelectStaticLds + p.select_lds};
   c.max_i32 = std::max<int64_t>({(int64_t)n_q + p.qw, (int64_t)p.n_qgroups * p.splits,
-                                 p.max_cand + p.split_len, (int64_t)p.splits * p.cap});
+                                 p.max_cand + p.split_len + 64 * ((int64_t)p.seed_stride + 2),
+                                 (int64_t)p.splits * p.cap});
   c.max_offset = (int64_t)batch * n_q * p.splits * (int64_t)p.cap;
   return finish_check(c);
 }
@@ -1351,7 +1508,7 @@ hipError_t launch_index_topk(const IndexPlan& p, const uint16_t* idx_q, const ui
                                   : index_prefill_kernel<HI_, AT_, true, NW_>), g1, dim3(64 * (NW_ + 1)), p.stream_lds, \
                      stream, idx_q, cmp_k,                                                         \
                      cmp_stride, q_pos0, n_q, r, k - 1, a_scale, w_epi, p.n_qgroups, p.splits,     \
-                     p.split_len, p.cap, buf, cnt, cu_q)
+                     p.split_len, p.cap, p.seed_stride, buf, cnt, cu_q)
     switch (p.hi) {
       case 1: QSA_LAUNCH_PREFILL(1, 1, 8); break;
       case 2: QSA_LAUNCH_PREFILL(2, 1, 8); break;

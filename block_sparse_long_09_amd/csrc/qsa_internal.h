@@ -43,6 +43,7 @@ struct IndexPlan {
   int splits;      // candidate splits
   int split_len;   // candidates per split (multiple of 32)
   int cap;         // buffer entries per (query, split)
+  int seed_stride; // wide kernel: sample every seed_stride-th tile to seed the thresholds (0: off)
   int64_t max_cand;
   int64_t score_stride;             // decode: floats per sequence in the score array
   int list_min, list_cap;           // decode: entries per split list (at least / room)

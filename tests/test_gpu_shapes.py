@@ -156,3 +156,40 @@ def test_index_topk_batched_prefill(qsa, n_q):
         o_sel, o_cnt, band, _ = oracle.select(iq[b], blocks[b], pos[b], r, k, 1.0 / Hi)
         check_selection(g_sel[b], g_cnt[b], o_sel, o_cnt, band,
                         lambda i: oracle.scores(iq[b][i], blocks[b][: (pos[b] + i) // r], 1.0 / Hi))
+
+
+def test_index_topk_seeded_buffers_that_end_short(qsa):
+    # At a budget of 512 blocks the many-query indexer first scores every
+    # 16th 64-block tile of its candidate split and seeds each query's
+    # threshold from that sample. Here the keys of exactly those tiles (one
+    # split: it starts at block 0) are scaled by 8, so each seed lands among
+    # their scores and fewer than k - 1 candidates reach it: such a buffer ends
+    # short and its split is scanned again from an unseeded threshold. Three
+    # of every eight consecutive queries (one wave's share) have zero indexer
+    # vectors (all scores 0, every candidate tied): their buffers fill, so
+    # they keep their first scan while their neighbours rescan.
+    B, n_q, Hi, r, k, seed = 4, 4096, 8, 4, 512, 977
+    pos0 = 40000
+    end = pos0 + n_q
+    N = end // r + 1
+    _say("seeded buffers that end short")
+    blocks = gen.normal(seed, 5, (B, N, 64))
+    x = gen.bf16_to_f64(blocks)
+    x[:, (np.arange(N) // 64) % 16 == 0] *= 8.0
+    blocks = gen.f32_to_bf16(x.astype(np.float32))
+    iq = gen.normal(seed, 4, (B, n_q, Hi, 64))
+    iq[:, (np.arange(n_q) % 8) < 3] = 0
+    d = qsa.index_desc(r, k, Hi)
+    sel = torch.empty((B, n_q, k), dtype=torch.int32, device="cuda")
+    cnt = torch.empty((B, n_q), dtype=torch.int32, device="cuda")
+    ws = qsa.workspace(qsa.qsa_index_topk_workspace_size(d, B, n_q, end))
+    q_pos0 = torch.full((B,), pos0, dtype=torch.int32, device="cuda")
+    qsa.qsa_index_topk(d, dev(iq), dev(blocks), q_pos0, end, sel, cnt, ws)
+    torch.cuda.synchronize()
+    g_sel, g_cnt = sel.cpu().numpy(), cnt.cpu().numpy()
+    rows = [0, 1, 2, 3, 7, 8, 100, 1001, 2047, 2050, 4093, 4094, 4095]
+    for b in range(B):
+        for qi in rows:
+            o_sel, o_cnt, band, _ = oracle.select(iq[b, qi:qi + 1], blocks[b], pos0 + qi, r, k, 1.0 / Hi)
+            check_selection(g_sel[b, qi:qi + 1], g_cnt[b, qi:qi + 1], o_sel, o_cnt, band,
+                            lambda i: oracle.scores(iq[b, qi], blocks[b][: (pos0 + qi) // r], 1.0 / Hi))
