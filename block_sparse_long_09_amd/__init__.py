@@ -42,7 +42,8 @@ class GdnDesc(ctypes.Structure):
 class PlanInfo(ctypes.Structure):
     _fields_ = [("n_launches", _i32), ("grid", (ctypes.c_uint32 * 3) * 3), ("block", ctypes.c_uint32 * 3),
                 ("lds", ctypes.c_uint64 * 3), ("max_int32_value", _i64), ("max_offset", _i64),
-                ("workspace_bytes", ctypes.c_uint64), ("splits", _i32), ("cap", _i32), ("fits", _i32)]
+                ("workspace_bytes", ctypes.c_uint64), ("splits", _i32), ("cap", _i32), ("fits", _i32),
+                ("sample_stride", _i32)]
 
 
 _PI, _PA, _PG = ctypes.POINTER(IndexDesc), ctypes.POINTER(AttnDesc), ctypes.POINTER(GdnDesc)

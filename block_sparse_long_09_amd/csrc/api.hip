@@ -262,7 +262,8 @@ qsa_status_t qsa_sparse_attn_decode(const qsa_attn_desc_t* desc, int32_t block_s
 
 /* ---------------------------------------------------------- diagnostics --- */
 
-static void fill_info(const qsa::PlanCheck& c, size_t ws, int splits, int cap, qsa_plan_info_t* info) {
+static void fill_info(const qsa::PlanCheck& c, size_t ws, int splits, int cap, int sample_stride,
+                      qsa_plan_info_t* info) {
   *info = qsa_plan_info_t{};
   info->n_launches = c.n;
   for (int i = 0; i < c.n && i < 3; ++i) {
@@ -276,6 +277,7 @@ static void fill_info(const qsa::PlanCheck& c, size_t ws, int splits, int cap, q
   info->splits = splits;
   info->cap = cap;
   info->fits = c.unfit ? 0 : 1;
+  info->sample_stride = sample_stride;
 }
 
 qsa_status_t qsa_index_topk_plan_info(const qsa_index_desc_t* desc, int32_t batch, int32_t n_q, int64_t max_q_end,
@@ -288,7 +290,7 @@ qsa_status_t qsa_index_topk_plan_info(const qsa_index_desc_t* desc, int32_t batc
   const qsa::IndexPlan p = qsa::plan_index(desc->n_idx_heads, desc->top_k_blocks, batch, n_q, max_q_end,
                                            desc->block_size, packed == 0);
   const qsa::PlanCheck c = qsa::check_index_plan(p, batch, n_q);
-  fill_info(c, p.workspace, p.splits, p.decode ? p.list_cap : p.cap, info);
+  fill_info(c, p.workspace, p.splits, p.decode ? p.list_cap : p.cap, p.decode ? 0 : p.seed_stride, info);
   return ok();
 }
 
@@ -300,7 +302,7 @@ qsa_status_t qsa_sparse_attn_plan_info(const qsa_attn_desc_t* desc, int32_t rows
   if (rows < 1) return fail(QSA_ERR_INVALID_ARGUMENT, "rows must be >= 1");
   const qsa::AttnPlan p = qsa::plan_attn(rows, (int64_t)top_k_blocks * block_size, decode != 0);
   const qsa::PlanCheck c = qsa::check_attn_plan(p, desc->n_q_heads, desc->n_kv_heads, top_k_blocks, block_size);
-  fill_info(c, qsa::attn_workspace_bytes(p, desc->n_q_heads), p.splits, (int)p.split_tokens, info);
+  fill_info(c, qsa::attn_workspace_bytes(p, desc->n_q_heads), p.splits, (int)p.split_tokens, 0, info);
   return ok();
 }
 

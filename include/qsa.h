@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define QSA_ABI_VERSION 1
+#define QSA_ABI_VERSION 2
 
 typedef enum {
   QSA_OK = 0,

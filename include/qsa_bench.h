@@ -54,6 +54,9 @@ typedef struct {
   int32_t splits;           /* indexer: candidate splits; attention: token-list splits */
   int32_t cap;              /* indexer: buffer / list entries per split; attention: tokens per split */
   int32_t fits;             /* 1 when every limit above holds */
+  int32_t sample_stride;    /* indexer: the many-query kernel first scores every sample_stride-th
+                               64-block tile of a split to seed its thresholds (0: no sample);
+                               added in ABI version 2 */
 } qsa_plan_info_t;
 
 /* Plan of qsa_index_topk (packed = 0) or qsa_index_topk_varlen (packed = 1,

@@ -30,7 +30,7 @@ def test_exports_every_declared_symbol(qsa):
     lib = ctypes.CDLL(qsa.LIB_PATH)
     for name in declared:
         assert hasattr(lib, name), name
-    assert qsa.abi_version() == 1
+    assert qsa.abi_version() == 2
 
 
 def _status(qsa, code):

@@ -98,3 +98,20 @@ def test_plans_refuse_what_does_not_fit(qsa):
     if info.fits == 0:
         assert info.max_int32_value >= 2 ** 31 or any(
             info.grid[i][0] > MAX_GRID_X or info.lds[i] > MAX_LDS for i in range(info.n_launches))
+
+
+@pytest.mark.parametrize("k,expect", [(512, 16), (1024, 32), (309, 16), (308, 0), (256, 0), (64, 0)])
+def test_index_plan_threshold_sample_stride(qsa, k, expect):
+    # the many-query indexer seeds its thresholds from every rho-th key tile:
+    # rho is the smallest power of two with 2.5 (k - 1) / rho <= 96 sample
+    # scores to rank, and the sample is taken only when rho >= 16 (at most
+    # 1/16 more scoring); so the seed's rank m = 2.5 (k - 1) / rho lies in
+    # (48, 96] whenever it is used
+    d = qsa.index_desc(4, k, 8, 64)
+    info = qsa.qsa_index_topk_plan_info(d, 1, 16384, 1 << 20)
+    assert info.sample_stride == expect
+    if expect:
+        assert 5 * (k - 1) <= 192 * expect and 5 * (k - 1) > 96 * expect
+    # decode (one query per sequence) and the few-query kernel take no sample
+    assert qsa.qsa_index_topk_plan_info(d, 4, 1, 1 << 20).sample_stride == 0
+    assert qsa.qsa_index_topk_plan_info(d, 1, 32, 1 << 20).sample_stride == 0
