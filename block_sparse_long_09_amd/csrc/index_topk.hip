@@ -26,7 +26,8 @@
 //   top-(k-1). Each split ends compacted to at most k-1 entries.
 // Prefill, many queries (n_q >= 64): index_prefill_kernel, the same scoring
 //   and buffers with workgroups of compute waves that share LDS tiles of block
-//   keys filled by a copy wave, and approximate compactions (see there).
+//   keys filled by a copy wave, approximate compactions, and thresholds seeded
+//   from a strided sample of the split, checked after the scan (see there).
 // Both end in index_select_kernel: one workgroup per query merges the split
 //   buffers (already in block order) in LDS, selects exactly and writes the
 //   output.
@@ -473,9 +474,11 @@ __global__ __launch_bounds__(256) void index_stream_kernel(
 // for before a tile is in place, as they would be if the compute waves loaded
 // the tiles (the memory counter is in order and counts stores too).
 // Per query: running threshold and a (score, block) buffer as in
-// index_stream_kernel; a wave compacts its own buffers (keys staged in its LDS
-// area) when one nears capacity. Splits end with at most `cap` entries; the
-// select kernel takes them as they are.
+// index_stream_kernel, the threshold starting from a seed taken from a sample
+// of the split's tiles when seed_stride > 0 (a split whose seeded buffer ends
+// short is scanned again unseeded); a wave compacts its own buffers (keys
+// staged in its LDS area) when one nears capacity. Splits end with at most
+// `cap` entries; the select kernel takes them as they are.
 constexpr int kPrefillDepth = 2;      // tiles the copy wave keeps in flight
 constexpr int prefill_vmcnt(int n) { return vmcnt_imm(n); }
 template <int HI, int AT, bool SCALE_EPI, int NW>
