@@ -193,3 +193,47 @@ def test_index_topk_seeded_buffers_that_end_short(qsa):
             o_sel, o_cnt, band, _ = oracle.select(iq[b, qi:qi + 1], blocks[b], pos0 + qi, r, k, 1.0 / Hi)
             check_selection(g_sel[b, qi:qi + 1], g_cnt[b, qi:qi + 1], o_sel, o_cnt, band,
                             lambda i: oracle.scores(iq[b, qi], blocks[b][: (pos0 + qi) // r], 1.0 / Hi))
+
+
+def test_index_topk_varlen_seeded_buffers_that_end_short(qsa):
+    # The same forced rescan on the packed-batch indexer (three 4-wave
+    # workgroups per CU, one tile per barrier): the keys of the sampled tiles
+    # of every candidate split (every 16th 64-block tile from the split's
+    # start; the split length follows from the plan's split count) are scaled
+    # by 8. Three sequences with their own cached prefixes; three of every
+    # eight rows have zero indexer vectors.
+    B, Hi, r, k, seed = 3, 8, 4, 512, 981
+    pos0 = [150000, 140000, 160000]
+    n = [200, 64, 150]
+    max_q, end = max(n), max(p + m for p, m in zip(pos0, n))
+    N = end // r + 1
+    _say("varlen seeded buffers that end short")
+    d = qsa.index_desc(r, k, Hi)
+    info = qsa.qsa_index_topk_plan_info(d, B, max_q, end, packed=True)
+    assert info.sample_stride == 16
+    max_cand = (end - 1) // r
+    split_len = ((max_cand + info.splits - 1) // info.splits + 63) // 64 * 64
+    blk = np.arange(N)
+    sampled = ((blk % split_len) // 64) % 16 == 0
+    blocks = gen.normal(seed, 5, (B, N, 64))
+    x = gen.bf16_to_f64(blocks)
+    x[:, sampled] *= 8.0
+    blocks = gen.f32_to_bf16(x.astype(np.float32))
+    iqs = [gen.normal(seed + b, 4, (n[b], Hi, 64)) for b in range(B)]
+    for b in range(B):
+        iqs[b][(np.arange(n[b]) % 8) < 3] = 0
+    cu = np.concatenate([[0], np.cumsum(n)]).astype(np.int32)
+    total = int(cu[-1])
+    sel = torch.empty((total, k), dtype=torch.int32, device="cuda")
+    cnt = torch.empty((total,), dtype=torch.int32, device="cuda")
+    ws = qsa.workspace(qsa.qsa_index_topk_varlen_workspace_size(d, B, max_q, end))
+    qsa.qsa_index_topk_varlen(d, dev(np.concatenate(iqs)), dev(blocks), torch.from_numpy(cu).cuda(),
+                              torch.tensor(pos0, dtype=torch.int32, device="cuda"), max_q, end, sel, cnt, ws)
+    torch.cuda.synchronize()
+    g_sel, g_cnt = sel.cpu().numpy(), cnt.cpu().numpy()
+    for b in range(B):
+        for qi in sorted({0, 1, 2, 3, 5, n[b] // 2, n[b] - 1}):
+            row = int(cu[b]) + qi
+            o_sel, o_cnt, band, _ = oracle.select(iqs[b][qi:qi + 1], blocks[b], pos0[b] + qi, r, k, 1.0 / Hi)
+            check_selection(g_sel[row:row + 1], g_cnt[row:row + 1], o_sel, o_cnt, band,
+                            lambda i: oracle.scores(iqs[b][qi], blocks[b][: (pos0[b] + qi) // r], 1.0 / Hi))
