@@ -25,6 +25,28 @@ def _say(*a):
     print("[case]", *a, flush=True)
 
 
+def _seed_ends_short(scores, keep, rho=16):
+    """Whether the many-query indexer's seed for one (query, split) lies above
+    the split's keep-th best score, so that its buffer ends short and the split
+    is scanned again. scores: the split's candidates' scores in block order.
+    Follows the kernel's sampling: 64-block tiles 0, rho, 2 rho, ... of the
+    split; lane c of a 32-candidate subtile keeps the four best sampled
+    scores of candidates c, c + 32, ...; the seed is the m-th best of those
+    128, m = ceil(2.5 keep S / n). None when the split is not seeded."""
+    n = len(scores)
+    j = np.arange(n)
+    sampled = (j // 64) % rho == 0
+    S = int(sampled.sum())
+    m = -(-(5 * keep * S) // (2 * n))
+    if n < 4 * keep or m > 96:
+        return None
+    kept = []
+    for c in range(32):
+        kept.extend(np.sort(scores[sampled & (j % 32 == c)])[::-1][:4])
+    seed = np.sort(np.asarray(kept))[::-1][m - 1]
+    return int((scores >= seed).sum()) < keep
+
+
 @pytest.mark.parametrize("Hq,Hkv", [(4, 4), (8, 4), (8, 2), (16, 1), (64, 4), (12, 4)])
 def test_attention_head_groups(qsa, Hq, Hkv):
     # prefill rows at the start and at the end of a 1500-token context, then
@@ -188,6 +210,11 @@ def test_index_topk_seeded_buffers_that_end_short(qsa):
     torch.cuda.synchronize()
     g_sel, g_cnt = sel.cpu().numpy(), cnt.cpu().numpy()
     rows = [0, 1, 2, 3, 7, 8, 100, 1001, 2047, 2050, 4093, 4094, 4095]
+    # the pattern does force the rescan: queries with nonzero vectors are
+    # seeded above their split's (k - 1)-th score (one split from block 0)
+    for qi in (3, 7, 1003, 4095):
+        sc = oracle.scores(iq[0, qi], blocks[0][: (pos0 + qi) // r], 1.0 / Hi)
+        assert _seed_ends_short(sc, k - 1) is True, qi
     for b in range(B):
         for qi in rows:
             o_sel, o_cnt, band, _ = oracle.select(iq[b, qi:qi + 1], blocks[b], pos0 + qi, r, k, 1.0 / Hi)
@@ -231,6 +258,13 @@ def test_index_topk_varlen_seeded_buffers_that_end_short(qsa):
                               torch.tensor(pos0, dtype=torch.int32, device="cuda"), max_q, end, sel, cnt, ws)
     torch.cuda.synchronize()
     g_sel, g_cnt = sel.cpu().numpy(), cnt.cpu().numpy()
+    # the pattern does force the rescan: in every seeded split of a query
+    # with a nonzero vector the seed lies above the split's (k - 1)-th score
+    for b in range(B):
+        qi = n[b] - 1
+        sc = oracle.scores(iqs[b][qi], blocks[b][: (pos0[b] + qi) // r], 1.0 / Hi)
+        short = [_seed_ends_short(sc[s0:s0 + split_len], k - 1) for s0 in range(0, len(sc), split_len)]
+        assert True in short and False not in short, (b, short)
     for b in range(B):
         for qi in sorted({0, 1, 2, 3, 5, n[b] // 2, n[b] - 1}):
             row = int(cu[b]) + qi
