@@ -271,3 +271,31 @@ def test_index_topk_varlen_seeded_buffers_that_end_short(qsa):
             o_sel, o_cnt, band, _ = oracle.select(iqs[b][qi:qi + 1], blocks[b], pos0[b] + qi, r, k, 1.0 / Hi)
             check_selection(g_sel[row:row + 1], g_cnt[row:row + 1], o_sel, o_cnt, band,
                             lambda i: oracle.scores(iqs[b][qi], blocks[b][: (pos0[b] + qi) // r], 1.0 / Hi))
+
+
+@pytest.mark.parametrize("Hi,n_q", [(8, 256), (4, 256), (8, 20)])
+def test_index_topk_non_power_of_two_weight(qsa, Hi, n_q):
+    # a head weight that is not a power of two is applied in the epilogue
+    # (sum * w) instead of being folded into the bf16 queries: the many-query
+    # kernel, seeded (each query has ~5000 candidates), and the few-query one
+    B, r, k, w, seed = 1, 4, 512, 0.3, 990 + Hi + n_q
+    pos = 20000
+    end = pos + n_q
+    N = end // r + 1
+    _say("head weight", w, "Hi", Hi, "n_q", n_q)
+    iq = gen.normal(seed, 4, (B, n_q, Hi, 64))
+    ik = gen.idx_keys(seed, 0, N * r, 0, N * r, 64, 512, r)
+    blocks = oracle.compress(ik, r)
+    cmp = torch.zeros((B, N, 64), dtype=torch.bfloat16, device="cuda")
+    qsa.qsa_compress_keys(dev(ik[None]), cmp, r, 0, N)
+    d = qsa.index_desc(r, k, Hi, idx_head_weight=w)
+    if n_q >= 64:
+        assert qsa.qsa_index_topk_plan_info(d, B, n_q, end).sample_stride == 16
+    sel = torch.empty((B, n_q, k), dtype=torch.int32, device="cuda")
+    cnt = torch.empty((B, n_q), dtype=torch.int32, device="cuda")
+    ws = qsa.workspace(qsa.qsa_index_topk_workspace_size(d, B, n_q, end))
+    qsa.qsa_index_topk(d, dev(iq), cmp, torch.tensor([pos], dtype=torch.int32, device="cuda"), end, sel, cnt, ws)
+    torch.cuda.synchronize()
+    g_sel, g_cnt = sel.cpu().numpy()[0], cnt.cpu().numpy()[0]
+    o_sel, o_cnt, band, _ = oracle.select(iq[0], blocks, pos, r, k, w)
+    check_selection(g_sel, g_cnt, o_sel, o_cnt, band, lambda i: oracle.scores(iq[0][i], blocks[: (pos + i) // r], w))
