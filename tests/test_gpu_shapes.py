@@ -273,12 +273,15 @@ def test_index_topk_varlen_seeded_buffers_that_end_short(qsa):
                             lambda i: oracle.scores(iqs[b][qi], blocks[b][: (pos0[b] + qi) // r], 1.0 / Hi))
 
 
-@pytest.mark.parametrize("Hi,n_q", [(8, 256), (4, 256), (8, 20)])
-def test_index_topk_non_power_of_two_weight(qsa, Hi, n_q):
-    # a head weight that is not a power of two is applied in the epilogue
-    # (sum * w) instead of being folded into the bf16 queries: the many-query
-    # kernel, seeded (each query has ~5000 candidates), and the few-query one
-    B, r, k, w, seed = 1, 4, 512, 0.3, 990 + Hi + n_q
+@pytest.mark.parametrize("Hi,n_q,w", [(8, 256, 0.3), (4, 256, 0.3), (8, 20, 0.3),
+                                      (1, 256, None), (2, 256, None), (16, 256, None)])
+def test_index_topk_seeded_head_counts_and_weights(qsa, Hi, n_q, w):
+    # the seeded many-query kernel (each query has ~5000 candidates) at every
+    # head count it is built for, and a head weight that is not a power of
+    # two (0.3), which is applied in the epilogue (sum * w) instead of being
+    # folded into the bf16 queries, also on the few-query kernel
+    B, r, k, seed = 1, 4, 512, 990 + Hi + n_q
+    w = 1.0 / Hi if w is None else w
     pos = 20000
     end = pos + n_q
     N = end // r + 1
