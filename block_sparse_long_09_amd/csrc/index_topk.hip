@@ -607,7 +607,10 @@ void index_prefill_kernel(
     // sample (split tiles 0, rho, 2 rho, ...) that seeds the thresholds,
     // [P1, P1 + P2) the scan of every tile, [P1 + P2, P1 + 2 P2) a second scan,
     // run only when a seeded buffer ended short. Without seeding P1 = 0.
-    const int rho = seed_stride;
+    // (not at one indexer head: its 16 queries per lane would need 64 more
+    // registers for the sample's scores)
+    constexpr bool kSample = NS <= 8;
+    const int rho = kSample ? seed_stride : 0;
     const int n1 = rho > 0 ? (ntiles + rho - 1) / rho : 0;
     const int P1 = (n1 + TT - 1) / TT * TT;
     const int P2 = (ntiles + TT - 1) / TT * TT;
@@ -877,12 +880,14 @@ void index_prefill_kernel(
       }
       __builtin_amdgcn_s_waitcnt(prefill_vmcnt(0));  // no copy into LDS outlives the workgroup
     } else {
-      for (int t = 0; t < n1; t += TT) {  // as far as P1
-        __syncthreads();
-        seed_group(t, n1 - t);
+      if constexpr (kSample) {
+        for (int t = 0; t < n1; t += TT) {  // as far as P1
+          __syncthreads();
+          seed_group(t, n1 - t);
+        }
       }
       uint32_t seeded = 0;  // bit s: slot s starts from a seeded threshold
-      if (P1 > 0) {
+      if (kSample && P1 > 0) {
         if (pendB) seed_epi(accB, cB, true);
         pendB = false;
         // Seed: with n candidates of this split, S of them sampled, take the
@@ -1390,7 +1395,7 @@ IndexPlan plan_index(int hi, int k, int batch, int n_q, int64_t max_q_end, int r
   // query, m about 2.5 keep / rho); only where rho >= 16, so that the sample
   // adds at most 1/16 to the scoring.
   p.seed_stride = 0;
-  if (p.wide) {
+  if (p.wide && hi >= 2) {  // the kernel takes no sample at one head
     int rho = 1;
     while (5 * keep > 192 * rho) rho *= 2;
     if (rho >= 16) p.seed_stride = rho;

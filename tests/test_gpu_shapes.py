@@ -276,8 +276,8 @@ def test_index_topk_varlen_seeded_buffers_that_end_short(qsa):
 @pytest.mark.parametrize("Hi,n_q,w", [(8, 256, 0.3), (4, 256, 0.3), (8, 20, 0.3),
                                       (1, 256, None), (2, 256, None), (16, 256, None)])
 def test_index_topk_seeded_head_counts_and_weights(qsa, Hi, n_q, w):
-    # the seeded many-query kernel (each query has ~5000 candidates) at every
-    # head count it is built for, and a head weight that is not a power of
+    # the many-query kernel (each query has ~5000 candidates; seeded from 2
+    # heads up) at every head count it is built for, and a head weight that is not a power of
     # two (0.3), which is applied in the epilogue (sum * w) instead of being
     # folded into the bf16 queries, also on the few-query kernel
     B, r, k, seed = 1, 4, 512, 990 + Hi + n_q
@@ -292,8 +292,8 @@ def test_index_topk_seeded_head_counts_and_weights(qsa, Hi, n_q, w):
     cmp = torch.zeros((B, N, 64), dtype=torch.bfloat16, device="cuda")
     qsa.qsa_compress_keys(dev(ik[None]), cmp, r, 0, N)
     d = qsa.index_desc(r, k, Hi, idx_head_weight=w)
-    if n_q >= 64:
-        assert qsa.qsa_index_topk_plan_info(d, B, n_q, end).sample_stride == 16
+    if n_q >= 64:  # no sample at one head (its kernel has no registers to spare)
+        assert qsa.qsa_index_topk_plan_info(d, B, n_q, end).sample_stride == (16 if Hi >= 2 else 0)
     sel = torch.empty((B, n_q, k), dtype=torch.int32, device="cuda")
     cnt = torch.empty((B, n_q), dtype=torch.int32, device="cuda")
     ws = qsa.workspace(qsa.qsa_index_topk_workspace_size(d, B, n_q, end))

@@ -112,6 +112,9 @@ def test_index_plan_threshold_sample_stride(qsa, k, expect):
     assert info.sample_stride == expect
     if expect:
         assert 5 * (k - 1) <= 192 * expect and 5 * (k - 1) > 96 * expect
-    # decode (one query per sequence) and the few-query kernel take no sample
+    # decode (one query per sequence), the few-query kernel and the
+    # many-query kernel at one indexer head take no sample
     assert qsa.qsa_index_topk_plan_info(d, 4, 1, 1 << 20).sample_stride == 0
     assert qsa.qsa_index_topk_plan_info(d, 1, 32, 1 << 20).sample_stride == 0
+    d1 = qsa.index_desc(4, k, 1, 64)
+    assert qsa.qsa_index_topk_plan_info(d1, 1, 16384, 1 << 20).sample_stride == 0
