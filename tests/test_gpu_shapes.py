@@ -302,3 +302,30 @@ def test_index_topk_seeded_head_counts_and_weights(qsa, Hi, n_q, w):
     g_sel, g_cnt = sel.cpu().numpy()[0], cnt.cpu().numpy()[0]
     o_sel, o_cnt, band, _ = oracle.select(iq[0], blocks, pos, r, k, w)
     check_selection(g_sel, g_cnt, o_sel, o_cnt, band, lambda i: oracle.scores(iq[0][i], blocks[: (pos + i) // r], w))
+
+
+def test_index_topk_seeded_budget_1024(qsa):
+    # a budget of 1024 blocks seeds from every 32nd tile: 2 x 8192 queries
+    # over ~10K-12K candidates each, one candidate split
+    B, n_q, Hi, r, k, seed = 2, 8192, 8, 4, 1024, 995
+    pos0 = 40000
+    end = pos0 + n_q
+    N = end // r + 1
+    _say("seeded budget 1024")
+    d = qsa.index_desc(r, k, Hi)
+    info = qsa.qsa_index_topk_plan_info(d, B, n_q, end)
+    assert info.sample_stride == 32 and info.splits == 1
+    blocks = gen.normal(seed, 5, (B, N, 64))
+    iq = gen.normal(seed, 4, (B, n_q, Hi, 64))
+    sel = torch.empty((B, n_q, k), dtype=torch.int32, device="cuda")
+    cnt = torch.empty((B, n_q), dtype=torch.int32, device="cuda")
+    ws = qsa.workspace(qsa.qsa_index_topk_workspace_size(d, B, n_q, end))
+    q_pos0 = torch.full((B,), pos0, dtype=torch.int32, device="cuda")
+    qsa.qsa_index_topk(d, dev(iq), dev(blocks), q_pos0, end, sel, cnt, ws)
+    torch.cuda.synchronize()
+    g_sel, g_cnt = sel.cpu().numpy(), cnt.cpu().numpy()
+    for b in range(B):
+        for qi in (0, 1, 63, 64, 4095, 4096, 8190, 8191):
+            o_sel, o_cnt, band, _ = oracle.select(iq[b, qi:qi + 1], blocks[b], pos0 + qi, r, k, 1.0 / Hi)
+            check_selection(g_sel[b, qi:qi + 1], g_cnt[b, qi:qi + 1], o_sel, o_cnt, band,
+                            lambda i: oracle.scores(iq[b, qi], blocks[b][: (pos0 + qi) // r], 1.0 / Hi))
