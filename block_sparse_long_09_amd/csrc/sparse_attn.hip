@@ -324,6 +324,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
 // and turned into weights; each thread then sums its dimension over the
 // splits with independent loads.
 constexpr int kMaxMergeSplits = 1024;
+constexpr int kMergeBatch = 64;  // partial outputs a merge thread has in flight
 
 __global__ __launch_bounds__(128) void attn_merge_kernel(const float* __restrict__ part_o,
                                                          const float2* __restrict__ part_ml,
@@ -336,6 +337,17 @@ __global__ __launch_bounds__(128) void attn_merge_kernel(const float* __restrict
   const int h = blockIdx.y;
   const int d = threadIdx.x;
   const int64_t base = row * n_splits * (int64_t)Hq + h;  // index of split 0
+  // with at least kMergeBatch splits, this thread's dimension of the first
+  // kMergeBatch partial outputs is loaded before the weights are known (it
+  // does not depend on them): one round trip for all of them
+  const bool batch = n_splits >= kMergeBatch;
+  float v[kMergeBatch];
+  if (batch) {
+    const int64_t pstride = (int64_t)Hq * kD;  // between the splits of one (row, head)
+    const float* po = part_o + base * kD + d;
+#pragma unroll
+    for (int u = 0; u < kMergeBatch; ++u) v[u] = po[u * pstride];
+  }
   float m_loc = -INFINITY;
   for (int s = d; s < n_splits; s += 128) {
     const float2 ml = part_ml[base + (int64_t)s * Hq];
@@ -359,14 +371,20 @@ __global__ __launch_bounds__(128) void attn_merge_kernel(const float* __restrict
   if ((d & 63) == 0) red[1][d >> 6] = l_loc;
   __syncthreads();
   const float L = red[1][0] + red[1][1];
+  // weighted sum in split order
   float acc = 0.0f;
   int s = 0;
+  if (batch) {
+#pragma unroll
+    for (int u = 0; u < kMergeBatch; ++u) acc += v[u] * wsplit[u];
+    s = kMergeBatch;
+  }
   for (; s + 8 <= n_splits; s += 8) {
-    float v[8];
+    float w8[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) v[u] = part_o[(base + (int64_t)(s + u) * Hq) * kD + d];
+    for (int u = 0; u < 8; ++u) w8[u] = part_o[(base + (int64_t)(s + u) * Hq) * kD + d];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) acc += v[u] * wsplit[s + u];
+    for (int u = 0; u < 8; ++u) acc += w8[u] * wsplit[s + u];
   }
   for (; s < n_splits; ++s) acc += part_o[(base + (int64_t)s * Hq) * kD + d] * wsplit[s];
   out[(row * Hq + h) * kD + d] = (uint16_t)f32_to_bf16_bits(acc / L);
