@@ -8,6 +8,9 @@ Sequence of library calls (every step runs in the HIP kernels of libqsa.so):
   packed batch:  qsa_compress_keys per sequence -> qsa_index_topk_varlen
                  -> qsa_sparse_attn_prefill_paged (new rows of several
                  sequences appended to cached prefixes, K/V in pages)
+  long prefill:  the prefill chunk's calls for each chunk in turn, chunk c's
+                 attention on one stream beside chunk c + 1's compression and
+                 indexer on another (ChunkedPrefill)
 The objects below only own the caller-side buffers (workspaces, selections,
 outputs) so that repeated calls allocate nothing.
 """
@@ -59,6 +62,52 @@ class PrefillPath:
         self.select(idx_q, cmp_k, q_pos0, n_q)
         return self.attend(q, k, v, q_pos0, n_q)
 
+
+
+class ChunkedPrefill:
+    """Causal prefill of `n_q` queries of one sequence in chunks of `chunk`
+    queries. Chunk c's attention and chunk c + 1's key compression and
+    indexer do not depend on each other (the indexer reads block keys, the
+    attention K, V and its own selection), so they run on two streams side by
+    side; two sets of selection buffers alternate between the chunks, and
+    chunk c + 2's indexer waits until chunk c's attention has read its set.
+    Outputs go to the caller's out [n_q, Hq, D] and lse [n_q, Hq]."""
+
+    def __init__(self, Hq, Hkv, Hi, r=4, k=512, chunk=8192, max_len=8192, D=128, di=64, device="cuda"):
+        self.chunk = chunk
+        self.paths = [PrefillPath(Hq, Hkv, Hi, r, k, n_q_max=chunk, max_len=max_len, D=D, di=di, device=device)
+                      for _ in range(2)]
+        self.s_attn = torch.cuda.Stream(device)
+        self.s_index = torch.cuda.Stream(device)
+
+    def __call__(self, q, k, v, idx_q, idx_k, cmp_k, q_pos0, n_q, out, lse=None):
+        cur = torch.cuda.current_stream()
+        self.s_attn.wait_stream(cur)
+        self.s_index.wait_stream(cur)
+        n_ch = (n_q + self.chunk - 1) // self.chunk
+        selected, attended = [None] * n_ch, [None] * n_ch
+        for c in range(n_ch):
+            c0 = c * self.chunk
+            n = min(self.chunk, n_q - c0)
+            p = self.paths[c % 2]
+            with torch.cuda.stream(self.s_index):
+                if c >= 2:
+                    self.s_index.wait_event(attended[c - 2])
+                p.compress(idx_k, cmp_k, q_pos0 + c0, n)
+                p.select(idx_q[c0:c0 + n], cmp_k, q_pos0 + c0, n)
+                selected[c] = torch.cuda.Event()
+                selected[c].record(self.s_index)
+            with torch.cuda.stream(self.s_attn):
+                self.s_attn.wait_event(selected[c])
+                end = q_pos0 + c0 + n
+                qsa_sparse_attn_prefill(p.adesc, p.r, q[c0:c0 + n], k[:end], v[:end], q_pos0 + c0,
+                                        p.sel[:n], p.cnt[:n], out[c0:c0 + n],
+                                        None if lse is None else lse[c0:c0 + n], p.ws_attn)
+                attended[c] = torch.cuda.Event()
+                attended[c].record(self.s_attn)
+        cur.wait_stream(self.s_attn)
+        cur.wait_stream(self.s_index)
+        return out, lse
 
 class DecodePath:
     """One decode step for `batch` sequences with caches of `max_len` tokens."""

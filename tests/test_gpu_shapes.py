@@ -329,3 +329,40 @@ def test_index_topk_seeded_budget_1024(qsa):
             o_sel, o_cnt, band, _ = oracle.select(iq[b, qi:qi + 1], blocks[b], pos0 + qi, r, k, 1.0 / Hi)
             check_selection(g_sel[b, qi:qi + 1], g_cnt[b, qi:qi + 1], o_sel, o_cnt, band,
                             lambda i: oracle.scores(iq[b, qi], blocks[b][: (pos0 + qi) // r], 1.0 / Hi))
+
+
+@pytest.mark.parametrize("q_pos0,n_q,chunk", [(0, 16384, 4096), (4096, 10000, 4096)])
+def test_chunked_prefill_two_streams_matches_chunk_by_chunk(qsa, q_pos0, n_q, chunk):
+    # chunk c's attention beside chunk c + 1's compression and indexer on two
+    # streams gives the bits of the chunks run one after the other (the
+    # second case starts after a cached prefix and ends with a ragged chunk)
+    from block_sparse_long_09_amd.pipeline import ChunkedPrefill, PrefillPath
+    Hq, Hkv, Hi, D, r, k, seed = 16, 2, 4, 128, 4, 512, 1010 + q_pos0
+    L = q_pos0 + n_q
+    _say("chunked prefill", q_pos0, n_q, chunk)
+    Q, K, V = dev(gen.normal(seed, 1, (n_q, Hq, D))), dev(gen.normal(seed, 2, (L, Hkv, D))), dev(gen.normal(seed, 3, (L, Hkv, D)))
+    iq = dev(gen.normal(seed, 4, (n_q, Hi, 64)))
+    ik = dev(gen.idx_keys(seed, 0, L, 0, L, 64, 512, r))
+    cmp_a = torch.zeros((L // r, 64), dtype=torch.bfloat16, device="cuda")
+    cmp_b = torch.zeros_like(cmp_a)
+    if q_pos0 // r:
+        qsa.qsa_compress_keys(ik, cmp_a, r, 0, q_pos0 // r)
+        qsa.qsa_compress_keys(ik, cmp_b, r, 0, q_pos0 // r)
+    seq = PrefillPath(Hq, Hkv, Hi, r, k, n_q_max=chunk, max_len=L)
+    ref_out = torch.empty((n_q, Hq, D), dtype=torch.bfloat16, device="cuda")
+    ref_lse = torch.empty((n_q, Hq), dtype=torch.float32, device="cuda")
+    for c0 in range(0, n_q, chunk):
+        n = min(chunk, n_q - c0)
+        o, l = seq(Q[c0:c0 + n], K, V, iq[c0:c0 + n], ik, cmp_a, q_pos0 + c0, n)
+        ref_out[c0:c0 + n] = o
+        ref_lse[c0:c0 + n] = l
+    torch.cuda.synchronize()
+    cp = ChunkedPrefill(Hq, Hkv, Hi, r, k, chunk=chunk, max_len=L)
+    for _ in range(2):  # twice: the alternating selection buffers are reused
+        out = torch.full((n_q, Hq, D), 7.0, dtype=torch.bfloat16, device="cuda")
+        lse = torch.full((n_q, Hq), 7.0, dtype=torch.float32, device="cuda")
+        cp(Q, K, V, iq, ik, cmp_b, q_pos0, n_q, out, lse)
+        torch.cuda.synchronize()
+        assert torch.equal(cmp_b, cmp_a)
+        assert torch.equal(out.view(torch.int16), ref_out.view(torch.int16))
+        assert torch.equal(lse, ref_lse)
